@@ -1,0 +1,177 @@
+/*
+ * i8mp.h: INT8 mixed-precision linear layers with row-wise scaling, for AMD
+ * MI355X (gfx950).  C ABI.
+ *
+ * What the library computes ("Quantized model training", section "INT8 mixed
+ * precision training"; "Integrate INT8 mixed-precision from torchao 0.7",
+ * gau-nernst's reply on memory): every GEMM of a linear layer's training
+ * step quantizes both bf16 operands dynamically to int8, with one fp32 scale
+ * per row of the contraction dimension, multiplies the codes with int32
+ * accumulation, and scales the result back to bf16.  Weights, activations and
+ * gradients stay bf16 between calls; nothing is cached.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains memory.  Scratch space comes in
+ *     through the `ws` argument of the calls that need it.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the null stream).  Buffers must stay valid until the stream
+ *     work completes.
+ *   - bf16 travels as uint16_t bit patterns.  Matrices are row-major with a
+ *     leading dimension `ld*` counted in elements.
+ *   - Every argument is validated on the host before any HIP call; a call
+ *     that fails validation launches nothing and writes nothing.
+ *   - Alignment: base pointers of bf16/int8/int32 matrices are 16-byte
+ *     aligned and ld * element size is a multiple of 16 bytes; scale vectors
+ *     are 4-byte aligned.  Any sizes >= 0 are accepted.  Reads of an input
+ *     may touch bytes between the end of a row and the next 16-byte boundary
+ *     (never outside that aligned 16-byte chunk); outputs are written only
+ *     inside their rows.
+ *   - Outputs must not overlap inputs.
+ *   - The library is stateless and reentrant.  The device check (gfx950) is
+ *     cached per device.
+ */
+#ifndef I8MP_H
+#define I8MP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  I8MP_OK = 0,
+  I8MP_EINVAL = 1,     /* null pointer, negative size, misalignment, ld too small, overlap */
+  I8MP_ERANGE = 2,     /* contraction longer than I8MP_MAX_CONTRACTION (int32 could overflow) */
+  I8MP_EDEVICE = 3,    /* no current HIP device, or it is not gfx950 */
+  I8MP_EHIP = 4,       /* a HIP launch reported an error */
+  I8MP_EWORKSPACE = 5, /* workspace NULL or smaller than the query function returns */
+} i8mp_status;
+
+/* Rounding of the quantization step.  RNE: round half to even.  SR:
+ * stochastic rounding, code = floor(RN32(x/s + u)) with u a 24-bit uniform
+ * from Philox4x32-10 ("Quantized model training", section "INT8 mixed
+ * precision training": stochastic rounding is an option of each INT8 GEMM's
+ * quantization; the pages leave the mechanism open). */
+typedef enum { I8MP_RNE = 0, I8MP_SR = 1 } i8mp_round;
+
+/* Operand layouts ("Quantized model training", section "Speed benchmarks >
+ * Matmul"): NT = A @ B.T (A is M x K, B is N x K), NN = A @ B (A is M x K,
+ * B is K x N), TN = A.T @ B (A is K x M, B is K x N).  C is M x N. */
+typedef enum { I8MP_NT = 0, I8MP_NN = 1, I8MP_TN = 2 } i8mp_layout;
+
+/* floor((2^31 - 1) / 127^2): the longest contraction whose int32 sum of
+ * int8 x int8 products (|code| <= 127) cannot overflow. */
+#define I8MP_MAX_CONTRACTION 133144
+
+/* Stochastic-rounding stream of one linear-layer call.  Quantization pass j
+ * of the call uses Philox counter offset `offset + j * 2^40`:
+ * j = 0 X row-wise, 1 W row-wise, 2 dY row-wise, 3 W column-wise,
+ * 4 dY column-wise, 5 X column-wise.  Callers advance `offset` (or `seed`)
+ * between steps.  Ignored under RNE. */
+typedef struct {
+  int32_t round; /* i8mp_round */
+  uint64_t seed;
+  uint64_t offset;
+} i8mp_linear_opts;
+
+const char* i8mp_status_str(i8mp_status s);
+
+/* Version of this ABI (incremented on any signature change). */
+int32_t i8mp_abi_version(void);
+
+/*
+ * Row-wise dynamic quantization ("Quantized model training", section "INT8
+ * mixed precision training"; the quantize step of "Add QAT support for
+ * distributed finetuning", summary, with zero point 0):
+ *   amax[r]  = max_c |x[r,c]|                 (exact)
+ *   scale[r] = RN32(amax[r] / 127)            (0 for an all-zero row)
+ *   q[r,c]   = clamp(round(RN32(x[r,c] / scale[r])), -127, 127), 0 if scale 0
+ * round = RNE: half to even.  round = SR: floor(RN32(x/s + u)),
+ * u = (w >> 8) * 2^-24 where w is word (e mod 4) of Philox4x32-10 block
+ * (offset + e/4), e = r*cols + c (the logical index, independent of ld),
+ * counter = (lo32(block), hi32(block), 0, 0), key = (lo32(seed), hi32(seed)).
+ *   x:     bf16 [rows x cols], leading dim ldx >= cols
+ *   q:     int8 [rows x cols], leading dim ldq >= cols (same layout as x)
+ *   scale: fp32 [rows]
+ */
+i8mp_status i8mp_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  int8_t* q, int64_t ldq, float* scale, int32_t round,
+                                  uint64_t seed, uint64_t offset, void* stream);
+
+/*
+ * Column-wise dynamic quantization: the same with the reduction over rows,
+ * for operands whose contraction runs down the columns (the A @ B and
+ * A.T @ B layouts).  scale is fp32 [cols]; q keeps x's layout (no
+ * transpose).  Stochastic rounding uses the same element index e = r*cols+c.
+ *   ws: scratch of at least i8mp_quantize_colwise_workspace_bytes(rows, cols)
+ *       bytes, 256-byte aligned; its contents on entry do not matter.
+ */
+size_t i8mp_quantize_colwise_workspace_bytes(int64_t rows, int64_t cols);
+i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  int8_t* q, int64_t ldq, float* scale, int32_t round,
+                                  uint64_t seed, uint64_t offset, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
+ * Scaled INT8 matmul ("Quantized model training", section "INT8 mixed
+ * precision training"; scaled back to BF16 per "Integrate INT8
+ * mixed-precision from torchao 0.7"):
+ *   acc[m,n] = sum_k A(m,k) * B(k,n)              (int32, exact)
+ *   C[m,n]   = bf16_RNE(RN32(RN32(float(acc)) * scale_a[m]) * scale_b[n])
+ * with A(m,k), B(k,n) read in the given layout (see i8mp_layout).  scale_a
+ * is indexed by the output row m and scale_b by the output column n in
+ * every layout.  K <= I8MP_MAX_CONTRACTION, else I8MP_ERANGE.  K = 0 writes
+ * zeros.
+ *   C: bf16 [M x N], leading dim ldc >= N
+ */
+i8mp_status i8mp_int8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K,
+                                const int8_t* A, int64_t lda, const float* scale_a,
+                                const int8_t* B, int64_t ldb, const float* scale_b, uint16_t* C,
+                                int64_t ldc, void* stream);
+
+/* The integer accumulators alone, C = int32 [M x N] (same layouts, same
+ * kernels without the scale epilogue).  For checking the int32 sums. */
+i8mp_status i8mp_int8_mm_i32(int32_t layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                             int64_t lda, const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
+                             void* stream);
+
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) words as the quantize
+ * kernels draw them: out[4*i + j] = word j of block (offset + i) under key
+ * seed.  out: uint32 [4 * n_blocks], 16-byte aligned.  For checking draws. */
+i8mp_status i8mp_philox4x32_10(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
+                               void* stream);
+
+/*
+ * One linear layer, Y = X @ W.T ("Quantized model training", section "INT8
+ * mixed precision training": forward).  X: bf16 [M x K], W: bf16 [N x K],
+ * Y: bf16 [M x N], all dense (leading dim = columns).  X and W are quantized
+ * row-wise over K, then the NT scaled matmul runs.  K <= I8MP_MAX_CONTRACTION.
+ * ws: at least i8mp_linear_workspace_bytes(M, N, K, 0) bytes, 256-aligned.
+ */
+size_t i8mp_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t backward);
+i8mp_status i8mp_linear_fwd(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                            int64_t N, int64_t K, const i8mp_linear_opts* opts, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the same layer (same section: backward grad input and grad
+ * weight, each an INT8 GEMM quantized along its own contraction):
+ *   dX = dY @ W     dY row-wise over N, W column-wise over N, NN; dX [M x K]
+ *   dW = dY.T @ X   dY column-wise over M, X column-wise over M, TN; dW [N x K]
+ * Either output may be NULL to skip its GEMM.  Outputs are overwritten.
+ * N <= I8MP_MAX_CONTRACTION when dX is wanted, M <= it when dW is wanted.
+ * ws: at least i8mp_linear_workspace_bytes(M, N, K, 1) bytes, 256-aligned.
+ */
+i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
+                            uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                            const i8mp_linear_opts* opts, void* ws, size_t ws_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8MP_H */

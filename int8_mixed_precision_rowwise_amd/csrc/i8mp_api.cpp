@@ -1,0 +1,370 @@
+// C ABI of the INT8 mixed-precision linear-layer library (include/i8mp.h).
+// Every argument is validated on the host before the first HIP call, so a
+// rejected call launches nothing and writes nothing.
+#include "../../include/i8mp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;  // rejects sizes whose products could overflow
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [begin, end) byte range of a rows x cols matrix with leading dim ld.
+struct Range {
+  uintptr_t b = 0, e = 0;
+};
+
+Range mat_range(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  Range r;
+  if (!p || rows <= 0 || cols <= 0) return r;
+  r.b = reinterpret_cast<uintptr_t>(p);
+  r.e = r.b + (uintptr_t)(((rows - 1) * ld + cols) * elem);
+  return r;
+}
+
+Range vec_range(const void* p, int64_t n, int64_t elem) { return mat_range(p, 1, n, n, elem); }
+
+bool overlap(Range a, Range b) { return a.b < a.e && b.b < b.e && a.b < b.e && b.b < a.e; }
+
+bool dims_ok(int64_t a, int64_t b = 0, int64_t c = 0) {
+  return a >= 0 && b >= 0 && c >= 0 && a < kMaxDim && b < kMaxDim && c < kMaxDim;
+}
+
+// Input or output matrix of `elem`-byte elements read/written in 16-byte
+// chunks: base 16-aligned, rows 16-aligned, ld >= cols.  A matrix with no
+// elements may be NULL.
+bool chunked_ok(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  if (rows == 0 || cols == 0) return ld >= 0 && ld < kMaxDim;
+  return p && aligned(p, 16) && ld >= cols && ld < kMaxDim && (ld * elem) % 16 == 0;
+}
+
+// Output matrix written element by element: natural alignment, ld >= cols.
+bool elementwise_ok(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  if (rows == 0 || cols == 0) return ld >= 0 && ld < kMaxDim;
+  return p && aligned(p, (uintptr_t)elem) && ld >= cols && ld < kMaxDim;
+}
+
+bool vec_ok(const void* p, int64_t n) { return n == 0 || (p && aligned(p, 4)); }
+
+// gfx950 check, cached per device: 0 unknown, 1 ok, 2 not gfx950.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];
+
+i8mp_status device_check() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return I8MP_EDEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int s = g_device_state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return I8MP_OK;
+    if (s == 2) return I8MP_EDEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return I8MP_EDEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? I8MP_OK : I8MP_EDEVICE;
+}
+
+i8mp_status hip_status(hipError_t e) { return e == hipSuccess ? I8MP_OK : I8MP_EHIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Storage shapes of the GEMM operands for a layout.
+void operand_shapes(int32_t layout, int64_t M, int64_t N, int64_t K, int64_t& ar, int64_t& ac,
+                    int64_t& br, int64_t& bc) {
+  if (layout == I8MP_NT) {
+    ar = M, ac = K, br = N, bc = K;
+  } else if (layout == I8MP_NN) {
+    ar = M, ac = K, br = K, bc = N;
+  } else {
+    ar = K, ac = M, br = K, bc = N;
+  }
+}
+
+i8mp_status validate_mm(int32_t layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                        int64_t lda, const int8_t* B, int64_t ldb, const void* C, int64_t ldc,
+                        int64_t c_elem, const float* sa, const float* sb, bool scaled) {
+  if (layout < 0 || layout > 2) return I8MP_EINVAL;
+  if (!dims_ok(M, N, K)) return I8MP_EINVAL;
+  if (K > I8MP_MAX_CONTRACTION) return I8MP_ERANGE;
+  int64_t ar, ac, br, bc;
+  operand_shapes(layout, M, N, K, ar, ac, br, bc);
+  const bool out = M > 0 && N > 0;  // anything to compute
+  if (!chunked_ok(out ? A : nullptr, out ? ar : 0, out ? ac : 0, lda, 1)) return I8MP_EINVAL;
+  if (!chunked_ok(out ? B : nullptr, out ? br : 0, out ? bc : 0, ldb, 1)) return I8MP_EINVAL;
+  if (!elementwise_ok(C, M, N, ldc, c_elem)) return I8MP_EINVAL;
+  if (scaled && out && (!vec_ok(sa, M) || !vec_ok(sb, N))) return I8MP_EINVAL;
+  if (!out) return I8MP_OK;
+  const Range rc = mat_range(C, M, N, ldc, c_elem);
+  if (overlap(rc, mat_range(A, ar, ac, lda, 1)) || overlap(rc, mat_range(B, br, bc, ldb, 1)))
+    return I8MP_EINVAL;
+  if (scaled && (overlap(rc, vec_range(sa, M, 4)) || overlap(rc, vec_range(sb, N, 4))))
+    return I8MP_EINVAL;
+  return I8MP_OK;
+}
+
+i8mp_status validate_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           const int8_t* q, int64_t ldq, const float* scale, int64_t nscale,
+                           int32_t round) {
+  if (round != I8MP_RNE && round != I8MP_SR) return I8MP_EINVAL;
+  if (!dims_ok(rows, cols)) return I8MP_EINVAL;
+  if (!chunked_ok(x, rows, cols, ldx, 2)) return I8MP_EINVAL;
+  if (!chunked_ok(q, rows, cols, ldq, 1)) return I8MP_EINVAL;
+  if (!vec_ok(scale, nscale)) return I8MP_EINVAL;
+  const Range rx = mat_range(x, rows, cols, ldx, 2), rq = mat_range(q, rows, cols, ldq, 1),
+              rs = vec_range(scale, nscale, 4);
+  if (overlap(rq, rx) || overlap(rs, rx) || overlap(rs, rq)) return I8MP_EINVAL;
+  return I8MP_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+int64_t pad16(int64_t n) { return (n + 15) / 16 * 16; }
+
+// Workspace carving: regions in a fixed order, each 256-byte aligned.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  void* take(size_t n) {
+    void* p = base ? base + used : nullptr;
+    used += up(n);
+    return p;
+  }
+};
+
+struct FwdWs {
+  int8_t *qx, *qw;
+  float *sx, *sw;
+};
+size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
+  Carver c{static_cast<char*>(ws)};
+  const int64_t kp = pad16(K);
+  FwdWs w;
+  w.qx = static_cast<int8_t*>(c.take((size_t)(M * kp)));
+  w.qw = static_cast<int8_t*>(c.take((size_t)(N * kp)));
+  w.sx = static_cast<float*>(c.take((size_t)M * 4));
+  w.sw = static_cast<float*>(c.take((size_t)N * 4));
+  if (out) *out = w;
+  return c.used;
+}
+
+struct BwdWs {
+  int8_t *qdy, *qw, *qx;
+  float *sdy, *sw, *sx;
+  void* col;
+};
+size_t carve_bwd(void* ws, int64_t M, int64_t N, int64_t K, BwdWs* out) {
+  Carver c{static_cast<char*>(ws)};
+  const int64_t kp = pad16(K), np = pad16(N);
+  BwdWs w;
+  w.qdy = static_cast<int8_t*>(c.take((size_t)(M * np)));
+  w.qw = static_cast<int8_t*>(c.take((size_t)(N * kp)));
+  w.qx = static_cast<int8_t*>(c.take((size_t)(M * kp)));
+  w.sdy = static_cast<float*>(c.take((size_t)(M > N ? M : N) * 4));
+  w.sw = static_cast<float*>(c.take((size_t)K * 4));
+  w.sx = static_cast<float*>(c.take((size_t)K * 4));
+  size_t col = i8mp::colwise_workspace_bytes(N, K);
+  const size_t c2 = i8mp::colwise_workspace_bytes(M, N), c3 = i8mp::colwise_workspace_bytes(M, K);
+  if (c2 > col) col = c2;
+  if (c3 > col) col = c3;
+  w.col = c.take(col);
+  if (out) *out = w;
+  return c.used;
+}
+
+uint64_t pass_offset(uint64_t offset, int j) { return offset + ((uint64_t)j << 40); }
+
+}  // namespace
+
+extern "C" {
+
+const char* i8mp_status_str(i8mp_status s) {
+  switch (s) {
+    case I8MP_OK: return "ok";
+    case I8MP_EINVAL: return "invalid argument (null, negative size, misaligned, ld too small or overlapping buffers)";
+    case I8MP_ERANGE: return "contraction longer than 133144: int32 accumulation could overflow";
+    case I8MP_EDEVICE: return "no current HIP device, or the device is not gfx950";
+    case I8MP_EHIP: return "HIP reported an error at launch";
+    case I8MP_EWORKSPACE: return "workspace missing, misaligned or too small";
+  }
+  return "unknown status";
+}
+
+int32_t i8mp_abi_version(void) { return 1; }
+
+i8mp_status i8mp_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  int8_t* q, int64_t ldq, float* scale, int32_t round,
+                                  uint64_t seed, uint64_t offset, void* stream) {
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q, ldq, scale, rows, round);
+  if (st != I8MP_OK) return st;
+  if (rows == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_rowwise(x, rows, cols, ldx, q, ldq, scale, round, seed,
+                                                  offset, as_stream(stream)));
+}
+
+size_t i8mp_quantize_colwise_workspace_bytes(int64_t rows, int64_t cols) {
+  if (!dims_ok(rows, cols) || cols == 0) return 0;
+  return up(i8mp::colwise_workspace_bytes(rows, cols));
+}
+
+i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  int8_t* q, int64_t ldq, float* scale, int32_t round,
+                                  uint64_t seed, uint64_t offset, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q, ldq, scale, cols, round);
+  if (st != I8MP_OK) return st;
+  if (cols == 0) return I8MP_OK;
+  const size_t need = i8mp_quantize_colwise_workspace_bytes(rows, cols);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  if (overlap(rw, mat_range(x, rows, cols, ldx, 2)) || overlap(rw, mat_range(q, rows, cols, ldq, 1)) ||
+      overlap(rw, vec_range(scale, cols, 4)))
+    return I8MP_EINVAL;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_colwise(x, rows, cols, ldx, q, ldq, scale, round, seed,
+                                                  offset, ws, as_stream(stream)));
+}
+
+i8mp_status i8mp_int8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K,
+                                const int8_t* A, int64_t lda, const float* scale_a,
+                                const int8_t* B, int64_t ldb, const float* scale_b, uint16_t* C,
+                                int64_t ldc, void* stream) {
+  i8mp_status st = validate_mm(layout, M, N, K, A, lda, B, ldb, C, ldc, 2, scale_a, scale_b, true);
+  if (st != I8MP_OK) return st;
+  if (M == 0 || N == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_gemm(layout, M, N, K, A, lda, scale_a, B, ldb, scale_b, C,
+                                      nullptr, ldc, as_stream(stream)));
+}
+
+i8mp_status i8mp_int8_mm_i32(int32_t layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                             int64_t lda, const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
+                             void* stream) {
+  i8mp_status st = validate_mm(layout, M, N, K, A, lda, B, ldb, C, ldc, 4, nullptr, nullptr, false);
+  if (st != I8MP_OK) return st;
+  if (M == 0 || N == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_gemm(layout, M, N, K, A, lda, nullptr, B, ldb, nullptr, nullptr,
+                                      C, ldc, as_stream(stream)));
+}
+
+i8mp_status i8mp_philox4x32_10(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
+                               void* stream) {
+  if (n_blocks < 0 || n_blocks >= kMaxDim) return I8MP_EINVAL;
+  if (n_blocks == 0) return I8MP_OK;
+  if (!out || !aligned(out, 16)) return I8MP_EINVAL;
+  i8mp_status st = device_check();
+  if (st != I8MP_OK) return st;
+  return hip_status(i8mp::launch_philox(seed, offset, n_blocks, out, as_stream(stream)));
+}
+
+size_t i8mp_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t backward) {
+  if (!dims_ok(M, N, K)) return 0;
+  return backward ? carve_bwd(nullptr, M, N, K, nullptr) : carve_fwd(nullptr, M, N, K, nullptr);
+}
+
+i8mp_status i8mp_linear_fwd(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                            int64_t N, int64_t K, const i8mp_linear_opts* opts, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!opts || (opts->round != I8MP_RNE && opts->round != I8MP_SR)) return I8MP_EINVAL;
+  if (!dims_ok(M, N, K)) return I8MP_EINVAL;
+  if (K > I8MP_MAX_CONTRACTION) return I8MP_ERANGE;
+  if (!chunked_ok(X, M, K, K, 2) || !chunked_ok(W, N, K, K, 2) || !elementwise_ok(Y, M, N, N, 2))
+    return I8MP_EINVAL;
+  const Range ry = mat_range(Y, M, N, N, 2);
+  if (overlap(ry, mat_range(X, M, K, K, 2)) || overlap(ry, mat_range(W, N, K, K, 2)))
+    return I8MP_EINVAL;
+  if (M == 0 || N == 0) return I8MP_OK;
+  const size_t need = carve_fwd(nullptr, M, N, K, nullptr);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  if (overlap(rw, ry) || overlap(rw, mat_range(X, M, K, K, 2)) || overlap(rw, mat_range(W, N, K, K, 2)))
+    return I8MP_EINVAL;
+  i8mp_status st = device_check();
+  if (st != I8MP_OK) return st;
+  FwdWs w;
+  carve_fwd(ws, M, N, K, &w);
+  const hipStream_t s = as_stream(stream);
+  const int64_t kp = pad16(K);
+  hipError_t e = i8mp::launch_quantize_rowwise(X, M, K, K, w.qx, kp, w.sx, opts->round, opts->seed,
+                                               pass_offset(opts->offset, 0), s);
+  if (e == hipSuccess)
+    e = i8mp::launch_quantize_rowwise(W, N, K, K, w.qw, kp, w.sw, opts->round, opts->seed,
+                                      pass_offset(opts->offset, 1), s);
+  if (e == hipSuccess)
+    e = i8mp::launch_gemm(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, nullptr, N, s);
+  return hip_status(e);
+}
+
+i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
+                            uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                            const i8mp_linear_opts* opts, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!opts || (opts->round != I8MP_RNE && opts->round != I8MP_SR)) return I8MP_EINVAL;
+  if (!dims_ok(M, N, K)) return I8MP_EINVAL;
+  if (dX && N > I8MP_MAX_CONTRACTION) return I8MP_ERANGE;
+  if (dW && M > I8MP_MAX_CONTRACTION) return I8MP_ERANGE;
+  if (!chunked_ok(dY, M, N, N, 2)) return I8MP_EINVAL;
+  if (dX && (!chunked_ok(W, N, K, K, 2) || !elementwise_ok(dX, M, K, K, 2))) return I8MP_EINVAL;
+  if (dW && (!chunked_ok(X, M, K, K, 2) || !elementwise_ok(dW, N, K, K, 2))) return I8MP_EINVAL;
+  if (dX && dW && dX == dW && M * K > 0 && N * K > 0) return I8MP_EINVAL;
+  const Range rdy = mat_range(dY, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
+              rwt = mat_range(W, N, K, K, 2), rdx = dX ? mat_range(dX, M, K, K, 2) : Range{},
+              rdw = dW ? mat_range(dW, N, K, K, 2) : Range{};
+  for (Range o : {rdx, rdw})
+    if (overlap(o, rdy) || overlap(o, rx) || overlap(o, rwt)) return I8MP_EINVAL;
+  if (overlap(rdx, rdw)) return I8MP_EINVAL;
+  const bool want_dx = dX && M > 0 && K > 0, want_dw = dW && N > 0 && K > 0;
+  if (!want_dx && !want_dw) return I8MP_OK;
+  const size_t need = carve_bwd(nullptr, M, N, K, nullptr);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  for (Range o : {rdy, rx, rwt, rdx, rdw})
+    if (overlap(rw, o)) return I8MP_EINVAL;
+  i8mp_status st = device_check();
+  if (st != I8MP_OK) return st;
+  BwdWs w;
+  carve_bwd(ws, M, N, K, &w);
+  const hipStream_t s = as_stream(stream);
+  const int64_t kp = pad16(K), np = pad16(N);
+  const int r = opts->round;
+  const uint64_t seed = opts->seed;
+  hipError_t e = hipSuccess;
+  if (want_dx) {
+    // dX = dY @ W: dY row-wise over N, W column-wise over N, NN
+    e = i8mp::launch_quantize_rowwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
+                                      pass_offset(opts->offset, 2), s);
+    if (e == hipSuccess)
+      e = i8mp::launch_quantize_colwise(W, N, K, K, w.qw, kp, w.sw, r, seed,
+                                        pass_offset(opts->offset, 3), w.col, s);
+    if (e == hipSuccess)
+      e = i8mp::launch_gemm(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, nullptr, K, s);
+  }
+  if (want_dw && e == hipSuccess) {
+    // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
+    e = i8mp::launch_quantize_colwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
+                                      pass_offset(opts->offset, 4), w.col, s);
+    if (e == hipSuccess)
+      e = i8mp::launch_quantize_colwise(X, M, K, K, w.qx, kp, w.sx, r, seed,
+                                        pass_offset(opts->offset, 5), w.col, s);
+    if (e == hipSuccess)
+      e = i8mp::launch_gemm(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, nullptr, K, s);
+  }
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal launchers of the gfx950 kernels.  The C ABI in i8mp_api.cpp
+// validates every argument before calling any of these; the launchers assume
+// valid, aligned arguments and only pick a kernel variant and a grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace i8mp {
+
+// Row-wise quantization (round: 0 = RNE, 1 = SR).
+hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
+                                   uint64_t offset, hipStream_t stream);
+
+// Column-wise quantization: partial column maxima into ws, a finalize pass
+// writing the scales, then the quantize pass.
+size_t colwise_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
+                                   uint64_t offset, void* ws, hipStream_t stream);
+
+// int8 GEMM in layout 0 = NT, 1 = NN, 2 = TN.  Exactly one of (C_bf16 with
+// both scales) or C_i32 is non-null.
+hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                       const float* sa, const int8_t* B, int64_t ldb, const float* sb,
+                       uint16_t* C_bf16, int32_t* C_i32, int64_t ldc, hipStream_t stream);
+
+hipError_t launch_philox(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
+                         hipStream_t stream);
+
+}  // namespace i8mp

@@ -1,0 +1,496 @@
+// Dynamic INT8 quantization kernels for gfx950: row-wise (one scale per row)
+// and column-wise (one scale per column), round-half-even or stochastic.
+//
+// Method ("Quantized model training", section "INT8 mixed precision
+// training": dynamic row-wise quantization before each scaled INT8 matmul;
+// the quantize step of "Add QAT support for distributed finetuning",
+// summary: divide by the scale, round, clamp; zero point 0):
+//   scale = RN32(absmax / 127), code = clamp(round(RN32(x / scale)), -127, 127)
+// An all-zero group has scale 0 and codes 0.  Stochastic rounding takes
+// code = floor(RN32(x/scale + u)), u from Philox4x32-10 at the element's
+// logical index.
+//
+// Both passes are HBM-bound streams: 2 bytes read and 1 byte written per
+// element.  Every lane moves 16-byte chunks (8 bf16), a wave covers 1 KiB of
+// a row per load, and the absmax is taken on bf16 bit patterns with the sign
+// cleared (for non-negative IEEE values bit order is value order, so the
+// maximum is exact and order-free).
+//
+// The quotient x / scale is evaluated as in FMA-based division (Markstein,
+// IBM J. Res. Dev. 34(1), 1990): with rcp = RN32(1/scale),
+//   q0 = RN(x * rcp); e = fma(-q0, scale, x) (exact); v = RN(fma(e, rcp, q0))
+// which equals the IEEE quotient RN32(x/scale) when nothing underflows.  For
+// scales below 2^-100 the kernels divide directly instead.  The equality is
+// checked on the GPU for every bf16 value against every bf16 absmax.
+#include "internal.h"
+#include "philox.h"
+
+namespace i8mp {
+namespace {
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / 64;
+
+__device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us2, w); }
+
+// Largest |x| bit pattern among the 8 bf16 of a chunk, kept as two halves.
+__device__ __forceinline__ us2 absmax_bits(us2 m, uint4 v) {
+  m = __builtin_elementwise_max(m, as_us2(v.x & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, as_us2(v.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, as_us2(v.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, as_us2(v.w & 0x7FFF7FFFu));
+  return m;
+}
+
+// Zero the bf16 elements at positions >= n (1 <= n < 8) of a chunk.
+__device__ __forceinline__ uint4 keep_first(uint4 v, int n) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lo = 2 * i, hi = 2 * i + 1;
+    uint32_t mask = (lo < n ? 0x0000FFFFu : 0u) | (hi < n ? 0xFFFF0000u : 0u);
+    w[i] &= mask;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  return m;
+}
+
+// Scale of one group and how its quotients are evaluated.
+struct GroupScale {
+  float s;    // RN32(amax / 127)
+  float rcp;  // RN32(1 / s)
+  int mode;   // 0: all-zero group, 1: FMA quotient, 2: direct division
+};
+
+__device__ __forceinline__ GroupScale scale_from_s(float s) {
+  GroupScale g;
+  g.s = s;
+  if (s == 0.0f) {
+    g.rcp = 0.0f;
+    g.mode = 0;
+  } else if (s >= 0x1p-100f) {
+    g.rcp = 1.0f / s;  // IEEE division (correctly rounded)
+    g.mode = 1;
+  } else {
+    g.rcp = 0.0f;
+    g.mode = 2;
+  }
+  return g;
+}
+
+// amax is the bit pattern of a non-negative bf16; the scale is RN32(amax/127)
+// (an IEEE division, correctly rounded), 0 only for amax = 0.
+__device__ __forceinline__ GroupScale make_scale(uint32_t amax_bits) {
+  return scale_from_s(__uint_as_float(amax_bits << 16) / 127.0f);
+}
+
+__device__ __forceinline__ float quotient(float x, const GroupScale& g) {
+  if (g.mode == 1) {
+    const float q0 = x * g.rcp;
+    const float e = __builtin_fmaf(-q0, g.s, x);
+    return __builtin_fmaf(e, g.rcp, q0);
+  }
+  return x / g.s;
+}
+
+template <bool SR>
+__device__ __forceinline__ int code_of(float x, const GroupScale& g, float u) {
+  if (g.mode == 0) return 0;
+  const float v = quotient(x, g);
+  float r;
+  if constexpr (SR) {
+    r = floorf(v + u);
+  } else {
+    r = rintf(v);  // round half to even
+  }
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)d << 24);
+}
+
+__device__ __forceinline__ float elem(const uint4& v, int j) {
+  const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+  return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+}
+
+// Uniforms of the 8 elements starting at logical index e0.  ALIGNED4: e0 is
+// a multiple of 4, so the chunk needs exactly two Philox blocks.
+template <bool ALIGNED4>
+__device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, uint64_t e0,
+                                               float u[8]) {
+  if constexpr (ALIGNED4) {
+    const uint64_t b = offset + (e0 >> 2);
+    const u32x4 w0 = philox_block(seed, b);
+    const u32x4 w1 = philox_block(seed, b + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[j] = word_to_uniform(w0.w[j]);
+      u[4 + j] = word_to_uniform(w1.w[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t e = e0 + j;
+      const u32x4 w = philox_block(seed, offset + (e >> 2));
+      const uint32_t k = (uint32_t)(e & 3);
+      const uint32_t word = k == 0 ? w.w[0] : k == 1 ? w.w[1] : k == 2 ? w.w[2] : w.w[3];
+      u[j] = word_to_uniform(word);
+    }
+  }
+}
+
+// Codes of one chunk under one scale per element (g[j]); returns 8 bytes.
+template <bool SR, bool ALIGNED4, bool PER_ELEM_SCALE>
+__device__ __forceinline__ uint2 quantize_chunk(const uint4& v, const GroupScale* g,
+                                                uint64_t seed, uint64_t offset, uint64_t e0) {
+  float u[8];
+  if constexpr (SR) {
+    chunk_uniforms<ALIGNED4>(seed, offset, e0, u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = 0.0f;
+  }
+  int c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = code_of<SR>(elem(v, j), g[PER_ELEM_SCALE ? j : 0], u[j]);
+  return make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+}
+
+__device__ __forceinline__ void store_partial(int8_t* dst, uint2 codes, int n) {
+  const uint64_t all = ((uint64_t)codes.y << 32) | codes.x;
+  for (int j = 0; j < n; ++j) dst[j] = (int8_t)(all >> (8 * j));
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise, one wave per row: the row stays in registers between the absmax
+// and the quantize sweep, so it is read from HBM once.  NV chunks per lane
+// cover rows of up to NV * 512 elements.
+
+template <int NV, bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(kThreads) void quant_rows_wave(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const uint16_t* xr = x + r * ldx;
+  uint4 v[NV];
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t c0 = (int64_t)(i * 64 + lane) * 8;
+    if (c0 < cols) {
+      v[i] = *reinterpret_cast<const uint4*>(xr + c0);
+      if (c0 + 8 > cols) v[i] = keep_first(v[i], (int)(cols - c0));
+    } else {
+      v[i] = make_uint4(0, 0, 0, 0);
+    }
+    m2 = absmax_bits(m2, v[i]);
+  }
+  const uint32_t amax = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
+  const GroupScale g = make_scale(amax);
+  if (lane == 0) scale[r] = g.s;
+  int8_t* qr = q + r * ldq;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t c0 = (int64_t)(i * 64 + lane) * 8;
+    if (c0 < cols) {
+      const uint2 codes =
+          quantize_chunk<SR, ALIGNED4, false>(v[i], &g, seed, offset, (uint64_t)(r * cols + c0));
+      if (c0 + 8 <= cols)
+        *reinterpret_cast<uint2*>(qr + c0) = codes;
+      else
+        store_partial(qr + c0, codes, (int)(cols - c0));
+    }
+  }
+}
+
+// Row-wise, one block per row, for rows longer than a wave holds: an absmax
+// sweep, then a quantize sweep that re-reads the row (from L2 / MALL).
+template <bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(kThreads) void quant_rows_block(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
+  __shared__ uint32_t red[kWavesPerBlock];
+  const int64_t r = blockIdx.x;
+  const uint16_t* xr = x + r * ldx;
+  const int64_t nchunks = (cols + 7) / 8;
+  us2 m2 = {0, 0};
+  constexpr int U = 4;
+  for (int64_t base = threadIdx.x; base < nchunks; base += (int64_t)kThreads * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t ch = base + (int64_t)k * kThreads;
+      v[k] = ch < nchunks ? *reinterpret_cast<const uint4*>(xr + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t ch = base + (int64_t)k * kThreads;
+      if (ch * 8 + 8 > cols && ch < nchunks) v[k] = keep_first(v[k], (int)(cols - ch * 8));
+      m2 = absmax_bits(m2, v[k]);
+    }
+  }
+  uint32_t m = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) m = max(m, red[w]);
+  const GroupScale g = make_scale(m);
+  if (threadIdx.x == 0) scale[r] = g.s;
+  int8_t* qr = q + r * ldq;
+  for (int64_t ch = threadIdx.x; ch < nchunks; ch += kThreads) {
+    const int64_t c0 = ch * 8;
+    uint4 v = *reinterpret_cast<const uint4*>(xr + c0);
+    const uint2 codes =
+        quantize_chunk<SR, ALIGNED4, false>(v, &g, seed, offset, (uint64_t)(r * cols + c0));
+    if (c0 + 8 <= cols)
+      *reinterpret_cast<uint2*>(qr + c0) = codes;
+    else
+      store_partial(qr + c0, codes, (int)(cols - c0));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column-wise.  A column tile is 512 columns: each lane owns 8 adjacent
+// columns, each wave walks rows.  Pass 1 writes per-slab column maxima (as
+// bf16 bit patterns) to the workspace, pass 2 reduces the slabs into the
+// scales, pass 3 quantizes.
+
+constexpr int kColTile = 512;
+
+__global__ __launch_bounds__(kThreads) void col_absmax_partial(const uint16_t* __restrict__ x,
+                                                               int64_t rows, int64_t cols,
+                                                               int64_t ldx, int64_t rows_per_slab,
+                                                               uint16_t* __restrict__ part,
+                                                               int64_t part_ld) {
+  __shared__ uint4 red[kWavesPerBlock][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_slab;
+  const int64_t r_end = min(rows, r_begin + rows_per_slab);
+  us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  if (c0 < cols) {
+    const bool tail = c0 + 8 > cols;
+    const int ntail = (int)(cols - c0);
+    int64_t r = r_begin + wave;
+    constexpr int U = 4;
+    for (; r + (U - 1) * kWavesPerBlock < r_end; r += U * kWavesPerBlock) {
+      uint4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        v[k] = *reinterpret_cast<const uint4*>(x + (r + k * kWavesPerBlock) * ldx + c0);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if (tail) v[k] = keep_first(v[k], ntail);
+        m[0] = __builtin_elementwise_max(m[0], as_us2(v[k].x & 0x7FFF7FFFu));
+        m[1] = __builtin_elementwise_max(m[1], as_us2(v[k].y & 0x7FFF7FFFu));
+        m[2] = __builtin_elementwise_max(m[2], as_us2(v[k].z & 0x7FFF7FFFu));
+        m[3] = __builtin_elementwise_max(m[3], as_us2(v[k].w & 0x7FFF7FFFu));
+      }
+    }
+    for (; r < r_end; r += kWavesPerBlock) {
+      uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + c0);
+      if (tail) v = keep_first(v, ntail);
+      m[0] = __builtin_elementwise_max(m[0], as_us2(v.x & 0x7FFF7FFFu));
+      m[1] = __builtin_elementwise_max(m[1], as_us2(v.y & 0x7FFF7FFFu));
+      m[2] = __builtin_elementwise_max(m[2], as_us2(v.z & 0x7FFF7FFFu));
+      m[3] = __builtin_elementwise_max(m[3], as_us2(v.w & 0x7FFF7FFFu));
+    }
+  }
+  red[wave][lane] = make_uint4(__builtin_bit_cast(uint32_t, m[0]), __builtin_bit_cast(uint32_t, m[1]),
+                               __builtin_bit_cast(uint32_t, m[2]), __builtin_bit_cast(uint32_t, m[3]));
+  __syncthreads();
+  if (wave == 0 && c0 < cols) {
+    us2 t[4] = {m[0], m[1], m[2], m[3]};
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) {
+      const uint4 o = red[w][lane];
+      t[0] = __builtin_elementwise_max(t[0], as_us2(o.x));
+      t[1] = __builtin_elementwise_max(t[1], as_us2(o.y));
+      t[2] = __builtin_elementwise_max(t[2], as_us2(o.z));
+      t[3] = __builtin_elementwise_max(t[3], as_us2(o.w));
+    }
+    *reinterpret_cast<uint4*>(part + (int64_t)blockIdx.y * part_ld + c0) =
+        make_uint4(__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
+                   __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3]));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void col_scale_finalize(const uint16_t* __restrict__ part,
+                                                               int64_t part_ld, int64_t slabs,
+                                                               int64_t cols,
+                                                               float* __restrict__ scale) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  uint32_t m = 0;
+  for (int64_t s = 0; s < slabs; ++s) m = max(m, (uint32_t)part[s * part_ld + c]);
+  scale[c] = __uint_as_float(m << 16) / 127.0f;
+}
+
+template <bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(kThreads) void quant_cols(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int64_t cols, int64_t ldx,
+                                                       int64_t rows_per_block,
+                                                       const float* __restrict__ scale,
+                                                       int8_t* __restrict__ q, int64_t ldq,
+                                                       uint64_t seed, uint64_t offset) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
+  if (c0 >= cols) return;
+  // row blocks run last-to-first, so the rows pass 1 touched last (still in
+  // L2 / MALL) are read first
+  const int64_t rb = (int64_t)gridDim.y - 1 - blockIdx.y;
+  const int64_t r_begin = rb * rows_per_block;
+  const int64_t r_end = min(rows, r_begin + rows_per_block);
+  const int nvalid = (int)min((int64_t)8, cols - c0);
+  GroupScale g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? scale[c0 + j] : 0.0f);
+  for (int64_t r = r_begin + wave; r < r_end; r += kWavesPerBlock) {
+    uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + c0);
+    const uint2 codes =
+        quantize_chunk<SR, ALIGNED4, true>(v, g, seed, offset, (uint64_t)(r * cols + c0));
+    int8_t* dst = q + r * ldq + c0;
+    if (nvalid == 8)
+      *reinterpret_cast<uint2*>(dst) = codes;
+    else
+      store_partial(dst, codes, nvalid);
+  }
+}
+
+struct ColPlan {
+  int64_t col_tiles, slabs, rows_per_slab, part_ld;
+};
+
+ColPlan col_plan(int64_t rows, int64_t cols) {
+  ColPlan p;
+  p.col_tiles = (cols + kColTile - 1) / kColTile;
+  int64_t slabs = (2048 + p.col_tiles - 1) / max(p.col_tiles, (int64_t)1);
+  slabs = min(slabs, (int64_t)256);
+  slabs = min(slabs, max((int64_t)1, (rows + 15) / 16));
+  slabs = max(slabs, (int64_t)1);
+  p.rows_per_slab = max((int64_t)1, (rows + slabs - 1) / slabs);
+  p.slabs = rows > 0 ? (rows + p.rows_per_slab - 1) / p.rows_per_slab : 1;
+  p.part_ld = (cols + 7) / 8 * 8;
+  return p;
+}
+
+template <int NV>
+void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
+                    int64_t ldq, float* scale, int round, uint64_t seed, uint64_t offset,
+                    hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + kWavesPerBlock - 1) / kWavesPerBlock));
+  const bool a4 = (cols % 4) == 0;
+  if (round == 1) {
+    if (a4)
+      quant_rows_wave<NV, true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    else
+      quant_rows_wave<NV, true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+  } else {
+    quant_rows_wave<NV, false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
+                                   uint64_t offset, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t per_lane = (cols + 511) / 512;  // 16-byte chunks per lane
+  if (per_lane <= 1)
+    launch_rows_nv<1>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 2)
+    launch_rows_nv<2>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 4)
+    launch_rows_nv<4>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 8)
+    launch_rows_nv<8>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 12)
+    launch_rows_nv<12>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 16)
+    launch_rows_nv<16>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 28)
+    launch_rows_nv<28>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else {
+    const dim3 grid((unsigned)rows);
+    const bool a4 = (cols % 4) == 0;
+    if (round == 1) {
+      if (a4)
+        quant_rows_block<true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+      else
+        quant_rows_block<true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    } else {
+      quant_rows_block<false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    }
+  }
+  return hipGetLastError();
+}
+
+size_t colwise_workspace_bytes(int64_t rows, int64_t cols) {
+  const ColPlan p = col_plan(rows, cols);
+  return (size_t)(p.slabs * p.part_ld * 2);
+}
+
+hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
+                                   uint64_t offset, void* ws, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const ColPlan p = col_plan(rows, cols);
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  if (rows > 0) {
+    col_absmax_partial<<<dim3((unsigned)p.col_tiles, (unsigned)p.slabs), kThreads, 0, stream>>>(
+        x, rows, cols, ldx, p.rows_per_slab, part, p.part_ld);
+  }
+  col_scale_finalize<<<dim3((unsigned)((cols + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(
+      part, p.part_ld, rows > 0 ? p.slabs : 0, cols, scale);
+  if (rows == 0) return hipGetLastError();
+  // quantize pass: 32 rows per block (more when rows would exceed the grid's y limit)
+  const int64_t rpb = max((int64_t)32, (rows + 65534) / 65535);
+  const dim3 grid((unsigned)p.col_tiles, (unsigned)((rows + rpb - 1) / rpb));
+  const bool a4 = (cols % 4) == 0;
+  if (round == 1) {
+    if (a4)
+      quant_cols<true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, rpb, scale, q, ldq, seed, offset);
+    else
+      quant_cols<true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, rpb, scale, q, ldq, seed, offset);
+  } else {
+    quant_cols<false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, rpb, scale, q, ldq, seed, offset);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+
+namespace {
+__global__ __launch_bounds__(kThreads) void philox_fill(uint64_t seed, uint64_t offset,
+                                                        int64_t n_blocks, uint4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n_blocks) return;
+  const u32x4 w = philox_block(seed, offset + (uint64_t)i);
+  out[i] = make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]);
+}
+}  // namespace
+
+hipError_t launch_philox(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
+                         hipStream_t stream) {
+  if (n_blocks == 0) return hipSuccess;
+  philox_fill<<<dim3((unsigned)((n_blocks + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(
+      seed, offset, n_blocks, reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace i8mp
