@@ -1,0 +1,277 @@
+"""Benchmark: one INT8 mixed-precision linear-layer training step on one MI355X.
+
+A step is the whole hot path once: forward Y = X @ W.T, grad-input dX = dY @ W
+and grad-weight dW = dY.T @ X, each GEMM quantizing its two bf16 operands
+along its contraction (6 quantize passes: X row, W row, dY row, W col, dY col,
+X col) and running the scaled INT8 matmul (NT, NN, TN) with the fp32 scale
+epilogue to bf16.  Workload: the square GEMM sweep's largest size,
+M = N = K = 4096 (X ~ N(0,1) with outlier channels, W ~ N(0,0.02),
+dY ~ N(0,1e-3), bf16, synthetic, seeded).
+
+Every launch goes through the C ABI on torch's current stream.  HIP events
+recorded on that stream between the launches give each kernel's duration
+inside the timed region.  Inputs rotate over several sets (more bytes than
+the 256 MB MALL) so every step reads its operands from HBM.
+
+Printed: one JSON line (rank 0).  `value` is the step's INT8 GEMM throughput,
+3 * 2*M*N*K / step time, in TOPS; `roofline` describes the GEMM with the
+largest share of the step; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same step (64 of the 4096 tokens).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "INT8 scaled-GEMM TOPS (fwd/dgrad/wgrad) as % of INT8 MFMA peak; quant GB/s"
+COUNTERS = os.path.join(ROOT, "profiles", "gemm_counters_square_4096.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--size", type=int, default=4096, help="M = N = K")
+    ap.add_argument("--rounding", default="rne", choices=["rne", "sr"])
+    ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "internal.h"):
+        with open(os.path.join(ROOT, "int8_mixed_precision_rowwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per dispatch of `kernel` from the committed counter summary,
+    if it was taken on the current GEMM source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    fields = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    key = f"hbm_bytes_per_dispatch_{kernel}"
+    return float(fields[key]) if key in fields else None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding "
+              "of this path is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int8_mixed_precision_rowwise_amd as i8
+    from workloads import linear_inputs, square
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = args.size
+    M = N = K = n
+    shape = square(n)
+    sets = []
+    for s in range(args.sets):
+        t = linear_inputs(shape, seed=s, device=dev)
+        sets.append((t["X"], t["W"], t["dY"]))
+    L = i8.lib
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    r = 0 if args.rounding == "rne" else 1
+    seed = 1234
+
+    def p(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    # outputs and int8 intermediates (dense, K and N multiples of 16 here)
+    qX = torch.empty((M, K), dtype=torch.int8, device=dev)
+    qW = torch.empty((N, K), dtype=torch.int8, device=dev)
+    qdY = torch.empty((M, N), dtype=torch.int8, device=dev)
+    qWc = torch.empty((N, K), dtype=torch.int8, device=dev)
+    qdYc = torch.empty((M, N), dtype=torch.int8, device=dev)
+    qXc = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sX = torch.empty(M, device=dev)
+    sW = torch.empty(N, device=dev)
+    sdY = torch.empty(M, device=dev)
+    sWc = torch.empty(K, device=dev)
+    sdYc = torch.empty(N, device=dev)
+    sXc = torch.empty(K, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    wsb = max(L.i8mp_quantize_colwise_workspace_bytes(N, K), L.i8mp_quantize_colwise_workspace_bytes(M, N),
+              L.i8mp_quantize_colwise_workspace_bytes(M, K))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    names = ["quant_row_X", "quant_row_W", "gemm_NT_fwd", "quant_row_dY", "quant_col_W",
+             "gemm_NN_dgrad", "quant_col_dY", "quant_col_X", "gemm_TN_wgrad"]
+
+    def launches(X, W, dY, step):
+        off = step << 44
+        ro = lambda j: off + (j << 40)  # noqa: E731  (per-pass Philox offsets)
+        return [
+            lambda: L.i8mp_quantize_rowwise(p(X), M, K, K, p(qX), K, p(sX), r, seed, ro(0), sp),
+            lambda: L.i8mp_quantize_rowwise(p(W), N, K, K, p(qW), K, p(sW), r, seed, ro(1), sp),
+            lambda: L.i8mp_int8_scaled_mm(0, M, N, K, p(qX), K, p(sX), p(qW), K, p(sW), p(Y), N, sp),
+            lambda: L.i8mp_quantize_rowwise(p(dY), M, N, N, p(qdY), N, p(sdY), r, seed, ro(2), sp),
+            lambda: L.i8mp_quantize_colwise(p(W), N, K, K, p(qWc), K, p(sWc), r, seed, ro(3), p(ws), wsb, sp),
+            lambda: L.i8mp_int8_scaled_mm(1, M, K, N, p(qdY), N, p(sdY), p(qWc), K, p(sWc), p(dX), K, sp),
+            lambda: L.i8mp_quantize_colwise(p(dY), M, N, N, p(qdYc), N, p(sdYc), r, seed, ro(4), p(ws), wsb, sp),
+            lambda: L.i8mp_quantize_colwise(p(X), M, K, K, p(qXc), K, p(sXc), r, seed, ro(5), p(ws), wsb, sp),
+            lambda: L.i8mp_int8_scaled_mm(2, N, K, M, p(qdYc), N, p(sdYc), p(qXc), K, p(sXc), p(dW), K, sp),
+        ]
+
+    plans = [launches(*sets[s], 0) for s in range(args.sets)]
+
+    def run_step(i, events=None):
+        plan = plans[i % args.sets]
+        for j, f in enumerate(plan):
+            if events is not None:
+                events[j].record(stream)
+            st = f()
+            if st != 0:
+                raise RuntimeError(f"{names[j]} failed with status {st}")
+        if events is not None:
+            events[len(plan)].record(stream)
+
+    # the primitive chain is the library's linear_fwd / linear_bwd chain
+    run_step(0)
+    Yc, dXc, dWc = Y.clone(), dX.clone(), dW.clone()
+    X0, W0, dY0 = sets[0]
+    ok = (torch.equal(i8.linear_fwd(X0, W0, args.rounding, seed, 0).view(torch.int16), Yc.view(torch.int16))
+          and all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+                  for a, b in zip(i8.linear_bwd(dY0, X0, W0, args.rounding, seed, 0), (dXc, dWc))))
+    if not ok:
+        raise RuntimeError("primitive chain differs from linear_fwd/linear_bwd")
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        run_step(i, ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / args.steps
+
+    per = {nm: 0.0 for nm in names}
+    for i in range(args.steps):
+        for j, nm in enumerate(names):
+            per[nm] += ev[i][j].elapsed_time(ev[i][j + 1])
+    per = {nm: v / args.steps for nm, v in per.items()}  # ms per launch (colwise: its 3 kernels)
+
+    gemm_ops = 2.0 * M * N * K
+    breakdown = {}
+    for nm, ms in per.items():
+        d = {"us": round(ms * 1e3, 2)}
+        if nm.startswith("gemm"):
+            tops = gemm_ops / (ms * 1e-3) / 1e12
+            d.update(tops=round(tops, 1), frac_int8_peak=round(tops / PEAK_INT8_TOPS, 4))
+        else:
+            tensor = {"X": (M, K), "W": (N, K), "dY": (M, N)}[nm.split("_")[-1]]
+            nscale = tensor[0] if "_row_" in nm else tensor[1]
+            algo = 3.0 * tensor[0] * tensor[1] + 4.0 * nscale
+            gbs = algo / (ms * 1e-3) / 1e9
+            d.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        breakdown[nm] = d
+    gemms = [nm for nm in names if nm.startswith("gemm")]
+    dom = max(gemms, key=lambda nm: per[nm])
+    achieved = gemm_ops / (per[dom] * 1e-3) / 1e12
+    traffic = read_traffic(dom)
+    value = 3 * gemm_ops / (step_ms * 1e-3) / 1e12
+
+    # context: torch bf16 matmul (hipBLASLt) at the same shape and layouts
+    a = sets[0][0]
+    b = sets[0][1]
+    ctx = {}
+    for lay, fn in (("NT", lambda: a @ b.t()), ("NN", lambda: a @ b), ("TN", lambda: a.t() @ b)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ctx[lay] = round(gemm_ops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_tokens, N, K, args.rounding)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"linear_fwd_bwd_square_{n}", "M": M, "N": N, "K": K,
+                   "rounding": args.rounding, "input_sets": args.sets},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+        "step_gemm_frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+        "context_torch_bf16_matmul_tflops": ctx,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(tokens: int, N: int, K: int, rounding: str):
+    """The CPU oracle, as it is, on the same layer step with `tokens` of the
+    tokens (X [tokens, K], dY [tokens, N], W [N, K] in full)."""
+    import oracle
+    from workloads import LinearShape, bf16_bits, linear_inputs
+
+    t = linear_inputs(LinearShape("cpu_sample", tokens, N, K), seed=0)
+    X, W, dY = (bf16_bits(t[k]) for k in ("X", "W", "dY"))
+    r = oracle.RNE if rounding == "rne" else oracle.SR
+    t0 = time.perf_counter()
+    oracle.linear_fwd(X, W, r, 1234, 0)
+    oracle.linear_bwd(dY, X, W, r, 1234, 0)
+    dt = time.perf_counter() - t0
+    ops = 3 * 2.0 * tokens * N * K
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"oracle linear fwd+bwd (6 quantize passes + NT/NN/TN) at {tokens} of the "
+                      f"tokens: X [{tokens},{K}], W [{N},{K}], dY [{tokens},{N}], single thread"}
+
+
+if __name__ == "__main__":
+    main()

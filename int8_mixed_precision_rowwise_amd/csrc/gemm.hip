@@ -19,11 +19,14 @@
 // 2j + h of a group addresses row k0 + j, columns n0 + 8h .. n0 + 8h + 7 of
 // a [k][n] tile, lane i therefore receives column n0 + i at rows k0 .. k0+7.
 //
-// MFMA 32x32x32 i8 operand/result layout: lane l supplies row l % 32 of the
-// A block and column l % 32 of the B block with 16 contraction values in
-// k order (k = 16 * (l / 32) + 0..15 of the 32-wide step); result register v
-// of lane l holds row 8 * (v / 4) + 4 * (l / 32) + v % 4, column l % 32.
+// MFMA 32x32x32 i8 operand/result layout: lane l supplies row l % 32 of its
+// first operand block and column l % 32 of its second with 16 contraction
+// values in k order (k = 16 * (l / 32) + 0..15 of the 32-wide step); result
+// register v of lane l holds row 8 * (v / 4) + 4 * (l / 32) + v % 4 (an index
+// of the first operand), column l % 32 (of the second).
 #include "internal.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set by the slab loads
 
 namespace i8mp {
 namespace {
@@ -157,8 +160,91 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
   tn = in_group / gm;
 }
 
-template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32>
-__global__ __launch_bounds__(kThreads) void gemm_i8(int64_t M, int64_t N, int64_t K,
+// Scales of the workgroup's BM rows and BN columns, staged in LDS once so
+// the epilogue reads them with ds_read (global loads would have to wait
+// behind the output stores, which share the vector-memory counter).
+template <int BM, int BN, bool OUT_I32>
+__device__ __forceinline__ void stage_scales(float* s_lds, int64_t m0, int64_t n0, int64_t M,
+                                             int64_t N, const float* __restrict__ sa,
+                                             const float* __restrict__ sb, int t) {
+  if constexpr (!OUT_I32) {
+    for (int i = t; i < BM + BN; i += kThreads) {
+      float v = 0.0f;
+      if (i < BM) {
+        if (m0 + i < M) v = sa[m0 + i];
+      } else if (n0 + (i - BM) < N) {
+        v = sb[n0 + (i - BM)];
+      }
+      s_lds[i] = v;
+    }
+  }
+  __syncthreads();
+}
+
+// Epilogue of one wave's TM x TN blocks of 32 x 32 accumulators whose
+// top-left output is (mw, nw) = tile origin + (wm, wn).  The MFMAs take the
+// B fragment as their first operand, so in block (i, j) lane l holds output
+// row m = mw + 32i + l % 32 and register v holds column
+// n = nw + 32j + 8(v / 4) + 4(l / 32) + v % 4: four consecutive registers
+// are four adjacent outputs of one row, stored together (8 bytes of bf16 or
+// 16 bytes of int32) when VEC.  y = RN(RN(float(acc) * sa[m]) * sb[n]).
+// s_lds holds sa[tile rows] then sb[tile columns].
+template <int BM, int TM, int TN, bool OUT_I32, bool VEC>
+__device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                           int wm, int wn, int64_t M, int64_t N,
+                                           const float* s_lds, void* __restrict__ Cv,
+                                           int64_t ldc, int lane) {
+  const int mr = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wm + 32 * i + mr;
+      if (m >= M) continue;
+      float sam = 0.0f;
+      if constexpr (!OUT_I32) sam = s_lds[wm + 32 * i + mr];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cn = wn + 32 * j + 8 * q + nq;  // column within the tile
+        const int64_t n4 = n0 + cn;
+        if (n4 >= N) continue;
+        if constexpr (OUT_I32) {
+          int32_t* row = static_cast<int32_t*>(Cv) + m * ldc;
+          if (VEC && n4 + 4 <= N) {
+            *reinterpret_cast<v4i*>(row + n4) =
+                (v4i){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n4 + e < N) row[n4 + e] = acc[i][j][4 * q + e];
+          }
+        } else {
+          const float4 sbq = *reinterpret_cast<const float4*>(s_lds + BM + cn);
+          const float sbv[4] = {sbq.x, sbq.y, sbq.z, sbq.w};
+          __bf16 h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float y = (float)acc[i][j][4 * q + e];
+            y = y * sam;
+            y = y * sbv[e];
+            h[e] = (__bf16)y;  // round to nearest even
+          }
+          __bf16* row = static_cast<__bf16*>(Cv) + m * ldc;
+          if (VEC && n4 + 4 <= N) {
+            *reinterpret_cast<uint2*>(row + n4) = __builtin_bit_cast(uint2, h);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n4 + e < N) row[n4 + e] = h[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
+__global__ __launch_bounds__(kThreads) void gemm_i8_general(int64_t M, int64_t N, int64_t K,
                                                     const int8_t* __restrict__ A, int64_t lda,
                                                     const float* __restrict__ sa,
                                                     const int8_t* __restrict__ B, int64_t ldb,
@@ -212,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8(int64_t M, int64_t N, int64_
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
     if (more) {
       sa_stage.store(nxt, t);
@@ -221,31 +307,271 @@ __global__ __launch_bounds__(kThreads) void gemm_i8(int64_t M, int64_t N, int64_
     __syncthreads();
   }
 
-  // epilogue
+  // every wave has passed its last LDS read of the slabs before any scale lands
+  __syncthreads();
+  float* s_lds = reinterpret_cast<float*>(lds);
+  stage_scales<BM, BN, OUT_I32>(s_lds, m0, n0, M, N, sa, sb, t);
+  store_tile<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
+}
+
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel, used when the contraction length is a multiple of 16.
+// Operand slabs go straight from memory into LDS with buffer_load ... lds
+// (16 bytes per lane, one lane-major KiB per instruction), STAGES slabs deep
+// and issued STAGES - 1 slabs ahead of use, so no registers stage them and
+// the loads of later slabs overlap the MFMAs of the current one.  Each lane
+// picks the source of the LDS chunk it lands in, which realizes the LDS
+// swizzles above.  Chunks outside the operand (tails of M, N or K) get an
+// out-of-range offset, which the buffer unit returns as zeros.  MFMA
+// fragments are double-buffered in registers across the 32-wide steps.
+
+constexpr int STAGES = 4;
+constexpr uint32_t kOob = 0x7FFFFFF0u;  // offset past every buffer's range
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations
+// are outstanding and leaves the other counters alone (gfx9 encoding).
+constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Scheduling template for one group of MFMAs: each MFMA is followed by a
+// share of the LDS fragment reads, the slab loads and their address
+// arithmetic, so the matrix core gets a new MFMA while the other units work
+// instead of idling between back-to-back MFMA groups.
+template <int NMFMA, int NDS, int NVM>
+__device__ __forceinline__ void interleave() {
+  constexpr int ds_per = (NDS + NMFMA - 1) / NMFMA;
+  constexpr int vm_per = (NVM + NMFMA - 1) / NMFMA;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t n = n0 + wn0 + 32 * j + (lane & 31);
-    if (n >= N) continue;
-    float sbn = 0.0f;
-    if constexpr (!OUT_I32) sbn = sb[n];
+  for (int m = 0; m < NMFMA; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (m * ds_per < NDS) __builtin_amdgcn_sched_group_barrier(0x100, ds_per, 0);  // DS read
+    if (m * vm_per < NVM) __builtin_amdgcn_sched_group_barrier(0x020, vm_per, 0);  // VMEM read
+  }
+}
+
+// Workgroup barrier for the pipelined loop: waits for this wave's LDS reads
+// (so no wave refills a buffer another wave is still reading) but not for
+// the slab loads in flight, whose completion is tracked with waitcnt_vm.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);  // nothing is scheduled across the barrier
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unchanged
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int R, bool KMAJOR>
+struct Dma {
+  static constexpr int kInst = R * BK / 1024 / 4;  // instructions per wave per slab
+  v4u rsrc;              // buffer descriptor (scalar registers)
+  uint32_t off0[kInst];  // offset of this lane's chunk in slab 0
+  int kpos[kInst];       // contraction index of the chunk within a slab (BK: outside the operand)
+  uint32_t kstride;      // offset advance per contraction index
+
+  // p: operand base, ld: leading dim (bytes), mn0: first output row/col of
+  // the tile, MN: output extent along this operand, K: contraction length.
+  // Buffer descriptor of `bytes` bytes at `base`, built from wave-uniform
+  // values (read from lane 0) so that it lives in scalar registers; out of
+  // range offsets read as zero.
+  static __device__ __forceinline__ v4u make_rsrc(const int8_t* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4u d;
+    d.x = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    d.y = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu;  // stride 0
+    d.z = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    d.w = 0x00020000u;
+    return d;
+  }
+
+  __device__ __forceinline__ void init(const int8_t* p, int64_t ld, int64_t mn0, int64_t MN,
+                                       int64_t K, int wave, int lane) {
+    if constexpr (KMAJOR) {
+      const int64_t rows_in = min((int64_t)R, MN - mn0);
+      rsrc = make_rsrc(p + mn0 * ld, rows_in * ld);
+      kstride = 1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int j = 0; j < kInst; ++j) {
+        const int pc = (wave + 4 * j) * 64 + lane;  // chunk index within the LDS tile
+        const int r = pc >> 2;
+        const int c = (pc & 3) ^ ((r >> 1) & 3);
+        kpos[j] = r < rows_in ? 16 * c : BK;  // BK never passes the slab limit
+        off0[j] = (uint32_t)(r * ld + 16 * c);
+      }
+    } else {
+      constexpr int CPR = R / 16;
+      const int64_t cols_in = min((int64_t)R, MN - mn0);
+      rsrc = make_rsrc(p + mn0, (K - 1) * ld + cols_in);
+      kstride = (uint32_t)ld;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m >= M) continue;
-        if constexpr (OUT_I32) {
-          static_cast<int32_t*>(Cv)[m * ldc + n] = acc[i][j][v];
-        } else {
-          float y = (float)acc[i][j][v];
-          y = y * sa[m];
-          y = y * sbn;
-          const __bf16 h = (__bf16)y;  // round to nearest even
-          static_cast<__bf16*>(Cv)[m * ldc + n] = h;
-        }
+      for (int j = 0; j < kInst; ++j) {
+        const int pc = (wave + 4 * j) * 64 + lane;
+        const int k = pc / CPR;
+        const int c = (pc % CPR) ^ (k & 7);
+        kpos[j] = 16 * c < cols_in ? k : BK;
+        off0[j] = (uint32_t)(k * ld + 16 * c);
       }
     }
   }
+
+  // Load instruction j (one KiB of the tile) of slab `slab` (contraction
+  // offset 64 * slab) into the LDS tile `dst`.  `wave` must be wave-uniform
+  // so the LDS address stays in scalar registers.
+  __device__ __forceinline__ void issue_one(int j, int8_t* dst, int slab, int64_t K, int wave) const {
+    const int k0 = BK * slab;
+    const int limit = (int)min(K - k0, (int64_t)BK);  // contraction indices left in this slab
+    const uint32_t o = kpos[j] < limit ? off0[j] + (uint32_t)k0 * kstride : kOob;
+    const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(dst + (wave + 4 * j) * 1024)));
+    // Issued as inline assembly: the compiler then does not treat the LDS
+    // write as pending on every later LDS read (which would make it wait for
+    // all slabs in flight); arrival is tracked explicitly with waitcnt_vm and
+    // the workgroup barrier.
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(l), "v"(o), "s"(rsrc)
+                 : "memory", "m0");
+  }
+
+  __device__ __forceinline__ void issue(int8_t* dst, int slab, int64_t K, int wave) const {
+#pragma unroll
+    for (int j = 0; j < kInst; ++j) issue_one(j, dst, slab, K, wave);
+  }
+};
+
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
+__global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
+                                                              const int8_t* __restrict__ A, int64_t lda,
+                                                              const float* __restrict__ sa,
+                                                              const int8_t* __restrict__ B, int64_t ldb,
+                                                              const float* __restrict__ sb,
+                                                              void* __restrict__ Cv, int64_t ldc) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SLAB = A_BYTES + B_BYTES;
+  constexpr int PER = Dma<BM, A_KMAJOR>::kInst + Dma<BN, B_KMAJOR>::kInst;  // loads per wave per slab
+  // LDS read instructions per 32-wide step: one per K-major fragment, two per transposed one
+  constexpr int FRAG_READS = TM * (A_KMAJOR ? 1 : 2) + TN * (B_KMAJOR ? 1 : 2);
+  __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * SLAB];
+
+  __shared__ __attribute__((aligned(16))) float s_lds[BM + BN];  // scales of the tile
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  // the epilogue's scales, fetched now so their latency hides under the main loop
+  constexpr int NPRE = (BM + BN + kThreads - 1) / kThreads;
+  float s_pre[NPRE];
+#pragma unroll
+  for (int r = 0; r < NPRE; ++r) {
+    const int i = t + r * kThreads;
+    s_pre[r] = 0.0f;
+    if (!OUT_I32 && i < BM + BN) {
+      if (i < BM) {
+        if (m0 + i < M) s_pre[r] = sa[m0 + i];
+      } else if (n0 + (i - BM) < N) {
+        s_pre[r] = sb[n0 + (i - BM)];
+      }
+    }
+  }
+
+  Dma<BM, A_KMAJOR> da;
+  Dma<BN, B_KMAJOR> db;
+  da.init(A, lda, m0, M, K, wave, lane);
+  db.init(B, ldb, n0, N, K, wave, lane);
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (v16i){};
+
+  const int nk = (int)((K + BK - 1) / BK);
+  v4i a0[TM], b0[TN], a1[TM], b1[TN];
+  // Slabs past the end are still "loaded", with out-of-range offsets (the
+  // buffer unit writes zeros into a buffer nobody reads), so every iteration
+  // issues the same number of loads and slab kt + 1 has always landed once
+  // at most 2 * PER loads of this wave are outstanding.
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    da.issue(lds + s * SLAB, s, K, wave);
+    db.issue(lds + s * SLAB + A_BYTES, s, K, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * PER));
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a0[i] = frag<BM, A_KMAJOR>(lds, wm0 + 32 * i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b0[j] = frag<BN, B_KMAJOR>(lds + A_BYTES, wn0 + 32 * j, 0, lane);
+
+  // Main loop, one slab per iteration, in two halves of TM * TN MFMAs.  Each
+  // MFMA is followed by at most one fragment read and one slab load, and a
+  // sched_barrier after each step keeps that order, so the matrix core is fed
+  // a new MFMA while the LDS and memory units work.
+  constexpr int NA = Dma<BM, A_KMAJOR>::kInst;
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int8_t* cur = lds + (kt % STAGES) * SLAB;
+    const int8_t* nxt = lds + ((kt + 1) % STAGES) * SLAB;
+    int8_t* dst = lds + ((kt + STAGES - 1) % STAGES) * SLAB;  // slab kt-1's buffer
+    const int ns = kt + STAGES - 1;
+#pragma unroll
+    for (int m = 0; m < TM * TN; ++m) {
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[m % TN], a0[m / TN], acc[m / TN][m % TN], 0, 0, 0);
+      if (m < TM) a1[m] = frag<BM, A_KMAJOR>(cur, wm0 + 32 * m, 1, lane);
+      else if (m < TM + TN) b1[m - TM] = frag<BN, B_KMAJOR>(cur + A_BYTES, wn0 + 32 * (m - TM), 1, lane);
+      if (m < NA) da.issue_one(m, dst, ns, K, wave);
+      else if (m < PER) db.issue_one(m - NA, dst + A_BYTES, ns, K, wave);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * PER));
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < TM * TN; ++m) {
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[m % TN], a1[m / TN], acc[m / TN][m % TN], 0, 0, 0);
+      if (m < TM) a0[m] = frag<BM, A_KMAJOR>(nxt, wm0 + 32 * m, 0, lane);
+      else if (m < TM + TN) b0[m - TM] = frag<BN, B_KMAJOR>(nxt + A_BYTES, wn0 + 32 * (m - TM), 0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (nk > 0) {  // last slab
+    const int8_t* cur = lds + ((nk - 1) % STAGES) * SLAB;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a1[i] = frag<BM, A_KMAJOR>(cur, wm0 + 32 * i, 1, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b1[j] = frag<BN, B_KMAJOR>(cur + A_BYTES, wn0 + 32 * j, 1, lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[j], a0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[j], a1[i], acc[i][j], 0, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing zero-fill loads and the scales
+#pragma unroll
+  for (int r = 0; r < NPRE; ++r)
+    if (!OUT_I32 && t + r * kThreads < BM + BN) s_lds[t + r * kThreads] = s_pre[r];
+  __syncthreads();
+  store_tile<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
+}
+
+
+template <int BM, int BN, bool AK, bool BKM, bool OUT_I32, bool VEC>
+void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+            const float* sa, const int8_t* B, int64_t ldb, const float* sb, void* C, int64_t ldc,
+            hipStream_t stream) {
+  if (fast)
+    gemm_i8_pipelined<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
+  else
+    gemm_i8_general<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
 }
 
 template <int BM, int BN, bool AK, bool BKM>
@@ -254,10 +580,23 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
                int64_t ldc, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
-  if (Ci)
-    gemm_i8<BM, BN, AK, BKM, true><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc);
-  else
-    gemm_i8<BM, BN, AK, BKM, false><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc);
+  // the pipelined kernel addresses each operand tile with 32-bit buffer
+  // offsets and zero-fills whole 16-byte chunks, so it needs K % 16 == 0 and
+  // tile extents below 2^31 bytes
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t a_ext = AK ? (int64_t)BM * lda : K * lda;
+  const int64_t b_ext = BKM ? (int64_t)BN * ldb : K * ldb;
+  const bool fast = K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024;
+  // packed stores of 4 adjacent outputs need 4-element alignment of every row
+  const uintptr_t c = Ci ? reinterpret_cast<uintptr_t>(Ci) : reinterpret_cast<uintptr_t>(Cb);
+  const bool vec = ldc % 4 == 0 && c % (Ci ? 16 : 8) == 0;
+  if (Ci) {
+    if (vec) launch<BM, BN, AK, BKM, true, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, stream);
+    else launch<BM, BN, AK, BKM, true, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, stream);
+  } else {
+    if (vec) launch<BM, BN, AK, BKM, false, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, stream);
+    else launch<BM, BN, AK, BKM, false, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, stream);
+  }
   return hipGetLastError();
 }
 
