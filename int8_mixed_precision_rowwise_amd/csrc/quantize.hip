@@ -91,27 +91,37 @@ __device__ __forceinline__ GroupScale make_scale(uint32_t amax_bits) {
   return scale_from_s(__uint_as_float(amax_bits << 16) / 127.0f);
 }
 
-__device__ __forceinline__ float quotient(float x, const GroupScale& g) {
-  if (g.mode == 1) {
-    const float q0 = x * g.rcp;
-    const float e = __builtin_fmaf(-q0, g.s, x);
-    return __builtin_fmaf(e, g.rcp, q0);
+// Quotient x / s under a known evaluation mode (1: FMA form, 2: division).
+template <int MODE>
+__device__ __forceinline__ float quotient(float x, float s, float rcp) {
+  if constexpr (MODE == 1) {
+    const float q0 = x * rcp;
+    const float e = __builtin_fmaf(-q0, s, x);
+    return __builtin_fmaf(e, rcp, q0);
+  } else {
+    return x / s;
   }
-  return x / g.s;
 }
 
-template <bool SR>
-__device__ __forceinline__ int code_of(float x, const GroupScale& g, float u) {
-  if (g.mode == 0) return 0;
-  const float v = quotient(x, g);
+// int8 code of x (as an int) under scale s with a known mode (1 or 2).
+template <bool SR, int MODE>
+__device__ __forceinline__ int code_of(float x, float s, float rcp, float u) {
+  const float v = quotient<MODE>(x, s, rcp);
   float r;
   if constexpr (SR) {
     r = floorf(v + u);
   } else {
     r = rintf(v);  // round half to even
   }
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
+  return (int)__builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
+}
+
+// Any mode, decided per element (0 gives code 0).
+template <bool SR>
+__device__ __forceinline__ int code_any(float x, const GroupScale& g, float u) {
+  if (g.mode == 1) return code_of<SR, 1>(x, g.s, g.rcp, u);
+  if (g.mode == 2) return code_of<SR, 2>(x, g.s, g.rcp, u);
+  return 0;
 }
 
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
@@ -150,8 +160,10 @@ __device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, u
   }
 }
 
-// Codes of one chunk under one scale per element (g[j]); returns 8 bytes.
-template <bool SR, bool ALIGNED4, bool PER_ELEM_SCALE>
+// Codes of one chunk.  MODE 1 or 2: every element uses that quotient form
+// with scale g[0] (g[j] when PER_ELEM_SCALE); MODE -1: each element's own
+// GroupScale decides.  Returns 8 bytes.
+template <bool SR, bool ALIGNED4, bool PER_ELEM_SCALE, int MODE>
 __device__ __forceinline__ uint2 quantize_chunk(const uint4& v, const GroupScale* g,
                                                 uint64_t seed, uint64_t offset, uint64_t e0) {
   float u[8];
@@ -163,7 +175,13 @@ __device__ __forceinline__ uint2 quantize_chunk(const uint4& v, const GroupScale
   }
   int c[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) c[j] = code_of<SR>(elem(v, j), g[PER_ELEM_SCALE ? j : 0], u[j]);
+  for (int j = 0; j < 8; ++j) {
+    const GroupScale& gj = g[PER_ELEM_SCALE ? j : 0];
+    if constexpr (MODE < 0)
+      c[j] = code_any<SR>(elem(v, j), gj, u[j]);
+    else
+      c[j] = code_of<SR, MODE>(elem(v, j), gj.s, gj.rcp, u[j]);
+  }
   return make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
 }
 
@@ -175,18 +193,13 @@ __device__ __forceinline__ void store_partial(int8_t* dst, uint2 codes, int n) {
 // ---------------------------------------------------------------------------
 // Row-wise, one wave per row: the row stays in registers between the absmax
 // and the quantize sweep, so it is read from HBM once.  NV chunks per lane
-// cover rows of up to NV * 512 elements.
+// cover rows of up to NV * 512 elements.  Waves walk rows with a grid stride;
+// with PREFETCH the next row's loads are in flight while the current row is
+// reduced, quantized and stored.
 
-template <int NV, bool SR, bool ALIGNED4>
-__global__ __launch_bounds__(kThreads) void quant_rows_wave(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const uint16_t* xr = x + r * ldx;
-  uint4 v[NV];
-  us2 m2 = {0, 0};
+template <int NV>
+__device__ __forceinline__ void load_row(uint4 (&v)[NV], const uint16_t* __restrict__ xr,
+                                         int64_t cols, int lane) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t c0 = (int64_t)(i * 64 + lane) * 8;
@@ -196,22 +209,71 @@ __global__ __launch_bounds__(kThreads) void quant_rows_wave(
     } else {
       v[i] = make_uint4(0, 0, 0, 0);
     }
-    m2 = absmax_bits(m2, v[i]);
   }
-  const uint32_t amax = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
-  const GroupScale g = make_scale(amax);
-  if (lane == 0) scale[r] = g.s;
-  int8_t* qr = q + r * ldq;
+}
+
+template <int NV, bool SR, bool ALIGNED4, int MODE>
+__device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const GroupScale& g,
+                                                  int64_t r, int64_t cols, int8_t* __restrict__ qr,
+                                                  uint64_t seed, uint64_t offset, int lane) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t c0 = (int64_t)(i * 64 + lane) * 8;
     if (c0 < cols) {
-      const uint2 codes =
-          quantize_chunk<SR, ALIGNED4, false>(v[i], &g, seed, offset, (uint64_t)(r * cols + c0));
+      uint2 codes = make_uint2(0, 0);
+      if constexpr (MODE > 0)
+        codes = quantize_chunk<SR, ALIGNED4, false, MODE>(v[i], &g, seed, offset, (uint64_t)(r * cols + c0));
       if (c0 + 8 <= cols)
         *reinterpret_cast<uint2*>(qr + c0) = codes;
       else
         store_partial(qr + c0, codes, (int)(cols - c0));
+    }
+  }
+}
+
+template <int NV, bool SR, bool ALIGNED4>
+__device__ __forceinline__ void quantize_row(const uint4 (&v)[NV], int64_t r, int64_t cols,
+                                             int8_t* __restrict__ q, int64_t ldq,
+                                             float* __restrict__ scale, uint64_t seed,
+                                             uint64_t offset, int lane) {
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) m2 = absmax_bits(m2, v[i]);
+  // the row maximum is the same in every lane: read it from lane 0 so the
+  // mode branch below is a scalar branch
+  const uint32_t amax = __builtin_amdgcn_readfirstlane(wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y)));
+  const GroupScale g = make_scale(amax);
+  if (lane == 0) scale[r] = g.s;
+  int8_t* qr = q + r * ldq;
+  if (g.mode == 1)
+    quantize_row_mode<NV, SR, ALIGNED4, 1>(v, g, r, cols, qr, seed, offset, lane);
+  else if (g.mode == 2)
+    quantize_row_mode<NV, SR, ALIGNED4, 2>(v, g, r, cols, qr, seed, offset, lane);
+  else
+    quantize_row_mode<NV, SR, ALIGNED4, 0>(v, g, r, cols, qr, seed, offset, lane);
+}
+
+template <int NV, bool SR, bool ALIGNED4, bool PREFETCH>
+__global__ __launch_bounds__(kThreads) void quant_rows_wave(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  uint4 v[NV];
+  load_row<NV>(v, x + r * ldx, cols, lane);
+  for (; r < rows; r += stride) {
+    const int64_t rn = r + stride;
+    if constexpr (PREFETCH) {
+      uint4 nv[NV];
+      if (rn < rows) load_row<NV>(nv, x + rn * ldx, cols, lane);
+      quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = nv[i];
+    } else {
+      quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
+      if (rn < rows) load_row<NV>(v, x + rn * ldx, cols, lane);
     }
   }
 }
@@ -248,14 +310,15 @@ __global__ __launch_bounds__(kThreads) void quant_rows_block(
   m = red[0];
 #pragma unroll
   for (int w = 1; w < kWavesPerBlock; ++w) m = max(m, red[w]);
-  const GroupScale g = make_scale(m);
+  const GroupScale g = make_scale(__builtin_amdgcn_readfirstlane(m));
   if (threadIdx.x == 0) scale[r] = g.s;
   int8_t* qr = q + r * ldq;
   for (int64_t ch = threadIdx.x; ch < nchunks; ch += kThreads) {
     const int64_t c0 = ch * 8;
     uint4 v = *reinterpret_cast<const uint4*>(xr + c0);
     const uint2 codes =
-        quantize_chunk<SR, ALIGNED4, false>(v, &g, seed, offset, (uint64_t)(r * cols + c0));
+        g.mode == 1 ? quantize_chunk<SR, ALIGNED4, false, 1>(v, &g, seed, offset, (uint64_t)(r * cols + c0))
+                    : quantize_chunk<SR, ALIGNED4, false, -1>(v, &g, seed, offset, (uint64_t)(r * cols + c0));
     if (c0 + 8 <= cols)
       *reinterpret_cast<uint2*>(qr + c0) = codes;
     else
@@ -329,15 +392,35 @@ __global__ __launch_bounds__(kThreads) void col_absmax_partial(const uint16_t* _
   }
 }
 
+// Column scales from the per-slab maxima: a block covers 64 columns with
+// 4 groups of slabs; every thread keeps 8 independent loads in flight.
 __global__ __launch_bounds__(kThreads) void col_scale_finalize(const uint16_t* __restrict__ part,
                                                                int64_t part_ld, int64_t slabs,
                                                                int64_t cols,
                                                                float* __restrict__ scale) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ uint32_t red[kWavesPerBlock][64];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
   uint32_t m = 0;
-  for (int64_t s = 0; s < slabs; ++s) m = max(m, (uint32_t)part[s * part_ld + c]);
-  scale[c] = __uint_as_float(m << 16) / 127.0f;
+  if (c < cols) {
+    constexpr int U = 8;
+    int64_t s = grp;
+    for (; s + (int64_t)(U - 1) * kWavesPerBlock < slabs; s += (int64_t)U * kWavesPerBlock) {
+      uint32_t v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) v[k] = part[(s + (int64_t)k * kWavesPerBlock) * part_ld + c];
+#pragma unroll
+      for (int k = 0; k < U; ++k) m = max(m, v[k]);
+    }
+    for (; s < slabs; s += kWavesPerBlock) m = max(m, (uint32_t)part[s * part_ld + c]);
+  }
+  red[grp][lane] = m;
+  __syncthreads();
+  if (grp == 0 && c < cols) {
+#pragma unroll
+    for (int g = 1; g < kWavesPerBlock; ++g) m = max(m, red[g][lane]);
+    scale[c] = __uint_as_float(m << 16) / 127.0f;
+  }
 }
 
 template <bool SR, bool ALIGNED4>
@@ -359,15 +442,34 @@ __global__ __launch_bounds__(kThreads) void quant_cols(const uint16_t* __restric
   GroupScale g[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? scale[c0 + j] : 0.0f);
-  for (int64_t r = r_begin + wave; r < r_end; r += kWavesPerBlock) {
-    uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + c0);
-    const uint2 codes =
-        quantize_chunk<SR, ALIGNED4, true>(v, g, seed, offset, (uint64_t)(r * cols + c0));
-    int8_t* dst = q + r * ldq + c0;
-    if (nvalid == 8)
-      *reinterpret_cast<uint2*>(dst) = codes;
-    else
-      store_partial(dst, codes, nvalid);
+  // almost always every column of the wave takes the FMA quotient: then no
+  // per-element mode test is needed (padding columns give zero codes that are
+  // never stored)
+  bool mine = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mine = mine && (j >= nvalid || g[j].mode == 1);
+  const bool all_fma = __all(mine);
+  constexpr int U = 4;  // rows in flight per wave
+  for (int64_t r0 = r_begin + wave; r0 < r_end; r0 += (int64_t)U * kWavesPerBlock) {
+    uint4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t r = r0 + (int64_t)k * kWavesPerBlock;
+      v[k] = r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t r = r0 + (int64_t)k * kWavesPerBlock;
+      if (r >= r_end) break;
+      const uint64_t e0 = (uint64_t)(r * cols + c0);
+      const uint2 codes = all_fma ? quantize_chunk<SR, ALIGNED4, true, 1>(v[k], g, seed, offset, e0)
+                                  : quantize_chunk<SR, ALIGNED4, true, -1>(v[k], g, seed, offset, e0);
+      int8_t* dst = q + r * ldq + c0;
+      if (nvalid == 8)
+        *reinterpret_cast<uint2*>(dst) = codes;
+      else
+        store_partial(dst, codes, nvalid);
+    }
   }
 }
 
@@ -378,9 +480,9 @@ struct ColPlan {
 ColPlan col_plan(int64_t rows, int64_t cols) {
   ColPlan p;
   p.col_tiles = (cols + kColTile - 1) / kColTile;
-  int64_t slabs = (2048 + p.col_tiles - 1) / max(p.col_tiles, (int64_t)1);
-  slabs = min(slabs, (int64_t)256);
-  slabs = min(slabs, max((int64_t)1, (rows + 15) / 16));
+  int64_t slabs = (1024 + p.col_tiles - 1) / max(p.col_tiles, (int64_t)1);
+  slabs = min(slabs, (int64_t)128);
+  slabs = min(slabs, max((int64_t)1, (rows + 31) / 32));
   slabs = max(slabs, (int64_t)1);
   p.rows_per_slab = max((int64_t)1, (rows + slabs - 1) / slabs);
   p.slabs = rows > 0 ? (rows + p.rows_per_slab - 1) / p.rows_per_slab : 1;
@@ -392,15 +494,17 @@ template <int NV>
 void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
                     int64_t ldq, float* scale, int round, uint64_t seed, uint64_t offset,
                     hipStream_t stream) {
+  // one row per wave: every row's loads are issued at once
   const dim3 grid((unsigned)((rows + kWavesPerBlock - 1) / kWavesPerBlock));
+  constexpr bool PF = false;
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if (a4)
-      quant_rows_wave<NV, true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+      quant_rows_wave<NV, true, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
     else
-      quant_rows_wave<NV, true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+      quant_rows_wave<NV, true, false, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   } else {
-    quant_rows_wave<NV, false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    quant_rows_wave<NV, false, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   }
 }
 
@@ -455,7 +559,7 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
     col_absmax_partial<<<dim3((unsigned)p.col_tiles, (unsigned)p.slabs), kThreads, 0, stream>>>(
         x, rows, cols, ldx, p.rows_per_slab, part, p.part_ld);
   }
-  col_scale_finalize<<<dim3((unsigned)((cols + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(
+  col_scale_finalize<<<dim3((unsigned)((cols + 63) / 64)), kThreads, 0, stream>>>(
       part, p.part_ld, rows > 0 ? p.slabs : 0, cols, scale);
   if (rows == 0) return hipGetLastError();
   // quantize pass: 32 rows per block (more when rows would exceed the grid's y limit)
