@@ -1,0 +1,224 @@
+"""GPU parity at the full sizes of the benchmarked and named workloads.
+
+* Every quantized operand (codes and scales) is compared with the CPU oracle
+  in full, bit for bit.
+* GEMM outputs of the library's linear forward / backward are compared on
+  sampled positions plus whole bands of rows, bit for bit, against the
+  oracle's scaled matmul of the oracle's own quantized operands.
+* Stochastic rounding is additionally checked for unbiasedness over 256
+  seeds on a [64, 64] slice, on the GPU's own draws.
+* The quotient x / s the kernels evaluate is checked exhaustively: every
+  finite bf16 value against every positive finite bf16 absmax.
+
+Inputs are seeded synthetic tensors with the layer shapes and distributions
+of the source pages' runs (see workloads.py); they are drawn on the GPU and
+copied to the host for the oracle.
+"""
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import tensor_bits
+from workloads import linear_inputs, llama3_8b_layers, llama_1b_layers, square
+
+pytestmark = pytest.mark.gpu
+
+i8 = pytest.importorskip("int8_mixed_precision_rowwise_amd")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+THREADS = min(16, len(os.sched_getaffinity(0)))
+RC = {"rne": oracle.RNE, "sr": oracle.SR}
+
+
+def oracle_rowwise(xb, rounding, seed, offset):
+    """The oracle's row-wise quantization, split over row bands in threads (rows
+    are independent; a band starting at row r0 draws from offset + r0*cols/4)."""
+    rows, cols = xb.shape
+    if rows * cols < 1 << 22 or cols % 4:
+        return oracle.quantize_rowwise(xb, RC[rounding], seed, offset)
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(rows, np.float32)
+    step = -(-rows // THREADS)
+
+    def work(r0):
+        r1 = min(rows, r0 + step)
+        qq, ss = oracle.quantize_rowwise(xb[r0:r1], RC[rounding], seed, offset + r0 * cols // 4)
+        q[r0:r1], s[r0:r1] = qq, ss
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(work, range(0, rows, step)))
+    return q, s
+
+
+def oracle_colwise(xb, rounding, seed, offset):
+    """The oracle's column-wise quantization; under RNE split over column bands
+    (columns are independent), under SR in one call (draws index the whole row)."""
+    rows, cols = xb.shape
+    if rounding == "sr" or rows * cols < 1 << 22:
+        return oracle.quantize_colwise(xb, RC[rounding], seed, offset)
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(cols, np.float32)
+    step = -(-cols // THREADS)
+
+    def work(c0):
+        c1 = min(cols, c0 + step)
+        qq, ss = oracle.quantize_colwise(xb[:, c0:c1], RC[rounding], seed, offset)
+        q[:, c0:c1], s[c0:c1] = qq, ss
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(work, range(0, cols, step)))
+    return q, s
+
+
+def check_quant(got, want, what):
+    q, s = got
+    qo, so = want
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32)), f"{what}: scales"
+    qn = q.cpu().numpy()
+    if not np.array_equal(qn, qo):
+        bad = np.argwhere(qn != qo)
+        raise AssertionError(f"{what}: {len(bad)} codes differ, first at {bad[0].tolist()}")
+
+
+def sampled_positions(M, N, K, rng):
+    """4096 random outputs plus whole rows at both ends, sized so the oracle's
+    exact dot products stay near 2^29 multiply-adds."""
+    budget = 1 << 29
+    n = max(256, min(4096, budget // K))
+    band = max(1, min(16, budget // (2 * N * K)))
+    ms = rng.integers(0, M, size=n)
+    ns = rng.integers(0, N, size=n)
+    rows = np.concatenate([np.arange(min(band, M)), np.arange(max(0, M - band), M)])
+    bm = np.repeat(rows, N)
+    bn = np.tile(np.arange(N), len(rows))
+    return np.concatenate([ms, bm]), np.concatenate([ns, bn])
+
+
+def check_gemm(layout, Y, qa, sa, qb, sb, rng, what):
+    M, N = Y.shape
+    K = qa.shape[1] if layout in ("NT", "NN") else qa.shape[0]
+    ms, ns = sampled_positions(M, N, K, rng)
+    _, y = oracle.scaled_mm_at(oracle.LAYOUTS[layout], qa, sa, qb, sb, ms, ns)
+    got = tensor_bits(Y)[ms, ns]
+    if not np.array_equal(got, y):
+        bad = int(np.count_nonzero(got != y))
+        raise AssertionError(f"{what}: {bad} of {len(ms)} sampled bf16 outputs differ")
+
+
+def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")):
+    t = linear_inputs(shape, seed=0, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
+    rng = np.random.default_rng(shape.M + shape.N + shape.K)
+    po = lambda j: offset + (j << 40)  # noqa: E731
+    name = f"{shape.name} {rounding}"
+    if "fwd" in gemms:
+        ox = oracle_rowwise(Xb, rounding, seed, po(0))
+        ow = oracle_rowwise(Wb, rounding, seed, po(1))
+        check_quant(i8.quantize_rowwise(X, rounding, seed, po(0)), ox, name + " X row")
+        check_quant(i8.quantize_rowwise(W, rounding, seed, po(1)), ow, name + " W row")
+        Y = i8.linear_fwd(X, W, rounding, seed, offset)
+        check_gemm("NT", Y, ox[0], ox[1], ow[0], ow[1], rng, name + " Y")
+        del Y, ox, ow
+    dX, dW = i8.linear_bwd(dY, X, W, rounding, seed, offset,
+                           want_dx="dgrad" in gemms, want_dw="wgrad" in gemms)
+    if "dgrad" in gemms:
+        ody = oracle_rowwise(dYb, rounding, seed, po(2))
+        owc = oracle_colwise(Wb, rounding, seed, po(3))
+        check_quant(i8.quantize_rowwise(dY, rounding, seed, po(2)), ody, name + " dY row")
+        check_quant(i8.quantize_colwise(W, rounding, seed, po(3)), owc, name + " W col")
+        check_gemm("NN", dX, ody[0], ody[1], owc[0], owc[1], rng, name + " dX")
+        del ody, owc
+    if "wgrad" in gemms:
+        odc = oracle_colwise(dYb, rounding, seed, po(4))
+        oxc = oracle_colwise(Xb, rounding, seed, po(5))
+        check_quant(i8.quantize_colwise(dY, rounding, seed, po(4)), odc, name + " dY col")
+        check_quant(i8.quantize_colwise(X, rounding, seed, po(5)), oxc, name + " X col")
+        check_gemm("TN", dW, odc[0], odc[1], oxc[0], oxc[1], rng, name + " dW")
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_square_4096_step(rounding):
+    """The benchmarked workload: one linear step at M = N = K = 4096."""
+    run_layer(square(4096), rounding, seed=1234)
+
+
+@pytest.mark.parametrize("layer", [s.name for s in llama_1b_layers()])
+def test_llama1b_layer_rne(layer):
+    """Llama-style 1B decoder linears at 16 x 2048 = 32768 tokens, RNE."""
+    shape = next(s for s in llama_1b_layers() if s.name == layer)
+    run_layer(shape, "rne")
+
+
+@pytest.mark.parametrize("layer", ["llama1b_k_proj", "llama1b_down_proj"])
+def test_llama1b_layer_sr(layer):
+    """The same layers with stochastic rounding in every quantize pass."""
+    shape = next(s for s in llama_1b_layers() if s.name == layer)
+    run_layer(shape, "sr", seed=7, offset=3)
+
+
+def test_sr_unbiased_over_256_seeds_on_gpu():
+    """GPU stochastic rounding: mean code over seeds 0..255 equals x/s on a
+    [64, 64] slice (row-wise over full 2048-wide rows of Llama-1B activations,
+    column-wise over all 32768 rows of its output gradients)."""
+    shape = next(s for s in llama_1b_layers() if s.name == "llama1b_q_proj")
+    t = linear_inputs(shape, seed=0, device="cuda")
+    X = t["X"][:64]
+    dY = t["dY"]
+    acc_r = torch.zeros((64, 64), dtype=torch.float64, device="cuda")
+    acc_c = torch.zeros((64, 64), dtype=torch.float64, device="cuda")
+    for seed in range(256):
+        q, s_r = i8.quantize_rowwise(X, "sr", seed, 0)
+        acc_r += q[:, :64].double()
+        qc, s_c = i8.quantize_colwise(dY[:, :64].contiguous(), "sr", seed, 0)
+        acc_c += qc[:64].double()
+    for acc, v in ((acc_r, X[:, :64].double() / s_r.double()[:, None]),
+                   (acc_c, dY[:64, :64].double() / s_c.double()[None, :])):
+        mean = (acc / 256).cpu().numpy()
+        v = v.cpu().numpy()
+        f = v - np.floor(v)
+        sd = np.sqrt(f * (1 - f) / 256)
+        assert (np.abs(mean - v) <= 5 * sd + 2.0**-16).all()
+        z = (acc.cpu().numpy() - 256 * v).sum() / np.sqrt(256 * (f * (1 - f)).sum())
+        assert abs(z) < 5
+
+
+@pytest.mark.parametrize("layer", ["llama3_8b_k_proj", "llama3_8b_down_proj", "llama3_8b_lm_head"])
+def test_llama3_8b_layer_rne(layer):
+    """Llama-3-8B-shaped linears at 8192 tokens, including the 128256-wide LM
+    head (grad-input contraction 128256, inside the int32 bound)."""
+    shape = next(s for s in llama3_8b_layers() if s.name == layer)
+    run_layer(shape, "rne")
+
+
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_quotient_exhaustive(rounding):
+    """Every finite bf16 x against every positive finite bf16 absmax a, |x| <= a:
+    row i holds all bf16 bit patterns b with (b & 0x7fff) <= a_i (others 0), so
+    its absmax is a_i; codes must equal the oracle's (IEEE division) codes."""
+    amax = np.arange(1, 0x7F80, dtype=np.uint32)  # positive finite bf16 patterns
+    cols = 65536
+    pats = np.arange(cols, dtype=np.uint32)
+    mag = pats & 0x7FFF
+    finite = mag < 0x7F80
+    band = 4096
+    for r0 in range(0, len(amax), band):
+        a = amax[r0:r0 + band]
+        keep = finite[None, :] & (mag[None, :] <= a[:, None])
+        xb = np.where(keep, pats[None, :], 0).astype(np.uint16)
+        xg = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        q, s = i8.quantize_rowwise(xg, rounding, 11, r0 * cols // 4)
+        qo, so = oracle_rowwise(xb, rounding, 11, r0 * cols // 4)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+        qn = q.cpu().numpy()
+        if not np.array_equal(qn, qo):
+            bad = np.argwhere(qn != qo)[0]
+            raise AssertionError(f"x bits {xb[bad[0], bad[1]]:#06x} amax bits {a[bad[0]]:#06x}: "
+                                 f"gpu {qn[bad[0], bad[1]]} oracle {qo[bad[0], bad[1]]}")
+        del xg, q
