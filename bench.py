@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, copy one 256 MiB buffer with torch (a plain "
+                         "copy kernel of known size for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -221,6 +224,14 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ctx[lay] = round(gemm_ops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 1)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

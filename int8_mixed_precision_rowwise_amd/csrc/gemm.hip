@@ -243,6 +243,70 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int64_t m0
   }
 }
 
+// bf16 epilogue through LDS: each wave scales its WM x WN accumulators,
+// writes them as bf16 into its own LDS region (rows of WN * 2 bytes, 16-byte
+// chunk c of row r at chunk c ^ (r mod chunks-per-row)), then reads whole
+// rows back 16 bytes per lane and stores them, so every store instruction
+// writes complete rows instead of scattered 8-byte pieces.  Needs C 16-byte
+// aligned and ldc a multiple of 8; `stage` holds at least 4 * WM * WN * 2
+// bytes and no wave reads the slab buffers any more.
+template <int BM, int TM, int TN>
+__device__ __forceinline__ void store_tile_staged(const v16i (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                                  int wm, int wn, int64_t M, int64_t N,
+                                                  const float* s_lds, int8_t* stage,
+                                                  __bf16* __restrict__ C, int64_t ldc, int lane,
+                                                  int wave) {
+  constexpr int WM = 32 * TM, WN = 32 * TN;
+  constexpr int CPR = WN / 8;           // 16-byte chunks per row
+  constexpr int PITCH = WN * 2;         // bytes per row
+  int8_t* mine = stage + wave * (WM * PITCH);
+  const int mr = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = 32 * i + mr;
+    const float sam = s_lds[wm + r];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int chunk = 4 * j + q;  // columns 8 * chunk .. + 7 of the wave tile
+        const float4 sbq = *reinterpret_cast<const float4*>(s_lds + BM + wn + 8 * chunk + 4 * half);
+        const float sbv[4] = {sbq.x, sbq.y, sbq.z, sbq.w};
+        __bf16 h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float y = (float)acc[i][j][4 * q + e];
+          y = y * sam;
+          y = y * sbv[e];
+          h[e] = (__bf16)y;  // round to nearest even
+        }
+        const int off = r * PITCH + ((chunk ^ (r & (CPR - 1))) << 4) + 8 * half;
+        *reinterpret_cast<uint2*>(mine + off) = __builtin_bit_cast(uint2, h);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int RPI = 64 / CPR;  // rows per read instruction
+  const int c = lane % CPR;
+#pragma unroll 4
+  for (int r0 = 0; r0 < WM; r0 += RPI) {
+    const int r = r0 + lane / CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(mine + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+    const int64_t m = m0 + wm + r;
+    const int64_t n = n0 + wn + 8 * c;
+    if (m < M) {
+      __bf16* dst = C + m * ldc + n;
+      if (n + 8 <= N) {
+        // streaming store: the output is not read again by this kernel
+        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(dst));
+      } else if (n < N) {
+        const __bf16* hv = reinterpret_cast<const __bf16*>(&v);
+        for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = hv[e];
+      }
+    }
+  }
+}
+
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
 __global__ __launch_bounds__(kThreads) void gemm_i8_general(int64_t M, int64_t N, int64_t K,
                                                     const int8_t* __restrict__ A, int64_t lda,
@@ -560,7 +624,10 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t
   for (int r = 0; r < NPRE; ++r)
     if (!OUT_I32 && t + r * kThreads < BM + BN) s_lds[t + r * kThreads] = s_pre[r];
   __syncthreads();
-  store_tile<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
+  if constexpr (!OUT_I32 && VEC)
+    store_tile_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
+  else
+    store_tile<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
 }
 
 
@@ -587,9 +654,9 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
   const int64_t a_ext = AK ? (int64_t)BM * lda : K * lda;
   const int64_t b_ext = BKM ? (int64_t)BN * ldb : K * ldb;
   const bool fast = K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024;
-  // packed stores of 4 adjacent outputs need 4-element alignment of every row
+  // packed stores of adjacent outputs need 16-byte aligned rows
   const uintptr_t c = Ci ? reinterpret_cast<uintptr_t>(Ci) : reinterpret_cast<uintptr_t>(Cb);
-  const bool vec = ldc % 4 == 0 && c % (Ci ? 16 : 8) == 0;
+  const bool vec = Ci ? (ldc % 4 == 0 && c % 16 == 0) : (ldc % 8 == 0 && c % 16 == 0);
   if (Ci) {
     if (vec) launch<BM, BN, AK, BKM, true, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, stream);
     else launch<BM, BN, AK, BKM, true, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, stream);
