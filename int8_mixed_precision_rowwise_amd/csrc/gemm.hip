@@ -6,8 +6,12 @@
 //   C[m,n]   = bf16_RNE(RN32(RN32(float(acc)) * sa[m]) * sb[n])
 // or the raw int32 accumulators.
 //
-// Structure: one workgroup of 4 waves per BM x BN output tile, K in steps of
-// 64 through double-buffered LDS, v_mfma_i32_32x32x32_i8 on 32 x 32 blocks.
+// Structure: one workgroup per BM x BN output tile, K in slabs of 64 bytes
+// through LDS, v_mfma_i32_32x32x32_i8 on 32 x 32 blocks.  Two kernels: a
+// pipelined one (slabs loaded memory -> LDS by the buffer unit, several slabs
+// in flight; 8 waves for 256 x 256 tiles, 4 for 128 x 128) for contraction
+// lengths that are multiples of 16, and a register-staged double-buffered one
+// (4 waves) for every other shape.
 // An operand whose contraction dimension is contiguous in memory (A in NT and
 // NN, B in NT) is staged K-major and fed to the MFMA with ds_read_b128; an
 // operand whose contraction runs down its rows (B in NN and TN, A in TN) is
@@ -399,22 +403,6 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // are outstanding and leaves the other counters alone (gfx9 encoding).
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// Scheduling template for one group of MFMAs: each MFMA is followed by a
-// share of the LDS fragment reads, the slab loads and their address
-// arithmetic, so the matrix core gets a new MFMA while the other units work
-// instead of idling between back-to-back MFMA groups.
-template <int NMFMA, int NDS, int NVM>
-__device__ __forceinline__ void interleave() {
-  constexpr int ds_per = (NDS + NMFMA - 1) / NMFMA;
-  constexpr int vm_per = (NVM + NMFMA - 1) / NMFMA;
-#pragma unroll
-  for (int m = 0; m < NMFMA; ++m) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if (m * ds_per < NDS) __builtin_amdgcn_sched_group_barrier(0x100, ds_per, 0);  // DS read
-    if (m * vm_per < NVM) __builtin_amdgcn_sched_group_barrier(0x020, vm_per, 0);  // VMEM read
-  }
-}
-
 // Workgroup barrier for the pipelined loop: waits for this wave's LDS reads
 // (so no wave refills a buffer another wave is still reading) but not for
 // the slab loads in flight, whose completion is tracked with waitcnt_vm.
@@ -427,9 +415,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int R, bool KMAJOR>
+template <int R, bool KMAJOR, int NW>
 struct Dma {
-  static constexpr int kInst = R * BK / 1024 / 4;  // instructions per wave per slab
+  static constexpr int kInst = R * BK / 1024 / NW;  // instructions per wave per slab (NW waves)
   v4u rsrc;              // buffer descriptor (scalar registers)
   uint32_t off0[kInst];  // offset of this lane's chunk in slab 0
   int kpos[kInst];       // contraction index of the chunk within a slab (BK: outside the operand)
@@ -458,7 +446,7 @@ struct Dma {
       kstride = 1;
 #pragma unroll
       for (int j = 0; j < kInst; ++j) {
-        const int pc = (wave + 4 * j) * 64 + lane;  // chunk index within the LDS tile
+        const int pc = (wave + NW * j) * 64 + lane;  // chunk index within the LDS tile
         const int r = pc >> 2;
         const int c = (pc & 3) ^ ((r >> 1) & 3);
         kpos[j] = r < rows_in ? 16 * c : BK;  // BK never passes the slab limit
@@ -471,7 +459,7 @@ struct Dma {
       kstride = (uint32_t)ld;
 #pragma unroll
       for (int j = 0; j < kInst; ++j) {
-        const int pc = (wave + 4 * j) * 64 + lane;
+        const int pc = (wave + NW * j) * 64 + lane;
         const int k = pc / CPR;
         const int c = (pc % CPR) ^ (k & 7);
         kpos[j] = 16 * c < cols_in ? k : BK;
@@ -488,12 +476,12 @@ struct Dma {
     const int limit = (int)min(K - k0, (int64_t)BK);  // contraction indices left in this slab
     const uint32_t o = kpos[j] < limit ? off0[j] + (uint32_t)k0 * kstride : kOob;
     const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(dst + (wave + 4 * j) * 1024)));
+        (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(dst + (wave + NW * j) * 1024)));
     // Issued as inline assembly: the compiler then does not treat the LDS
     // write as pending on every later LDS read (which would make it wait for
     // all slabs in flight); arrival is tracked explicitly with waitcnt_vm and
     // the workgroup barrier.
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(l), "v"(o), "s"(rsrc)
                  : "memory", "m0");
@@ -505,19 +493,18 @@ struct Dma {
   }
 };
 
-template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
-__global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
+template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
+__global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
                                                               const int8_t* __restrict__ A, int64_t lda,
                                                               const float* __restrict__ sa,
                                                               const int8_t* __restrict__ B, int64_t ldb,
                                                               const float* __restrict__ sb,
                                                               void* __restrict__ Cv, int64_t ldc) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NW = 2 * WGN, NT = 64 * NW;  // 2 x WGN waves
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SLAB = A_BYTES + B_BYTES;
-  constexpr int PER = Dma<BM, A_KMAJOR>::kInst + Dma<BN, B_KMAJOR>::kInst;  // loads per wave per slab
-  // LDS read instructions per 32-wide step: one per K-major fragment, two per transposed one
-  constexpr int FRAG_READS = TM * (A_KMAJOR ? 1 : 2) + TN * (B_KMAJOR ? 1 : 2);
+  constexpr int PER = Dma<BM, A_KMAJOR, NW>::kInst + Dma<BN, B_KMAJOR, NW>::kInst;  // loads per wave per slab
   __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * SLAB];
 
   __shared__ __attribute__((aligned(16))) float s_lds[BM + BN];  // scales of the tile
@@ -527,13 +514,13 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   // the epilogue's scales, fetched now so their latency hides under the main loop
-  constexpr int NPRE = (BM + BN + kThreads - 1) / kThreads;
+  constexpr int NPRE = (BM + BN + NT - 1) / NT;
   float s_pre[NPRE];
 #pragma unroll
   for (int r = 0; r < NPRE; ++r) {
-    const int i = t + r * kThreads;
+    const int i = t + r * NT;
     s_pre[r] = 0.0f;
     if (!OUT_I32 && i < BM + BN) {
       if (i < BM) {
@@ -544,8 +531,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t
     }
   }
 
-  Dma<BM, A_KMAJOR> da;
-  Dma<BN, B_KMAJOR> db;
+  Dma<BM, A_KMAJOR, NW> da;
+  Dma<BN, B_KMAJOR, NW> db;
   da.init(A, lda, m0, M, K, wave, lane);
   db.init(B, ldb, n0, N, K, wave, lane);
 
@@ -576,8 +563,11 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t
   // Main loop, one slab per iteration, in two halves of TM * TN MFMAs.  Each
   // MFMA is followed by at most one fragment read and one slab load, and a
   // sched_barrier after each step keeps that order, so the matrix core is fed
-  // a new MFMA while the LDS and memory units work.
-  constexpr int NA = Dma<BM, A_KMAJOR>::kInst;
+  // a new MFMA while the LDS and memory units work.  The slab-(kt+3) loads go
+  // half into each half of the slab, so their issue never bunches up; the
+  // buffer they fill was released by the barrier of the previous iteration.
+  constexpr int NA = Dma<BM, A_KMAJOR, NW>::kInst;
+  constexpr int H1 = PER / 2;  // loads issued in the first half
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int8_t* cur = lds + (kt % STAGES) * SLAB;
     const int8_t* nxt = lds + ((kt + 1) % STAGES) * SLAB;
@@ -588,17 +578,26 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t
       acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[m % TN], a0[m / TN], acc[m / TN][m % TN], 0, 0, 0);
       if (m < TM) a1[m] = frag<BM, A_KMAJOR>(cur, wm0 + 32 * m, 1, lane);
       else if (m < TM + TN) b1[m - TM] = frag<BN, B_KMAJOR>(cur + A_BYTES, wn0 + 32 * (m - TM), 1, lane);
-      if (m < NA) da.issue_one(m, dst, ns, K, wave);
-      else if (m < PER) db.issue_one(m - NA, dst + A_BYTES, ns, K, wave);
+      if (m % 2 == 1 && m / 2 < H1) {
+        const int j = m / 2;
+        if (j < NA) da.issue_one(j, dst, ns, K, wave);
+        else db.issue_one(j - NA, dst + A_BYTES, ns, K, wave);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * PER));
+    // slab kt+1 has landed once at most (slabs kt+2, kt+3 half) of this wave's loads are pending
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 3) * PER + H1));
     lds_barrier();
 #pragma unroll
     for (int m = 0; m < TM * TN; ++m) {
       acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[m % TN], a1[m / TN], acc[m / TN][m % TN], 0, 0, 0);
       if (m < TM) a0[m] = frag<BM, A_KMAJOR>(nxt, wm0 + 32 * m, 0, lane);
       else if (m < TM + TN) b0[m - TM] = frag<BN, B_KMAJOR>(nxt + A_BYTES, wn0 + 32 * (m - TM), 0, lane);
+      if (m % 2 == 1 && H1 + m / 2 < PER) {
+        const int j = H1 + m / 2;
+        if (j < NA) da.issue_one(j, dst, ns, K, wave);
+        else db.issue_one(j - NA, dst + A_BYTES, ns, K, wave);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -622,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_pipelined(int64_t M, int64_t
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing zero-fill loads and the scales
 #pragma unroll
   for (int r = 0; r < NPRE; ++r)
-    if (!OUT_I32 && t + r * kThreads < BM + BN) s_lds[t + r * kThreads] = s_pre[r];
+    if (!OUT_I32 && t + r * NT < BM + BN) s_lds[t + r * NT] = s_pre[r];
   __syncthreads();
   if constexpr (!OUT_I32 && VEC)
     store_tile_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
@@ -635,8 +634,11 @@ template <int BM, int BN, bool AK, bool BKM, bool OUT_I32, bool VEC>
 void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
             const float* sa, const int8_t* B, int64_t ldb, const float* sb, void* C, int64_t ldc,
             hipStream_t stream) {
+  // 256 x 256 tiles: 8 waves (2 per SIMD, 128 x 64 each) so one wave's MFMAs
+  // run while the other waits on its slab-load issue; 128 x 128: 4 waves.
+  constexpr int WGN = BM >= 256 ? 4 : 2;
   if (fast)
-    gemm_i8_pipelined<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
   else
     gemm_i8_general<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
 }
