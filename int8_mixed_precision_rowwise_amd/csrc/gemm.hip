@@ -43,17 +43,29 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 constexpr int BK = 64;
 constexpr int kThreads = 256;
 
+// gfx950 LDS: 64 banks of 4 bytes (256 bytes per clock per CU); a 16-byte
+// read is served 16 lanes at a time, an 8-byte read 32 lanes at a time, and
+// each phase runs at full rate only if its lanes hit 64 distinct banks.
+//
 // K-major LDS tile: rows of 64 bytes, 16-byte chunk c of row r stored at
-// chunk c ^ ((r >> 1) & 3), so that 8 lanes reading one chunk column of 8
-// consecutive rows (the MFMA fragment read) and 8 lanes writing two rows hit
-// 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int kmajor_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 3)) << 4); }
+// chunk c ^ ((r >> 2) & 3).  The MFMA fragment read has 16 lanes read one
+// chunk column of 16 consecutive rows: rows r and r + 4j share the bank
+// offset of r * 64 and the swizzle moves them to 4 different 16-byte groups.
+__device__ __forceinline__ int kmajor_off(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // Storage-orientation LDS tile: BK rows (k) of W bytes, 16-byte chunk c of
-// row k stored at chunk c ^ (k & 7): the 8 rows one transpose read touches
-// land in 8 distinct bank groups.
+// row k stored at chunk c ^ s(k).  A transpose read has 32 lanes read 8
+// bytes each from 8 consecutive rows in each of two chunks: either two
+// adjacent chunks of the same rows (32 x 32 blocks) or one chunk of rows k
+// and k + 16 (16 x 16 blocks).  W = 256: every row starts at bank 0 and
+// s(k) = 2 (k & 7) ^ ((k >> 4) & 1) sends all 16 chunk reads to distinct
+// 16-byte bank groups; W = 128: rows alternate between the two halves of the
+// banks and s(k) = (k & 7) ^ ((k >> 4) & 1) does the same.
+__device__ __forceinline__ constexpr int mnmajor_swz(int W, int k) {
+  return (W >= 256 ? 2 * (k & 7) : (k & 7)) ^ ((k >> 4) & 1);
+}
 template <int W>
-__device__ __forceinline__ int mnmajor_off(int k, int c) { return k * W + ((c ^ (k & 7)) << 4); }
+__device__ __forceinline__ int mnmajor_off(int k, int c) { return k * W + ((c ^ mnmajor_swz(W, k)) << 4); }
 
 // Keep the first n (0..16) bytes of a 16-byte chunk.
 __device__ __forceinline__ uint4 keep_bytes(uint4 v, int n) {
@@ -448,7 +460,7 @@ struct Dma {
       for (int j = 0; j < kInst; ++j) {
         const int pc = (wave + NW * j) * 64 + lane;  // chunk index within the LDS tile
         const int r = pc >> 2;
-        const int c = (pc & 3) ^ ((r >> 1) & 3);
+        const int c = (pc & 3) ^ ((r >> 2) & 3);
         kpos[j] = r < rows_in ? 16 * c : BK;  // BK never passes the slab limit
         off0[j] = (uint32_t)(r * ld + 16 * c);
       }
@@ -461,7 +473,7 @@ struct Dma {
       for (int j = 0; j < kInst; ++j) {
         const int pc = (wave + NW * j) * 64 + lane;
         const int k = pc / CPR;
-        const int c = (pc % CPR) ^ (k & 7);
+        const int c = (pc % CPR) ^ mnmajor_swz(R, k);
         kpos[j] = 16 * c < cols_in ? k : BK;
         off0[j] = (uint32_t)(k * ld + 16 * c);
       }
@@ -493,6 +505,180 @@ struct Dma {
   }
 };
 
+// MFMA 16x16x64 i8 operand/result layout: lane l supplies row l % 16 of its
+// first operand block and column l % 16 of its second, each with 16
+// contraction values (here k = 16 (l / 16) + 0..15 of the 64-deep slab; the
+// dot product only needs both operands to use the same assignment); result
+// register v of lane l holds row 4 (l / 16) + v of the first operand's block
+// and column l % 16 of the second's.  Per operation it moves half the
+// accumulator register traffic of the 32 x 32 x 32 form, which matters
+// because the chip runs int8 matrix work at its power limit.
+//
+// Operand for 16-row (or column) block blk0 of an operand tile, whole slab.
+template <int R, bool KMAJOR>
+__device__ __forceinline__ v4i frag16(const int8_t* lds, int blk0, int lane) {
+  if constexpr (KMAJOR) {
+    return *reinterpret_cast<const v4i*>(lds + kmajor_off(blk0 + (lane & 15), lane >> 4));
+  } else {
+    const int li = lane & 15;
+    const int krow = 16 * (lane >> 4) + (li >> 1);
+    const int c = blk0 >> 4;
+    const int half = (li & 1) << 3;
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_v2i*)(lds + mnmajor_off<R>(krow, c) + half));
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_v2i*)(lds + mnmajor_off<R>(krow + 8, c) + half));
+    v4i out;
+    out.x = lo.x;
+    out.y = lo.y;
+    out.z = hi.x;
+    out.w = hi.y;
+    return out;
+  }
+}
+
+// Epilogue of one wave's TM x TN blocks of 16 x 16 accumulators whose
+// top-left output is (m0 + wm, n0 + wn).  The MFMAs take the B fragment as
+// their first operand, so in block (i, j) lane l holds output row
+// m = 16 i + l % 16 and register v holds column n = 16 j + 4 (l / 16) + v:
+// the four registers are four adjacent outputs of one row, stored together
+// (8 bytes of bf16 or 16 bytes of int32) when VEC.
+// y = RN(RN(float(acc) * sa[m]) * sb[n]); s_lds holds sa[tile rows] then
+// sb[tile columns].
+template <int BM, int TM, int TN, bool OUT_I32, bool VEC>
+__device__ __forceinline__ void store16_direct(const v4i (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                               int wm, int wn, int64_t M, int64_t N,
+                                               const float* s_lds, void* __restrict__ Cv,
+                                               int64_t ldc, int lane) {
+  const int mr = lane & 15, nq = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm + 16 * i + mr;
+    if (m >= M) continue;
+    float sam = 0.0f;
+    if constexpr (!OUT_I32) sam = s_lds[wm + 16 * i + mr];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int cn = wn + 16 * j + nq;  // first of the 4 columns within the tile
+      const int64_t n4 = n0 + cn;
+      if (n4 >= N) continue;
+      if constexpr (OUT_I32) {
+        int32_t* row = static_cast<int32_t*>(Cv) + m * ldc;
+        if (VEC && n4 + 4 <= N) {
+          *reinterpret_cast<v4i*>(row + n4) = acc[i][j];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n4 + e < N) row[n4 + e] = acc[i][j][e];
+        }
+      } else {
+        const float4 sbq = *reinterpret_cast<const float4*>(s_lds + BM + cn);
+        const float sbv[4] = {sbq.x, sbq.y, sbq.z, sbq.w};
+        __bf16 h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float y = (float)acc[i][j][e];
+          y = y * sam;
+          y = y * sbv[e];
+          h[e] = (__bf16)y;  // round to nearest even
+        }
+        __bf16* row = static_cast<__bf16*>(Cv) + m * ldc;
+        if (VEC && n4 + 4 <= N) {
+          *reinterpret_cast<uint2*>(row + n4) = __builtin_bit_cast(uint2, h);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n4 + e < N) row[n4 + e] = h[e];
+        }
+      }
+    }
+  }
+}
+
+// bf16 epilogue through LDS for 16 x 16 blocks: each wave scales its
+// WM x WN accumulators, writes them as bf16 into its own LDS region (rows of
+// WN * 2 bytes, 16-byte chunk c of row r at chunk c ^ (r mod chunks-per-row)),
+// then reads whole rows back 16 bytes per lane and stores them, so each
+// store instruction writes complete row segments.  Needs C 16-byte aligned
+// and ldc a multiple of 8; `stage` holds NW * WM * WN * 2 bytes and no wave
+// reads the slab buffers any more.
+template <int BM, int TM, int TN>
+__device__ __forceinline__ void store16_staged(const v4i (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                               int wm, int wn, int64_t M, int64_t N,
+                                               const float* s_lds, int8_t* stage,
+                                               __bf16* __restrict__ C, int64_t ldc, int lane,
+                                               int wave) {
+  constexpr int WM = 16 * TM, WN = 16 * TN;
+  constexpr int CPR = WN / 8;    // 16-byte chunks per row
+  constexpr int PITCH = WN * 2;  // bytes per row
+  int8_t* mine = stage + wave * (WM * PITCH);
+  const int mr = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = 16 * i + mr;
+    const float sam = s_lds[wm + r];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float4 sbq = *reinterpret_cast<const float4*>(s_lds + BM + wn + 16 * j + 4 * q);
+      const float sbv[4] = {sbq.x, sbq.y, sbq.z, sbq.w};
+      __bf16 h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y = (float)acc[i][j][e];
+        y = y * sam;
+        y = y * sbv[e];
+        h[e] = (__bf16)y;  // round to nearest even
+      }
+      const int chunk = 2 * j + (q >> 1);  // columns 8 * chunk .. + 7 of the wave tile
+      const int off = r * PITCH + ((chunk ^ (r & (CPR - 1))) << 4) + 8 * (q & 1);
+      *reinterpret_cast<uint2*>(mine + off) = __builtin_bit_cast(uint2, h);
+    }
+  }
+  __syncthreads();
+  constexpr int RPI = 64 / CPR;  // rows per read instruction
+  const int c = lane % CPR;
+#pragma unroll 4
+  for (int r0 = 0; r0 < WM; r0 += RPI) {
+    const int r = r0 + lane / CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(mine + r * PITCH + ((c ^ (r & (CPR - 1))) << 4));
+    const int64_t m = m0 + wm + r;
+    const int64_t n = n0 + wn + 8 * c;
+    if (m < M) {
+      __bf16* dst = C + m * ldc + n;
+      if (n + 8 <= N) {
+        // streaming store: the output is not read again by this kernel
+        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(dst));
+      } else if (n < N) {
+        const __bf16* hv = reinterpret_cast<const __bf16*>(&v);
+        for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = hv[e];
+      }
+    }
+  }
+}
+
+// Main-loop schedule of one slab (TM x TN MFMAs of 16 x 16 x 64, A-block
+// major: MFMA m works on A block m / TN and B block m % TN).  The first
+// IA * TN MFMAs run before the workgroup barrier; after it, each MFMA is
+// followed by at most one fragment read of the next slab and at most one
+// slab load.  Fragment reads go A blocks 0 .. IA-1 (free since the barrier),
+// then the TN B blocks (into the other B register set), then A blocks
+// IA .. TM-1, each no earlier than the MFMA that last reads it.
+template <int TM, int TN, int PER>
+struct SlabSchedule {
+  static constexpr int IA = 1;
+  static constexpr int HA = IA * TN;        // MFMAs before the barrier
+  static constexpr int NM = TM * TN;
+  static constexpr int DMA_STEP = (NM - HA) / PER > 0 ? (NM - HA) / PER : 1;
+  static constexpr int a_read(int i) {  // MFMA index after which A block i is read
+    return i < IA ? HA + i : (HA + TN + i > TN * (i + 1) - 1 ? HA + TN + i : TN * (i + 1) - 1);
+  }
+  static constexpr int b_read(int j) { return HA + IA + j; }
+  static constexpr int dma_at(int d) { return HA + 1 + DMA_STEP * d; }
+  static_assert(TM > IA, "need A blocks after the barrier");
+  static_assert(3 * TN + TM <= TM * TN, "reads of the next slab fit in the slab's MFMAs");
+  static_assert(HA + 1 + DMA_STEP * (PER - 1) <= NM - 1, "slab loads fit in the slab's MFMAs");
+};
+
 template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
 __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
                                                               const int8_t* __restrict__ A, int64_t lda,
@@ -502,9 +688,12 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
                                                               void* __restrict__ Cv, int64_t ldc) {
   constexpr int NW = 2 * WGN, NT = 64 * NW;  // 2 x WGN waves
   constexpr int WM = BM / 2, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SLAB = A_BYTES + B_BYTES;
-  constexpr int PER = Dma<BM, A_KMAJOR, NW>::kInst + Dma<BN, B_KMAJOR, NW>::kInst;  // loads per wave per slab
+  constexpr int NA = Dma<BM, A_KMAJOR, NW>::kInst;
+  constexpr int PER = NA + Dma<BN, B_KMAJOR, NW>::kInst;  // loads per wave per slab
+  using S = SlabSchedule<TM, TN, PER>;
+  static_assert(NW * WM * WN * 2 <= STAGES * SLAB, "epilogue staging fits in the slab buffers");
   __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * SLAB];
 
   __shared__ __attribute__((aligned(16))) float s_lds[BM + BN];  // scales of the tile
@@ -536,87 +725,84 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   da.init(A, lda, m0, M, K, wave, lane);
   db.init(B, ldb, n0, N, K, wave, lane);
 
-  v16i acc[TM][TN];
+  v4i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (v16i){};
+    for (int j = 0; j < TN; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
   const int nk = (int)((K + BK - 1) / BK);
-  v4i a0[TM], b0[TN], a1[TM], b1[TN];
-  // Slabs past the end are still "loaded", with out-of-range offsets (the
-  // buffer unit writes zeros into a buffer nobody reads), so every iteration
-  // issues the same number of loads and slab kt + 1 has always landed once
-  // at most 2 * PER loads of this wave are outstanding.
+  v4i a[TM], b0[TN], b1[TN];
+  // Slabs 0 .. STAGES-1 go out first.  Slabs past the end are still
+  // "loaded", with out-of-range offsets (the buffer unit writes zeros into a
+  // buffer nobody reads), so every slab costs the same PER loads per wave and
+  // the waits below count slabs.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
+  for (int s = 0; s < STAGES; ++s) {
     da.issue(lds + s * SLAB, s, K, wave);
     db.issue(lds + s * SLAB + A_BYTES, s, K, wave);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * PER));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 1) * PER));  // slab 0 has landed
   lds_barrier();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) a0[i] = frag<BM, A_KMAJOR>(lds, wm0 + 32 * i, 0, lane);
+  for (int i = 0; i < TM; ++i) a[i] = frag16<BM, A_KMAJOR>(lds, wm0 + 16 * i, lane);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b0[j] = frag<BN, B_KMAJOR>(lds + A_BYTES, wn0 + 32 * j, 0, lane);
+  for (int j = 0; j < TN; ++j) b0[j] = frag16<BN, B_KMAJOR>(lds + A_BYTES, wn0 + 16 * j, lane);
 
-  // Main loop, one slab per iteration, in two halves of TM * TN MFMAs.  Each
-  // MFMA is followed by at most one fragment read and one slab load, and a
-  // sched_barrier after each step keeps that order, so the matrix core is fed
-  // a new MFMA while the LDS and memory units work.  The slab-(kt+3) loads go
-  // half into each half of the slab, so their issue never bunches up; the
-  // buffer they fill was released by the barrier of the previous iteration.
-  constexpr int NA = Dma<BM, A_KMAJOR, NW>::kInst;
-  constexpr int H1 = PER / 2;  // loads issued in the first half
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int8_t* cur = lds + (kt % STAGES) * SLAB;
+  // One slab: MFMAs on the fragments of slab kt (registers a, bc) while the
+  // fragments of slab kt + 1 are read into a and bn and slab kt + STAGES is
+  // loaded into slab kt's buffer.  The barrier guarantees that slab kt + 1
+  // has landed for every wave and that every wave has finished reading slab
+  // kt, whose fragments were read during the previous slab.  A sched_barrier
+  // after each step keeps the matrix core fed while the LDS and memory units
+  // work.
+  auto slab = [&](v4i (&bc)[TN], v4i (&bn)[TN], int kt) __attribute__((always_inline)) {
     const int8_t* nxt = lds + ((kt + 1) % STAGES) * SLAB;
-    int8_t* dst = lds + ((kt + STAGES - 1) % STAGES) * SLAB;  // slab kt-1's buffer
-    const int ns = kt + STAGES - 1;
+    int8_t* dst = lds + (kt % STAGES) * SLAB;
+    const int ns = kt + STAGES;
 #pragma unroll
-    for (int m = 0; m < TM * TN; ++m) {
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[m % TN], a0[m / TN], acc[m / TN][m % TN], 0, 0, 0);
-      if (m < TM) a1[m] = frag<BM, A_KMAJOR>(cur, wm0 + 32 * m, 1, lane);
-      else if (m < TM + TN) b1[m - TM] = frag<BN, B_KMAJOR>(cur + A_BYTES, wn0 + 32 * (m - TM), 1, lane);
-      if (m % 2 == 1 && m / 2 < H1) {
-        const int j = m / 2;
-        if (j < NA) da.issue_one(j, dst, ns, K, wave);
-        else db.issue_one(j - NA, dst + A_BYTES, ns, K, wave);
-      }
+    for (int m = 0; m < S::HA; ++m) {
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bc[m % TN], a[m / TN], acc[m / TN][m % TN], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slab kt+1 has landed once at most (slabs kt+2, kt+3 half) of this wave's loads are pending
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 3) * PER + H1));
+    // slab kt+1 has landed once only slabs kt+2 .. kt+STAGES-1 are pending
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 2) * PER));
     lds_barrier();
 #pragma unroll
-    for (int m = 0; m < TM * TN; ++m) {
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[m % TN], a1[m / TN], acc[m / TN][m % TN], 0, 0, 0);
-      if (m < TM) a0[m] = frag<BM, A_KMAJOR>(nxt, wm0 + 32 * m, 0, lane);
-      else if (m < TM + TN) b0[m - TM] = frag<BN, B_KMAJOR>(nxt + A_BYTES, wn0 + 32 * (m - TM), 0, lane);
-      if (m % 2 == 1 && H1 + m / 2 < PER) {
-        const int j = H1 + m / 2;
-        if (j < NA) da.issue_one(j, dst, ns, K, wave);
-        else db.issue_one(j - NA, dst + A_BYTES, ns, K, wave);
-      }
+    for (int m = S::HA; m < S::NM; ++m) {
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bc[m % TN], a[m / TN], acc[m / TN][m % TN], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        if (m == S::a_read(i)) a[i] = frag16<BM, A_KMAJOR>(nxt, wm0 + 16 * i, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        if (m == S::b_read(j)) bn[j] = frag16<BN, B_KMAJOR>(nxt + A_BYTES, wn0 + 16 * j, lane);
+#pragma unroll
+      for (int d = 0; d < PER; ++d)
+        if (m == S::dma_at(d)) {
+          if (d < NA) da.issue_one(d, dst, ns, K, wave);
+          else db.issue_one(d - NA, dst + A_BYTES, ns, K, wave);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // slabs 0 .. nk-2 in pairs (the B register sets swap roles each slab)
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    slab(b0, b1, kt);
+    slab(b1, b0, kt + 1);
   }
-  if (nk > 0) {  // last slab
-    const int8_t* cur = lds + ((nk - 1) % STAGES) * SLAB;
+  if (kt + 1 < nk) {
+    slab(b0, b1, kt);
+    ++kt;
+  }
+  if (nk > 0) {  // slab nk-1, whose fragments are in a and b0 (nk-1 even) or b1
+    const bool odd = kt & 1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a1[i] = frag<BM, A_KMAJOR>(cur, wm0 + 32 * i, 1, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b1[j] = frag<BN, B_KMAJOR>(cur + A_BYTES, wn0 + 32 * j, 1, lane);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[j], a0[i], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[j], a1[i], acc[i][j], 0, 0, 0);
+    for (int m = 0; m < S::NM; ++m)
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_16x16x64_i8(odd ? b1[m % TN] : b0[m % TN], a[m / TN],
+                                                                 acc[m / TN][m % TN], 0, 0, 0);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing zero-fill loads and the scales
 #pragma unroll
@@ -624,9 +810,9 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
     if (!OUT_I32 && t + r * NT < BM + BN) s_lds[t + r * NT] = s_pre[r];
   __syncthreads();
   if constexpr (!OUT_I32 && VEC)
-    store_tile_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
+    store16_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
   else
-    store_tile<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
+    store16_direct<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
 }
 
 

@@ -327,19 +327,50 @@ __global__ __launch_bounds__(kThreads) void quant_rows_block(
 }
 
 // ---------------------------------------------------------------------------
-// Column-wise.  A column tile is 512 columns: each lane owns 8 adjacent
-// columns, each wave walks rows.  Pass 1 writes per-slab column maxima (as
-// bf16 bit patterns) to the workspace, pass 2 reduces the slabs into the
-// scales, pass 3 quantizes.
+// Column-wise, two passes.  A column tile is 512 columns: each lane owns 8
+// adjacent columns and the 8 waves of a block walk rows.  Pass 1 writes the
+// column maxima of each slab of rows (as bf16 bit patterns) to the
+// workspace.  Pass 2 starts every block by reducing the slab maxima of its
+// column tile into the scales (each block of a tile does this; the first row
+// block stores them), then quantizes its rows.
 
 constexpr int kColTile = 512;
+constexpr int kColThreads = 512;
+constexpr int kColWaves = kColThreads / 64;
+constexpr int kColMaxSlabs = 32;
+constexpr int kColLoads = 8;  // rows in flight per wave
 
-__global__ __launch_bounds__(kThreads) void col_absmax_partial(const uint16_t* __restrict__ x,
-                                                               int64_t rows, int64_t cols,
-                                                               int64_t ldx, int64_t rows_per_slab,
-                                                               uint16_t* __restrict__ part,
-                                                               int64_t part_ld) {
-  __shared__ uint4 red[kWavesPerBlock][64];
+__device__ __forceinline__ void max_chunk(us2 (&m)[4], uint4 v) {
+  m[0] = __builtin_elementwise_max(m[0], as_us2(v.x & 0x7FFF7FFFu));
+  m[1] = __builtin_elementwise_max(m[1], as_us2(v.y & 0x7FFF7FFFu));
+  m[2] = __builtin_elementwise_max(m[2], as_us2(v.z & 0x7FFF7FFFu));
+  m[3] = __builtin_elementwise_max(m[3], as_us2(v.w & 0x7FFF7FFFu));
+}
+
+__device__ __forceinline__ uint4 pack_max(const us2 (&m)[4]) {
+  return make_uint4(__builtin_bit_cast(uint32_t, m[0]), __builtin_bit_cast(uint32_t, m[1]),
+                    __builtin_bit_cast(uint32_t, m[2]), __builtin_bit_cast(uint32_t, m[3]));
+}
+
+// Elementwise maximum of the per-wave partial maxima in red (every wave
+// computes it; the caller has synchronized after the writes).
+__device__ __forceinline__ void reduce_waves(us2 (&m)[4], const uint4 (*red)[64], int lane) {
+#pragma unroll
+  for (int w = 0; w < kColWaves; ++w) {
+    const uint4 o = red[w][lane];
+    m[0] = __builtin_elementwise_max(m[0], as_us2(o.x));
+    m[1] = __builtin_elementwise_max(m[1], as_us2(o.y));
+    m[2] = __builtin_elementwise_max(m[2], as_us2(o.z));
+    m[3] = __builtin_elementwise_max(m[3], as_us2(o.w));
+  }
+}
+
+__global__ __launch_bounds__(kColThreads) void col_absmax_partial(const uint16_t* __restrict__ x,
+                                                                  int64_t rows, int64_t cols,
+                                                                  int64_t ldx, int64_t rows_per_slab,
+                                                                  uint16_t* __restrict__ part,
+                                                                  int64_t part_ld) {
+  __shared__ uint4 red[kColWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_slab;
@@ -348,100 +379,78 @@ __global__ __launch_bounds__(kThreads) void col_absmax_partial(const uint16_t* _
   if (c0 < cols) {
     const bool tail = c0 + 8 > cols;
     const int ntail = (int)(cols - c0);
+    constexpr int U = kColLoads;
     int64_t r = r_begin + wave;
-    constexpr int U = 4;
-    for (; r + (U - 1) * kWavesPerBlock < r_end; r += U * kWavesPerBlock) {
+    for (; r + (U - 1) * kColWaves < r_end; r += U * kColWaves) {
       uint4 v[U];
 #pragma unroll
       for (int k = 0; k < U; ++k)
-        v[k] = *reinterpret_cast<const uint4*>(x + (r + k * kWavesPerBlock) * ldx + c0);
+        v[k] = *reinterpret_cast<const uint4*>(x + (r + k * kColWaves) * ldx + c0);
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        if (tail) v[k] = keep_first(v[k], ntail);
-        m[0] = __builtin_elementwise_max(m[0], as_us2(v[k].x & 0x7FFF7FFFu));
-        m[1] = __builtin_elementwise_max(m[1], as_us2(v[k].y & 0x7FFF7FFFu));
-        m[2] = __builtin_elementwise_max(m[2], as_us2(v[k].z & 0x7FFF7FFFu));
-        m[3] = __builtin_elementwise_max(m[3], as_us2(v[k].w & 0x7FFF7FFFu));
-      }
+      for (int k = 0; k < U; ++k) max_chunk(m, tail ? keep_first(v[k], ntail) : v[k]);
     }
-    for (; r < r_end; r += kWavesPerBlock) {
-      uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + c0);
-      if (tail) v = keep_first(v, ntail);
-      m[0] = __builtin_elementwise_max(m[0], as_us2(v.x & 0x7FFF7FFFu));
-      m[1] = __builtin_elementwise_max(m[1], as_us2(v.y & 0x7FFF7FFFu));
-      m[2] = __builtin_elementwise_max(m[2], as_us2(v.z & 0x7FFF7FFFu));
-      m[3] = __builtin_elementwise_max(m[3], as_us2(v.w & 0x7FFF7FFFu));
+    for (; r < r_end; r += kColWaves) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + c0);
+      max_chunk(m, tail ? keep_first(v, ntail) : v);
     }
   }
-  red[wave][lane] = make_uint4(__builtin_bit_cast(uint32_t, m[0]), __builtin_bit_cast(uint32_t, m[1]),
-                               __builtin_bit_cast(uint32_t, m[2]), __builtin_bit_cast(uint32_t, m[3]));
+  red[wave][lane] = pack_max(m);
   __syncthreads();
   if (wave == 0 && c0 < cols) {
-    us2 t[4] = {m[0], m[1], m[2], m[3]};
-#pragma unroll
-    for (int w = 1; w < kWavesPerBlock; ++w) {
-      const uint4 o = red[w][lane];
-      t[0] = __builtin_elementwise_max(t[0], as_us2(o.x));
-      t[1] = __builtin_elementwise_max(t[1], as_us2(o.y));
-      t[2] = __builtin_elementwise_max(t[2], as_us2(o.z));
-      t[3] = __builtin_elementwise_max(t[3], as_us2(o.w));
-    }
-    *reinterpret_cast<uint4*>(part + (int64_t)blockIdx.y * part_ld + c0) =
-        make_uint4(__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
-                   __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3]));
-  }
-}
-
-// Column scales from the per-slab maxima: a block covers 64 columns with
-// 4 groups of slabs; every thread keeps 8 independent loads in flight.
-__global__ __launch_bounds__(kThreads) void col_scale_finalize(const uint16_t* __restrict__ part,
-                                                               int64_t part_ld, int64_t slabs,
-                                                               int64_t cols,
-                                                               float* __restrict__ scale) {
-  __shared__ uint32_t red[kWavesPerBlock][64];
-  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  uint32_t m = 0;
-  if (c < cols) {
-    constexpr int U = 8;
-    int64_t s = grp;
-    for (; s + (int64_t)(U - 1) * kWavesPerBlock < slabs; s += (int64_t)U * kWavesPerBlock) {
-      uint32_t v[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) v[k] = part[(s + (int64_t)k * kWavesPerBlock) * part_ld + c];
-#pragma unroll
-      for (int k = 0; k < U; ++k) m = max(m, v[k]);
-    }
-    for (; s < slabs; s += kWavesPerBlock) m = max(m, (uint32_t)part[s * part_ld + c]);
-  }
-  red[grp][lane] = m;
-  __syncthreads();
-  if (grp == 0 && c < cols) {
-#pragma unroll
-    for (int g = 1; g < kWavesPerBlock; ++g) m = max(m, red[g][lane]);
-    scale[c] = __uint_as_float(m << 16) / 127.0f;
+    reduce_waves(m, red, lane);
+    *reinterpret_cast<uint4*>(part + (int64_t)blockIdx.y * part_ld + c0) = pack_max(m);
   }
 }
 
 template <bool SR, bool ALIGNED4>
-__global__ __launch_bounds__(kThreads) void quant_cols(const uint16_t* __restrict__ x, int64_t rows,
-                                                       int64_t cols, int64_t ldx,
-                                                       int64_t rows_per_block,
-                                                       const float* __restrict__ scale,
-                                                       int8_t* __restrict__ q, int64_t ldq,
-                                                       uint64_t seed, uint64_t offset) {
+__global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __restrict__ x, int64_t rows,
+                                                          int64_t cols, int64_t ldx,
+                                                          int64_t rows_per_block,
+                                                          const uint16_t* __restrict__ part,
+                                                          int64_t part_ld, int64_t slabs,
+                                                          float* __restrict__ scale,
+                                                          int8_t* __restrict__ q, int64_t ldq,
+                                                          uint64_t seed, uint64_t offset) {
+  __shared__ uint4 red[kColWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
-  if (c0 >= cols) return;
+  const bool active = c0 < cols;
   // row blocks run last-to-first, so the rows pass 1 touched last (still in
   // L2 / MALL) are read first
   const int64_t rb = (int64_t)gridDim.y - 1 - blockIdx.y;
   const int64_t r_begin = rb * rows_per_block;
   const int64_t r_end = min(rows, r_begin + rows_per_block);
+  constexpr int U = kColLoads;
+  // the first rows' loads go out before the scales are known
+  uint4 v[U];
+  int64_t r0 = r_begin + wave;
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t r = r0 + (int64_t)k * kColWaves;
+    v[k] = active && r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
+  }
+  // column maxima of the tile from the slab maxima
+  us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  if (active) {
+    for (int64_t s = wave; s < slabs; s += kColWaves)
+      max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
+  }
+  red[wave][lane] = pack_max(m);
+  __syncthreads();
+  if (!active) return;
+  reduce_waves(m, red, lane);
   const int nvalid = (int)min((int64_t)8, cols - c0);
   GroupScale g[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? scale[c0 + j] : 0.0f);
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t bits = j & 1 ? m[j >> 1].y : m[j >> 1].x;
+    g[j] = make_scale(j < nvalid ? bits : 0u);
+  }
+  if (blockIdx.y == 0 && wave == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < nvalid) scale[c0 + j] = g[j].s;
+  }
   // almost always every column of the wave takes the FMA quotient: then no
   // per-element mode test is needed (padding columns give zero codes that are
   // never stored)
@@ -449,17 +458,10 @@ __global__ __launch_bounds__(kThreads) void quant_cols(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < 8; ++j) mine = mine && (j >= nvalid || g[j].mode == 1);
   const bool all_fma = __all(mine);
-  constexpr int U = 4;  // rows in flight per wave
-  for (int64_t r0 = r_begin + wave; r0 < r_end; r0 += (int64_t)U * kWavesPerBlock) {
-    uint4 v[U];
+  for (; r0 < r_end; r0 += (int64_t)U * kColWaves) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int64_t r = r0 + (int64_t)k * kWavesPerBlock;
-      v[k] = r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int64_t r = r0 + (int64_t)k * kWavesPerBlock;
+      const int64_t r = r0 + (int64_t)k * kColWaves;
       if (r >= r_end) break;
       const uint64_t e0 = (uint64_t)(r * cols + c0);
       const uint2 codes = all_fma ? quantize_chunk<SR, ALIGNED4, true, 1>(v[k], g, seed, offset, e0)
@@ -470,23 +472,37 @@ __global__ __launch_bounds__(kThreads) void quant_cols(const uint16_t* __restric
       else
         store_partial(dst, codes, nvalid);
     }
+    const int64_t rn = r0 + (int64_t)U * kColWaves;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t r = rn + (int64_t)k * kColWaves;
+      v[k] = r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
+// Launch shapes: pass 1 has col_tiles x slabs blocks (about 256, at most
+// kColMaxSlabs slabs of at least 64 rows); pass 2 has col_tiles x row_blocks
+// blocks of at least 128 rows, so each block's re-read of the slab maxima
+// (slabs KiB) stays small next to its rows_per_block KiB of input.
 struct ColPlan {
-  int64_t col_tiles, slabs, rows_per_slab, part_ld;
+  int64_t col_tiles, slabs, rows_per_slab, part_ld, row_blocks, rows_per_block;
 };
 
 ColPlan col_plan(int64_t rows, int64_t cols) {
   ColPlan p;
-  p.col_tiles = (cols + kColTile - 1) / kColTile;
-  int64_t slabs = (1024 + p.col_tiles - 1) / max(p.col_tiles, (int64_t)1);
-  slabs = min(slabs, (int64_t)128);
-  slabs = min(slabs, max((int64_t)1, (rows + 31) / 32));
-  slabs = max(slabs, (int64_t)1);
+  p.col_tiles = max((int64_t)1, (cols + kColTile - 1) / kColTile);
+  int64_t slabs = (256 + p.col_tiles - 1) / p.col_tiles;
+  slabs = min(slabs, (int64_t)kColMaxSlabs);
+  slabs = min(slabs, max((int64_t)1, (rows + 63) / 64));
   p.rows_per_slab = max((int64_t)1, (rows + slabs - 1) / slabs);
-  p.slabs = rows > 0 ? (rows + p.rows_per_slab - 1) / p.rows_per_slab : 1;
+  p.slabs = rows > 0 ? (rows + p.rows_per_slab - 1) / p.rows_per_slab : 0;
   p.part_ld = (cols + 7) / 8 * 8;
+  const int64_t want_blocks = (256 + p.col_tiles - 1) / p.col_tiles;
+  int64_t rpb = max((int64_t)128, (rows + want_blocks - 1) / want_blocks);
+  rpb = max(rpb, (rows + 65534) / 65535);  // grid y limit
+  p.rows_per_block = rpb;
+  p.row_blocks = max((int64_t)1, (rows + rpb - 1) / rpb);
   return p;
 }
 
@@ -546,7 +562,7 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols
 
 size_t colwise_workspace_bytes(int64_t rows, int64_t cols) {
   const ColPlan p = col_plan(rows, cols);
-  return (size_t)(p.slabs * p.part_ld * 2);
+  return (size_t)(max(p.slabs, (int64_t)1) * p.part_ld * 2);
 }
 
 hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -555,24 +571,20 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
   if (cols == 0) return hipSuccess;
   const ColPlan p = col_plan(rows, cols);
   uint16_t* part = static_cast<uint16_t*>(ws);
-  if (rows > 0) {
-    col_absmax_partial<<<dim3((unsigned)p.col_tiles, (unsigned)p.slabs), kThreads, 0, stream>>>(
+  if (p.slabs > 0) {
+    col_absmax_partial<<<dim3((unsigned)p.col_tiles, (unsigned)p.slabs), kColThreads, 0, stream>>>(
         x, rows, cols, ldx, p.rows_per_slab, part, p.part_ld);
   }
-  col_scale_finalize<<<dim3((unsigned)((cols + 63) / 64)), kThreads, 0, stream>>>(
-      part, p.part_ld, rows > 0 ? p.slabs : 0, cols, scale);
-  if (rows == 0) return hipGetLastError();
-  // quantize pass: 32 rows per block (more when rows would exceed the grid's y limit)
-  const int64_t rpb = max((int64_t)32, (rows + 65534) / 65535);
-  const dim3 grid((unsigned)p.col_tiles, (unsigned)((rows + rpb - 1) / rpb));
+  // with no rows the quantize pass only stores the (zero) scales
+  const dim3 grid((unsigned)p.col_tiles, (unsigned)p.row_blocks);
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if (a4)
-      quant_cols<true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, rpb, scale, q, ldq, seed, offset);
+      quant_cols<true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
     else
-      quant_cols<true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, rpb, scale, q, ldq, seed, offset);
+      quant_cols<true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
   } else {
-    quant_cols<false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, rpb, scale, q, ldq, seed, offset);
+    quant_cols<false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
   }
   return hipGetLastError();
 }
