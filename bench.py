@@ -239,6 +239,38 @@ def main():
         torch.cuda.synchronize()
         ctx[lay] = round(gemm_ops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 1)
 
+    # context: the same layer step (forward + backward) through the autograd
+    # integration, against torch's bf16 nn.Linear at the same shape
+    from int8_mixed_precision_rowwise_amd.training import (Int8MixedPrecisionConfig,
+                                                           Int8MixedPrecisionLinear)
+    X0, W0, dY0 = sets[0]
+    lin8 = Int8MixedPrecisionLinear(K, N, Int8MixedPrecisionConfig(
+        stochastic_rounding=args.rounding == "sr", seed=seed), device=dev)
+    lin16 = torch.nn.Linear(K, N, bias=False, device=dev, dtype=torch.bfloat16)
+    with torch.no_grad():
+        lin8.weight.copy_(W0)
+        lin16.weight.copy_(W0)
+    xg = X0.clone().requires_grad_()
+
+    def layer_step(lin):
+        xg.grad = None
+        lin.weight.grad = None
+        lin(xg).backward(dY0)
+
+    autograd_ms = {}
+    for tag, lin in (("int8", lin8), ("bf16", lin16)):
+        for _ in range(5):
+            layer_step(lin)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            layer_step(lin)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        autograd_ms[tag] = round(e0.elapsed_time(e1) / 20, 4)
+    autograd_ms["speedup_vs_bf16"] = round(autograd_ms["bf16"] / autograd_ms["int8"], 3)
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -274,6 +306,7 @@ def main():
         "breakdown": breakdown,
         "step_gemm_frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
         "context_torch_bf16_matmul_tflops": ctx,
+        "context_autograd_layer_step_ms": autograd_ms,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)

@@ -1,0 +1,179 @@
+"""Training integration: an autograd op and a module swap over the C ABI.
+
+This is the user boundary the pages describe, restated for this library:
+- weights of bias-free ``nn.Linear`` modules are swapped so that each linear's
+  forward and its two backward GEMMs run as INT8 mixed precision ("Integrate
+  INT8 mixed-precision from torchao 0.7", the usage reply: ``quantize_`` with a
+  filter over modules);
+- each of the three GEMMs can be INT8 or BF16 on its own, and stochastic
+  rounding can be switched on ("Quantized model training", section "INT8 mixed
+  precision training", the ablation table: forward, backward grad input,
+  backward grad weight, stochastic rounding).
+
+Every INT8 GEMM and its quantization passes run in ``libi8mp``'s kernels
+(``linear_fwd`` / ``linear_bwd``).  A GEMM switched to BF16 is a plain bf16
+matmul by torch (hipBLASLt): that is the configuration's meaning, not a
+fallback.  Inputs, weights and gradients are bf16.
+
+Stochastic rounding draws from Philox4x32-10 keyed by a per-module seed; the
+layer's step counter advances the counter offset by ``STEP_STRIDE`` per forward
+call, so every quantize pass of every step draws fresh numbers and a run is
+reproducible from the seed.  The backward of a step reuses its forward's
+(seed, offset): the six quantize passes of one step use offsets
+``offset + j * 2**40``, j = 0..5.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional
+
+import torch
+
+from . import linear_bwd, linear_fwd
+
+__all__ = ["Int8MixedPrecisionConfig", "Int8MixedPrecisionLinearFunction",
+           "Int8MixedPrecisionLinear", "swap_linear_modules", "STEP_STRIDE", "module_seed"]
+
+STEP_STRIDE = 8 << 40  # Philox blocks reserved per linear step (6 passes of 2**40 each, rounded up)
+
+
+@dataclasses.dataclass(frozen=True)
+class Int8MixedPrecisionConfig:
+    """Which GEMMs of a linear layer run in INT8, and how codes are rounded.
+
+    output: forward Y = X @ W.T; grad_input: dX = dY @ W; grad_weight:
+    dW = dY.T @ X.  A GEMM left False runs as a bf16 matmul.
+    """
+    output: bool = True
+    grad_input: bool = True
+    grad_weight: bool = True
+    stochastic_rounding: bool = False
+    seed: int = 0
+
+    @property
+    def rounding(self) -> str:
+        return "sr" if self.stochastic_rounding else "rne"
+
+
+def module_seed(base_seed: int, index: int) -> int:
+    """Philox key of the index-th swapped module: a SplitMix64 step of
+    (base_seed + index), so neighbouring modules get unrelated keys."""
+    z = (base_seed + (index + 1) * 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & 0xFFFFFFFFFFFFFFFF
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & 0xFFFFFFFFFFFFFFFF
+    return z ^ (z >> 31)
+
+
+def _as_rows(t: torch.Tensor, cols: int) -> torch.Tensor:
+    t2 = t.reshape(-1, cols)
+    return t2 if t2.is_contiguous() else t2.contiguous()
+
+
+class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
+    """y = x @ weight.T (bias-free), x [..., K], weight [N, K], all bf16.
+
+    Saved for backward: the bf16 input and weight (what the pages' op keeps;
+    nothing quantized is stored)."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, weight: torch.Tensor, config: Int8MixedPrecisionConfig,
+                seed: int, offset: int):
+        if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+            raise TypeError("INT8 mixed-precision linear takes bf16 input and weight, got "
+                            f"{x.dtype} and {weight.dtype}")
+        if weight.dim() != 2 or x.shape[-1] != weight.shape[1]:
+            raise ValueError(f"shapes {tuple(x.shape)} and {tuple(weight.shape)} do not match")
+        lead = x.shape[:-1]
+        x2 = _as_rows(x, x.shape[-1])
+        w = weight if weight.is_contiguous() else weight.contiguous()
+        if config.output:
+            y = linear_fwd(x2, w, config.rounding, seed, offset)
+        else:
+            y = torch.mm(x2, w.t())
+        ctx.save_for_backward(x2, w)
+        ctx.config, ctx.seed, ctx.offset, ctx.lead = config, seed, offset, lead
+        return y.view(*lead, w.shape[0])
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, w = ctx.saved_tensors
+        cfg = ctx.config
+        need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        dy2 = _as_rows(dy.to(torch.bfloat16), w.shape[0])
+        int_dx, int_dw = need_dx and cfg.grad_input, need_dw and cfg.grad_weight
+        dx = dw = None
+        if int_dx or int_dw:
+            dx, dw = linear_bwd(dy2, x2, w, cfg.rounding, ctx.seed, ctx.offset,
+                                want_dx=int_dx, want_dw=int_dw)
+        if need_dx and not int_dx:
+            dx = torch.mm(dy2, w)
+        if need_dw and not int_dw:
+            dw = torch.mm(dy2.t(), x2)
+        if dx is not None:
+            dx = dx.view(*ctx.lead, w.shape[1])
+        return dx, dw, None, None, None
+
+
+class Int8MixedPrecisionLinear(torch.nn.Linear):
+    """Bias-free linear layer whose GEMMs run per ``config``.
+
+    ``seed`` keys this module's stochastic-rounding stream; ``step`` counts its
+    forward calls (the Philox offset of a call is step * STEP_STRIDE)."""
+
+    def __init__(self, in_features: int, out_features: int,
+                 config: Optional[Int8MixedPrecisionConfig] = None, seed: int = 0,
+                 device=None, dtype=torch.bfloat16):
+        super().__init__(in_features, out_features, bias=False, device=device, dtype=dtype)
+        self.config = config or Int8MixedPrecisionConfig()
+        self.seed = seed
+        self.step = 0
+
+    @classmethod
+    def from_linear(cls, lin: torch.nn.Linear, config: Int8MixedPrecisionConfig,
+                    seed: int) -> "Int8MixedPrecisionLinear":
+        """Wrap an existing bias-free linear, keeping its weight Parameter (same
+        object, so optimizers and state dicts see no change)."""
+        if lin.bias is not None:
+            raise ValueError("INT8 mixed-precision linear layers are bias-free")
+        new = cls.__new__(cls)
+        torch.nn.Module.__init__(new)
+        new.in_features, new.out_features = lin.in_features, lin.out_features
+        new.weight = lin.weight
+        new.register_parameter("bias", None)
+        new.config, new.seed, new.step = config, seed, 0
+        return new
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        offset = self.step * STEP_STRIDE
+        if self.training:
+            self.step += 1
+        return Int8MixedPrecisionLinearFunction.apply(x, self.weight, self.config, self.seed, offset)
+
+    def extra_repr(self) -> str:
+        c = self.config
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"output={'int8' if c.output else 'bf16'}, grad_input={'int8' if c.grad_input else 'bf16'}, "
+                f"grad_weight={'int8' if c.grad_weight else 'bf16'}, rounding={c.rounding}")
+
+
+def swap_linear_modules(model: torch.nn.Module, config: Optional[Int8MixedPrecisionConfig] = None,
+                        filter_fn: Optional[Callable[[torch.nn.Module, str], bool]] = None
+                        ) -> torch.nn.Module:
+    """Replace, in place, every bias-free ``nn.Linear`` of ``model`` for which
+    ``filter_fn(module, qualified_name)`` holds (all of them by default) with an
+    ``Int8MixedPrecisionLinear`` that shares its weight.  Linears with a bias
+    are left alone.  Modules are numbered in ``named_modules`` order; the n-th
+    swapped module's seed is ``module_seed(config.seed, n)``.  Returns model."""
+    config = config or Int8MixedPrecisionConfig()
+    targets = []
+    for name, mod in model.named_modules():
+        if not name:
+            continue  # the root module is not replaced (wrap a bare Linear in a container)
+        if type(mod) is torch.nn.Linear and mod.bias is None and (filter_fn is None or filter_fn(mod, name)):
+            targets.append(name)
+    for index, name in enumerate(targets):
+        parent_name, _, child = name.rpartition(".")
+        parent = model.get_submodule(parent_name) if parent_name else model
+        lin = getattr(parent, child)
+        setattr(parent, child, Int8MixedPrecisionLinear.from_linear(lin, config, module_seed(config.seed, index)))
+    return model
