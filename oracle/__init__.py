@@ -52,6 +52,8 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [p, i64, i64, i64, p, i64, p, i32, u64, u64]
         f.restype = None
+    lib.oracle_col_absmax.argtypes = [p, i64, i64, i64, p]
+    lib.oracle_col_absmax.restype = None
     lib.oracle_quantize_given_u.argtypes = [p, i64, ctypes.c_float, i32, p, p]
     lib.oracle_quantize_given_u.restype = None
     lib.oracle_mm_i32.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64]
@@ -119,6 +121,15 @@ def quantize_rowwise(x: np.ndarray, rounding: int = RNE, seed: int = 0, offset: 
 def quantize_colwise(x: np.ndarray, rounding: int = RNE, seed: int = 0, offset: int = 0):
     """Column-wise dynamic quantization -> (int8 q in x's layout, fp32 scale[cols])."""
     return _quantize(_load().oracle_quantize_colwise, x, lambda r, c: c, rounding, seed, offset)
+
+
+def col_absmax(x: np.ndarray) -> np.ndarray:
+    """fp32 [cols]: the maximum |x| of each column of bf16 bits ``x`` (0 without rows)."""
+    assert x.dtype == np.uint16
+    rows, cols, ldx = _rows_ld(x)
+    out = np.zeros(cols, dtype=np.float32)
+    _load().oracle_col_absmax(_ptr(x), rows, cols, ldx, _ptr(out))
+    return out
 
 
 def quantize_given_u(x: np.ndarray, s: float, rounding: int, u: np.ndarray | None = None):

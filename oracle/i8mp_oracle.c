@@ -202,6 +202,21 @@ void oracle_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int6
   }
 }
 
+/* Column maxima alone: out[c] = max over rows of |x[r,c]| (0 when there are
+ * no rows), the statistic behind the column-wise scales above
+ * (scale[c] = RN(out[c] / 127)), returned by itself so that a row-wise pass
+ * that also reports it can be checked. */
+void oracle_col_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* out) {
+  for (int64_t c = 0; c < cols; ++c) {
+    float amax = 0.0f;
+    for (int64_t r = 0; r < rows; ++r) {
+      float a = fabsf(bf16_to_float(x[r * ldx + c]));
+      if (a > amax) amax = a;
+    }
+    out[c] = amax;
+  }
+}
+
 /* ---- integer matmul in the three layouts ([QT] "Speed benchmarks") ------ */
 
 /* Element (m,k) of the left operand and (k,n) of the right operand.

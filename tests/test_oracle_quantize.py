@@ -202,3 +202,26 @@ def test_ragged_leading_dimension():
     q1, s1 = oracle.quantize_rowwise(x, oracle.SR, seed=9, offset=5)
     q2, s2 = oracle.quantize_rowwise(big[:, :40], oracle.SR, seed=9, offset=5)
     assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------
+# column maxima on their own (the statistic a row-wise pass also reports)
+
+
+def test_col_absmax_matches_numpy_and_column_scales():
+    x = bf16_bits(gaussian_bf16(37, 53, seed=9))
+    # signed zeros, subnormals, the largest finite bf16 and its negative
+    x[0, :4] = [0x8000, 0x0001, 0x8001, 0x7F7F]
+    x[5, 4] = 0xFF7F
+    x[:, 10] = 0x8000
+    cm = oracle.col_absmax(x)
+    widened = (x.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(cm, np.abs(widened).max(axis=0))
+    assert cm[10] == 0.0 and not np.signbit(cm[10])
+    _, s = oracle.quantize_colwise(x)
+    assert np.array_equal(s, (cm / np.float32(127)).astype(np.float32))
+    # a strided view, and no rows at all
+    y = np.zeros((6, 20), dtype=np.uint16)
+    y[:, :13] = x[:6, :13]
+    assert np.array_equal(oracle.col_absmax(y[:, :13]), np.abs(widened[:6, :13]).max(axis=0))
+    assert np.array_equal(oracle.col_absmax(x[:0]), np.zeros(53, np.float32))
