@@ -127,10 +127,17 @@ def main():
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    wsb = max(L.i8mp_quantize_colwise_workspace_bytes(N, K), L.i8mp_quantize_colwise_workspace_bytes(M, N),
-              L.i8mp_quantize_colwise_workspace_bytes(M, K))
+    cX = torch.empty(K, device=dev)  # column maxima from the row-wise passes
+    cW = torch.empty(K, device=dev)
+    cdY = torch.empty(N, device=dev)
+    wsb = max(L.i8mp_quantize_rowwise_colmax_workspace_bytes(M, K),
+              L.i8mp_quantize_rowwise_colmax_workspace_bytes(N, K),
+              L.i8mp_quantize_rowwise_colmax_workspace_bytes(M, N))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
+    # each row-wise pass also reports its tensor's column maxima, so each
+    # column-wise pass reads its tensor once (i8mp_linear_fwd_colmax /
+    # i8mp_linear_bwd_colmax run the same launches)
     names = ["quant_row_X", "quant_row_W", "gemm_NT_fwd", "quant_row_dY", "quant_col_W",
              "gemm_NN_dgrad", "quant_col_dY", "quant_col_X", "gemm_TN_wgrad"]
 
@@ -138,14 +145,20 @@ def main():
         off = step << 44
         ro = lambda j: off + (j << 40)  # noqa: E731  (per-pass Philox offsets)
         return [
-            lambda: L.i8mp_quantize_rowwise(p(X), M, K, K, p(qX), K, p(sX), r, seed, ro(0), sp),
-            lambda: L.i8mp_quantize_rowwise(p(W), N, K, K, p(qW), K, p(sW), r, seed, ro(1), sp),
+            lambda: L.i8mp_quantize_rowwise_colmax(p(X), M, K, K, p(qX), K, p(sX), p(cX), r, seed, ro(0),
+                                                   p(ws), wsb, sp),
+            lambda: L.i8mp_quantize_rowwise_colmax(p(W), N, K, K, p(qW), K, p(sW), p(cW), r, seed, ro(1),
+                                                   p(ws), wsb, sp),
             lambda: L.i8mp_int8_scaled_mm(0, M, N, K, p(qX), K, p(sX), p(qW), K, p(sW), p(Y), N, sp),
-            lambda: L.i8mp_quantize_rowwise(p(dY), M, N, N, p(qdY), N, p(sdY), r, seed, ro(2), sp),
-            lambda: L.i8mp_quantize_colwise(p(W), N, K, K, p(qWc), K, p(sWc), r, seed, ro(3), p(ws), wsb, sp),
+            lambda: L.i8mp_quantize_rowwise_colmax(p(dY), M, N, N, p(qdY), N, p(sdY), p(cdY), r, seed,
+                                                   ro(2), p(ws), wsb, sp),
+            lambda: L.i8mp_quantize_colwise_given_colmax(p(W), N, K, K, p(cW), p(qWc), K, p(sWc), r, seed,
+                                                         ro(3), sp),
             lambda: L.i8mp_int8_scaled_mm(1, M, K, N, p(qdY), N, p(sdY), p(qWc), K, p(sWc), p(dX), K, sp),
-            lambda: L.i8mp_quantize_colwise(p(dY), M, N, N, p(qdYc), N, p(sdYc), r, seed, ro(4), p(ws), wsb, sp),
-            lambda: L.i8mp_quantize_colwise(p(X), M, K, K, p(qXc), K, p(sXc), r, seed, ro(5), p(ws), wsb, sp),
+            lambda: L.i8mp_quantize_colwise_given_colmax(p(dY), M, N, N, p(cdY), p(qdYc), N, p(sdYc), r,
+                                                         seed, ro(4), sp),
+            lambda: L.i8mp_quantize_colwise_given_colmax(p(X), M, K, K, p(cX), p(qXc), K, p(sXc), r, seed,
+                                                         ro(5), sp),
             lambda: L.i8mp_int8_scaled_mm(2, N, K, M, p(qdYc), N, p(sdYc), p(qXc), K, p(sXc), p(dW), K, sp),
         ]
 
@@ -166,11 +179,14 @@ def main():
     run_step(0)
     Yc, dXc, dWc = Y.clone(), dX.clone(), dW.clone()
     X0, W0, dY0 = sets[0]
-    ok = (torch.equal(i8.linear_fwd(X0, W0, args.rounding, seed, 0).view(torch.int16), Yc.view(torch.int16))
+    Yl, cx0, cw0 = i8.linear_fwd_colmax(X0, W0, args.rounding, seed, 0)
+    ok = (torch.equal(Yl.view(torch.int16), Yc.view(torch.int16))
+          and torch.equal(cx0, cX) and torch.equal(cw0, cW)
           and all(torch.equal(a.view(torch.int16), b.view(torch.int16))
-                  for a, b in zip(i8.linear_bwd(dY0, X0, W0, args.rounding, seed, 0), (dXc, dWc))))
+                  for a, b in zip(i8.linear_bwd(dY0, X0, W0, args.rounding, seed, 0,
+                                                colmax_x=cx0, colmax_w=cw0), (dXc, dWc))))
     if not ok:
-        raise RuntimeError("primitive chain differs from linear_fwd/linear_bwd")
+        raise RuntimeError("primitive chain differs from linear_fwd_colmax/linear_bwd")
 
     for i in range(args.warmup):
         run_step(i)
@@ -202,7 +218,7 @@ def main():
     for i in range(args.steps):
         for j, nm in enumerate(names):
             per[nm] += ev[i][j].elapsed_time(ev[i][j + 1])
-    per = {nm: v / args.steps for nm, v in per.items()}  # ms per launch (colwise: its 2 kernels)
+    per = {nm: v / args.steps for nm, v in per.items()}  # ms per launch (row-wise: 2 kernels)
 
     gemm_ops = 2.0 * M * N * K
     breakdown = {}

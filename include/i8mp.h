@@ -116,6 +116,38 @@ i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols,
                                   void* stream);
 
 /*
+ * Row-wise quantization that also returns each column's maximum magnitude,
+ *   colmax[c] = max_r |x[r,c]|   (fp32; exact: bf16 values widen exactly),
+ * the statistic the column-wise quantization of the same tensor needs
+ * (scale[c] = RN32(colmax[c] / 127)).  Codes and scales are those of
+ * i8mp_quantize_rowwise.  This is how the linear chains avoid a second read
+ * of X, W and dY for their column-wise passes (the pages report dynamic
+ * quantization as a cost worth code-generating: "Integrate INT8
+ * mixed-precision from torchao 0.7", known limitations).
+ *   colmax: fp32 [cols], 4-byte aligned; rows = 0 gives zeros.
+ *   ws: scratch of at least i8mp_quantize_rowwise_colmax_workspace_bytes(rows,
+ *       cols) bytes, 256-byte aligned; its contents on entry do not matter.
+ */
+size_t i8mp_quantize_rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols);
+i8mp_status i8mp_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                         float* colmax, int32_t round, uint64_t seed,
+                                         uint64_t offset, void* ws, size_t ws_bytes,
+                                         void* stream);
+
+/*
+ * Column-wise quantization with the column maxima already known (one pass
+ * over x, no scratch): scale[c] = RN32(colmax[c] / 127), codes as in
+ * i8mp_quantize_colwise.  colmax must hold the column maxima of x (for
+ * instance from i8mp_quantize_rowwise_colmax); other values give the codes
+ * of the scales they imply, clamped to [-127, 127].
+ */
+i8mp_status i8mp_quantize_colwise_given_colmax(const uint16_t* x, int64_t rows, int64_t cols,
+                                               int64_t ldx, const float* colmax, int8_t* q,
+                                               int64_t ldq, float* scale, int32_t round,
+                                               uint64_t seed, uint64_t offset, void* stream);
+
+/*
  * Scaled INT8 matmul ("Quantized model training", section "INT8 mixed
  * precision training"; scaled back to BF16 per "Integrate INT8
  * mixed-precision from torchao 0.7"):
@@ -169,6 +201,29 @@ i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_
                             uint16_t* dW, int64_t M, int64_t N, int64_t K,
                             const i8mp_linear_opts* opts, void* ws, size_t ws_bytes,
                             void* stream);
+
+/*
+ * The same forward, also returning the column maxima of X and W (fp32 [K]
+ * each, as i8mp_quantize_rowwise_colmax defines them) for the backward's
+ * column-wise passes.  Either pointer may be NULL.  Y is identical to
+ * i8mp_linear_fwd's.  Same workspace size.
+ */
+i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                   int64_t N, int64_t K, const i8mp_linear_opts* opts,
+                                   float* colmax_x, float* colmax_w, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
+ * The same backward, taking the column maxima of X and W from the forward
+ * (either may be NULL: that pass then reads its tensor twice).  dX and dW
+ * are identical to i8mp_linear_bwd's when the maxima are X's and W's.  The
+ * column maxima of dY always come from its row-wise pass when both outputs
+ * are wanted.  Same workspace size.
+ */
+i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                   uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                   const i8mp_linear_opts* opts, const float* colmax_x,
+                                   const float* colmax_w, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

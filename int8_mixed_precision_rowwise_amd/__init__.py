@@ -22,7 +22,8 @@ __all__ = [
     "I8mpError", "RNE", "SR", "NT", "NN", "TN", "MAX_CONTRACTION", "lib",
     "quantize_rowwise", "quantize_colwise", "int8_scaled_mm", "int8_mm_i32",
     "philox4x32_10", "linear_fwd", "linear_bwd", "linear_workspace_bytes",
-    "colwise_workspace_bytes", "EXPORTED_SYMBOLS",
+    "colwise_workspace_bytes", "quantize_rowwise_colmax", "quantize_colwise_given_colmax",
+    "rowwise_colmax_workspace_bytes", "linear_fwd_colmax", "EXPORTED_SYMBOLS",
 ]
 
 RNE, SR = 0, 1
@@ -35,7 +36,9 @@ EXPORTED_SYMBOLS = (
     "i8mp_status_str", "i8mp_abi_version", "i8mp_quantize_rowwise",
     "i8mp_quantize_colwise_workspace_bytes", "i8mp_quantize_colwise", "i8mp_int8_scaled_mm",
     "i8mp_int8_mm_i32", "i8mp_philox4x32_10", "i8mp_linear_workspace_bytes", "i8mp_linear_fwd",
-    "i8mp_linear_bwd",
+    "i8mp_linear_bwd", "i8mp_quantize_rowwise_colmax_workspace_bytes",
+    "i8mp_quantize_rowwise_colmax", "i8mp_quantize_colwise_given_colmax", "i8mp_linear_fwd_colmax",
+    "i8mp_linear_bwd_colmax",
 )
 
 
@@ -69,6 +72,12 @@ def _load() -> ctypes.CDLL:
         "i8mp_linear_workspace_bytes": ([i64, i64, i64, i32], sz),
         "i8mp_linear_fwd": ([p, p, p, i64, i64, i64, ctypes.POINTER(_Opts), p, sz, p], i32),
         "i8mp_linear_bwd": ([p, p, p, p, p, i64, i64, i64, ctypes.POINTER(_Opts), p, sz, p], i32),
+        "i8mp_quantize_rowwise_colmax_workspace_bytes": ([i64, i64], sz),
+        "i8mp_quantize_rowwise_colmax": ([p, i64, i64, i64, p, i64, p, p, i32, u64, u64, p, sz, p], i32),
+        "i8mp_quantize_colwise_given_colmax": ([p, i64, i64, i64, p, p, i64, p, i32, u64, u64, p], i32),
+        "i8mp_linear_fwd_colmax": ([p, p, p, i64, i64, i64, ctypes.POINTER(_Opts), p, p, p, sz, p], i32),
+        "i8mp_linear_bwd_colmax": ([p, p, p, p, p, i64, i64, i64, ctypes.POINTER(_Opts), p, p, p, sz, p],
+                                   i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -132,6 +141,50 @@ def quantize_rowwise(x: torch.Tensor, rounding="rne", seed: int = 0, offset: int
         st = lib.i8mp_quantize_rowwise(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
                                        _ROUNDING[rounding], seed, offset, _stream(x.device))
     _check(st, "i8mp_quantize_rowwise")
+    return q, scale
+
+
+def rowwise_colmax_workspace_bytes(rows: int, cols: int) -> int:
+    return lib.i8mp_quantize_rowwise_colmax_workspace_bytes(rows, cols)
+
+
+def quantize_rowwise_colmax(x: torch.Tensor, rounding="rne", seed: int = 0, offset: int = 0,
+                            q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                            colmax: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None):
+    """Row-wise quantization that also returns the column maxima of |x|:
+    (int8 q [R, C], fp32 scale [R], fp32 colmax [C])."""
+    _bits(x)
+    R, C = x.shape
+    q = _empty_2d(R, C, torch.int8, x.device) if q is None else q
+    scale = torch.empty(R, dtype=torch.float32, device=x.device) if scale is None else scale
+    colmax = torch.empty(C, dtype=torch.float32, device=x.device) if colmax is None else colmax
+    need = rowwise_colmax_workspace_bytes(R, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        st = lib.i8mp_quantize_rowwise_colmax(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
+                                              _ptr(colmax), _ROUNDING[rounding], seed, offset,
+                                              _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check(st, "i8mp_quantize_rowwise_colmax")
+    return q, scale, colmax
+
+
+def quantize_colwise_given_colmax(x: torch.Tensor, colmax: torch.Tensor, rounding="rne",
+                                  seed: int = 0, offset: int = 0, q: torch.Tensor | None = None,
+                                  scale: torch.Tensor | None = None):
+    """Column-wise quantization with known column maxima (one pass):
+    (int8 q [R, C] in x's layout, fp32 scale [C])."""
+    _bits(x)
+    _bits(colmax, torch.float32)
+    R, C = x.shape
+    q = _empty_2d(R, C, torch.int8, x.device) if q is None else q
+    scale = torch.empty(C, dtype=torch.float32, device=x.device) if scale is None else scale
+    with torch.cuda.device(x.device):
+        st = lib.i8mp_quantize_colwise_given_colmax(_ptr(x), R, C, _ld(x), _ptr(colmax), _ptr(q),
+                                                    _ld(q), _ptr(scale), _ROUNDING[rounding], seed,
+                                                    offset, _stream(x.device))
+    _check(st, "i8mp_quantize_colwise_given_colmax")
     return q, scale
 
 
@@ -244,12 +297,41 @@ def linear_fwd(X: torch.Tensor, W: torch.Tensor, rounding="rne", seed: int = 0, 
     return Y
 
 
+def linear_fwd_colmax(X: torch.Tensor, W: torch.Tensor, rounding="rne", seed: int = 0,
+                      offset: int = 0, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
+    """linear_fwd that also returns the column maxima of X and W (fp32 [K]
+    each) for linear_bwd: (Y, colmax_x, colmax_w)."""
+    _bits(X), _bits(W)
+    M, K = X.shape
+    N = W.shape[0]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device) if out is None else out
+    cx = torch.empty(K, dtype=torch.float32, device=X.device)
+    cw = torch.empty(K, dtype=torch.float32, device=X.device)
+    need = linear_workspace_bytes(M, N, K, False)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    o = _opts(rounding, seed, offset)
+    with torch.cuda.device(X.device):
+        st = lib.i8mp_linear_fwd_colmax(_ptr(X), _ptr(W), _ptr(Y), M, N, K, ctypes.byref(o),
+                                        _ptr(cx), _ptr(cw), _ptr(workspace), workspace.numel(),
+                                        _stream(X.device))
+    _check(st, "i8mp_linear_fwd_colmax")
+    return Y, cx, cw
+
+
 def linear_bwd(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, rounding="rne", seed: int = 0,
                offset: int = 0, want_dx: bool = True, want_dw: bool = True,
                dX: torch.Tensor | None = None, dW: torch.Tensor | None = None,
-               workspace: torch.Tensor | None = None):
-    """(dX = dY @ W, dW = dY.T @ X), each quantized along its own contraction."""
+               workspace: torch.Tensor | None = None, colmax_x: torch.Tensor | None = None,
+               colmax_w: torch.Tensor | None = None):
+    """(dX = dY @ W, dW = dY.T @ X), each quantized along its own contraction.
+    colmax_x / colmax_w: the column maxima from linear_fwd_colmax (optional;
+    the results are the same, the column-wise passes then read X / W once)."""
     _bits(dY), _bits(X), _bits(W)
+    for c in (colmax_x, colmax_w):
+        if c is not None:
+            _bits(c, torch.float32)
     M, N = dY.shape
     K = W.shape[1]
     if want_dx and dX is None:
@@ -261,8 +343,9 @@ def linear_bwd(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, rounding="rne
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dY.device)
     o = _opts(rounding, seed, offset)
     with torch.cuda.device(dY.device):
-        st = lib.i8mp_linear_bwd(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX if want_dx else None),
-                                 _ptr(dW if want_dw else None), M, N, K, ctypes.byref(o),
-                                 _ptr(workspace), workspace.numel(), _stream(dY.device))
-    _check(st, "i8mp_linear_bwd")
+        st = lib.i8mp_linear_bwd_colmax(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX if want_dx else None),
+                                        _ptr(dW if want_dw else None), M, N, K, ctypes.byref(o),
+                                        _ptr(colmax_x), _ptr(colmax_w), _ptr(workspace),
+                                        workspace.numel(), _stream(dY.device))
+    _check(st, "i8mp_linear_bwd_colmax")
     return (dX if want_dx else None), (dW if want_dw else None)

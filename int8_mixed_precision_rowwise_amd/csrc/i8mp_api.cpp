@@ -148,6 +148,7 @@ struct Carver {
 struct FwdWs {
   int8_t *qx, *qw;
   float *sx, *sw;
+  void* part;  // slab column maxima of the row-wise passes
 };
 size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   Carver c{static_cast<char*>(ws)};
@@ -157,14 +158,18 @@ size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   w.qw = static_cast<int8_t*>(c.take((size_t)(N * kp)));
   w.sx = static_cast<float*>(c.take((size_t)M * 4));
   w.sw = static_cast<float*>(c.take((size_t)N * 4));
+  size_t part = i8mp::rowwise_colmax_workspace_bytes(M, K);
+  const size_t p2 = i8mp::rowwise_colmax_workspace_bytes(N, K);
+  if (p2 > part) part = p2;
+  w.part = c.take(part);
   if (out) *out = w;
   return c.used;
 }
 
 struct BwdWs {
   int8_t *qdy, *qw, *qx;
-  float *sdy, *sw, *sx;
-  void* col;
+  float *sdy, *sw, *sx, *cdy;
+  void* col;  // slab column maxima (column-wise passes, dY's row-wise pass)
 };
 size_t carve_bwd(void* ws, int64_t M, int64_t N, int64_t K, BwdWs* out) {
   Carver c{static_cast<char*>(ws)};
@@ -176,10 +181,11 @@ size_t carve_bwd(void* ws, int64_t M, int64_t N, int64_t K, BwdWs* out) {
   w.sdy = static_cast<float*>(c.take((size_t)(M > N ? M : N) * 4));
   w.sw = static_cast<float*>(c.take((size_t)K * 4));
   w.sx = static_cast<float*>(c.take((size_t)K * 4));
+  w.cdy = static_cast<float*>(c.take((size_t)N * 4));
   size_t col = i8mp::colwise_workspace_bytes(N, K);
-  const size_t c2 = i8mp::colwise_workspace_bytes(M, N), c3 = i8mp::colwise_workspace_bytes(M, K);
-  if (c2 > col) col = c2;
-  if (c3 > col) col = c3;
+  for (size_t n : {i8mp::colwise_workspace_bytes(M, N), i8mp::colwise_workspace_bytes(M, K),
+                   i8mp::rowwise_colmax_workspace_bytes(M, N)})
+    if (n > col) col = n;
   w.col = c.take(col);
   if (out) *out = w;
   return c.used;
@@ -239,6 +245,53 @@ i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols,
                                                   offset, ws, as_stream(stream)));
 }
 
+size_t i8mp_quantize_rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols) {
+  if (!dims_ok(rows, cols) || cols == 0) return 0;
+  return up(i8mp::rowwise_colmax_workspace_bytes(rows, cols));
+}
+
+i8mp_status i8mp_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                         float* colmax, int32_t round, uint64_t seed,
+                                         uint64_t offset, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q, ldq, scale, rows, round);
+  if (st != I8MP_OK) return st;
+  if (!vec_ok(colmax, cols)) return I8MP_EINVAL;
+  const Range rx = mat_range(x, rows, cols, ldx, 2), rq = mat_range(q, rows, cols, ldq, 1),
+              rs = vec_range(scale, rows, 4), rc = vec_range(colmax, cols, 4);
+  if (overlap(rc, rx) || overlap(rc, rq) || overlap(rc, rs)) return I8MP_EINVAL;
+  if (cols == 0) {
+    if (rows == 0) return I8MP_OK;
+    if ((st = device_check()) != I8MP_OK) return st;
+    return hip_status(i8mp::launch_quantize_rowwise(x, rows, cols, ldx, q, ldq, scale, round, seed,
+                                                    offset, as_stream(stream)));
+  }
+  const size_t need = i8mp_quantize_rowwise_colmax_workspace_bytes(rows, cols);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  if (overlap(rw, rx) || overlap(rw, rq) || overlap(rw, rs) || overlap(rw, rc)) return I8MP_EINVAL;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_rowwise_colmax(x, rows, cols, ldx, q, ldq, scale, colmax,
+                                                         round, seed, offset, ws, as_stream(stream)));
+}
+
+i8mp_status i8mp_quantize_colwise_given_colmax(const uint16_t* x, int64_t rows, int64_t cols,
+                                               int64_t ldx, const float* colmax, int8_t* q,
+                                               int64_t ldq, float* scale, int32_t round,
+                                               uint64_t seed, uint64_t offset, void* stream) {
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q, ldq, scale, cols, round);
+  if (st != I8MP_OK) return st;
+  if (!vec_ok(colmax, cols)) return I8MP_EINVAL;
+  const Range rc = vec_range(colmax, cols, 4);
+  if (overlap(rc, mat_range(q, rows, cols, ldq, 1)) || overlap(rc, vec_range(scale, cols, 4)))
+    return I8MP_EINVAL;
+  if (cols == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_colwise_given(x, rows, cols, ldx, colmax, q, ldq, scale,
+                                                        round, seed, offset, as_stream(stream)));
+}
+
 i8mp_status i8mp_int8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K,
                                 const int8_t* A, int64_t lda, const float* scale_a,
                                 const int8_t* B, int64_t ldb, const float* scale_b, uint16_t* C,
@@ -277,43 +330,62 @@ size_t i8mp_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t back
   return backward ? carve_bwd(nullptr, M, N, K, nullptr) : carve_fwd(nullptr, M, N, K, nullptr);
 }
 
-i8mp_status i8mp_linear_fwd(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
-                            int64_t N, int64_t K, const i8mp_linear_opts* opts, void* ws,
-                            size_t ws_bytes, void* stream) {
+i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                   int64_t N, int64_t K, const i8mp_linear_opts* opts,
+                                   float* colmax_x, float* colmax_w, void* ws, size_t ws_bytes,
+                                   void* stream) {
   if (!opts || (opts->round != I8MP_RNE && opts->round != I8MP_SR)) return I8MP_EINVAL;
   if (!dims_ok(M, N, K)) return I8MP_EINVAL;
   if (K > I8MP_MAX_CONTRACTION) return I8MP_ERANGE;
   if (!chunked_ok(X, M, K, K, 2) || !chunked_ok(W, N, K, K, 2) || !elementwise_ok(Y, M, N, N, 2))
     return I8MP_EINVAL;
-  const Range ry = mat_range(Y, M, N, N, 2);
-  if (overlap(ry, mat_range(X, M, K, K, 2)) || overlap(ry, mat_range(W, N, K, K, 2)))
-    return I8MP_EINVAL;
+  if ((colmax_x && !vec_ok(colmax_x, K)) || (colmax_w && !vec_ok(colmax_w, K))) return I8MP_EINVAL;
+  const Range ry = mat_range(Y, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
+              rwt = mat_range(W, N, K, K, 2);
+  const Range rcx = colmax_x ? vec_range(colmax_x, K, 4) : Range{},
+              rcw = colmax_w ? vec_range(colmax_w, K, 4) : Range{};
+  if (overlap(ry, rx) || overlap(ry, rwt)) return I8MP_EINVAL;
+  for (Range o : {ry, rx, rwt})
+    if (overlap(o, rcx) || overlap(o, rcw)) return I8MP_EINVAL;
+  if (overlap(rcx, rcw)) return I8MP_EINVAL;
   if (M == 0 || N == 0) return I8MP_OK;
   const size_t need = carve_fwd(nullptr, M, N, K, nullptr);
   if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
   const Range rw = vec_range(ws, (int64_t)need, 1);
-  if (overlap(rw, ry) || overlap(rw, mat_range(X, M, K, K, 2)) || overlap(rw, mat_range(W, N, K, K, 2)))
-    return I8MP_EINVAL;
+  for (Range o : {ry, rx, rwt, rcx, rcw})
+    if (overlap(rw, o)) return I8MP_EINVAL;
   i8mp_status st = device_check();
   if (st != I8MP_OK) return st;
   FwdWs w;
   carve_fwd(ws, M, N, K, &w);
   const hipStream_t s = as_stream(stream);
   const int64_t kp = pad16(K);
-  hipError_t e = i8mp::launch_quantize_rowwise(X, M, K, K, w.qx, kp, w.sx, opts->round, opts->seed,
+  const int r = opts->round;
+  hipError_t e =
+      colmax_x ? i8mp::launch_quantize_rowwise_colmax(X, M, K, K, w.qx, kp, w.sx, colmax_x, r, opts->seed,
+                                                      pass_offset(opts->offset, 0), w.part, s)
+               : i8mp::launch_quantize_rowwise(X, M, K, K, w.qx, kp, w.sx, r, opts->seed,
                                                pass_offset(opts->offset, 0), s);
   if (e == hipSuccess)
-    e = i8mp::launch_quantize_rowwise(W, N, K, K, w.qw, kp, w.sw, opts->round, opts->seed,
-                                      pass_offset(opts->offset, 1), s);
+    e = colmax_w ? i8mp::launch_quantize_rowwise_colmax(W, N, K, K, w.qw, kp, w.sw, colmax_w, r, opts->seed,
+                                                        pass_offset(opts->offset, 1), w.part, s)
+                 : i8mp::launch_quantize_rowwise(W, N, K, K, w.qw, kp, w.sw, r, opts->seed,
+                                                 pass_offset(opts->offset, 1), s);
   if (e == hipSuccess)
     e = i8mp::launch_gemm(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, nullptr, N, s);
   return hip_status(e);
 }
 
-i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
-                            uint16_t* dW, int64_t M, int64_t N, int64_t K,
-                            const i8mp_linear_opts* opts, void* ws, size_t ws_bytes,
-                            void* stream) {
+i8mp_status i8mp_linear_fwd(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                            int64_t N, int64_t K, const i8mp_linear_opts* opts, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return i8mp_linear_fwd_colmax(X, W, Y, M, N, K, opts, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                   uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                   const i8mp_linear_opts* opts, const float* colmax_x,
+                                   const float* colmax_w, void* ws, size_t ws_bytes, void* stream) {
   if (!opts || (opts->round != I8MP_RNE && opts->round != I8MP_SR)) return I8MP_EINVAL;
   if (!dims_ok(M, N, K)) return I8MP_EINVAL;
   if (dX && N > I8MP_MAX_CONTRACTION) return I8MP_ERANGE;
@@ -321,19 +393,23 @@ i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_
   if (!chunked_ok(dY, M, N, N, 2)) return I8MP_EINVAL;
   if (dX && (!chunked_ok(W, N, K, K, 2) || !elementwise_ok(dX, M, K, K, 2))) return I8MP_EINVAL;
   if (dW && (!chunked_ok(X, M, K, K, 2) || !elementwise_ok(dW, N, K, K, 2))) return I8MP_EINVAL;
+  if ((colmax_x && !vec_ok(colmax_x, K)) || (colmax_w && !vec_ok(colmax_w, K))) return I8MP_EINVAL;
   if (dX && dW && dX == dW && M * K > 0 && N * K > 0) return I8MP_EINVAL;
   const Range rdy = mat_range(dY, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
               rwt = mat_range(W, N, K, K, 2), rdx = dX ? mat_range(dX, M, K, K, 2) : Range{},
               rdw = dW ? mat_range(dW, N, K, K, 2) : Range{};
+  const Range rcx = colmax_x ? vec_range(colmax_x, K, 4) : Range{},
+              rcw = colmax_w ? vec_range(colmax_w, K, 4) : Range{};
   for (Range o : {rdx, rdw})
-    if (overlap(o, rdy) || overlap(o, rx) || overlap(o, rwt)) return I8MP_EINVAL;
+    if (overlap(o, rdy) || overlap(o, rx) || overlap(o, rwt) || overlap(o, rcx) || overlap(o, rcw))
+      return I8MP_EINVAL;
   if (overlap(rdx, rdw)) return I8MP_EINVAL;
   const bool want_dx = dX && M > 0 && K > 0, want_dw = dW && N > 0 && K > 0;
   if (!want_dx && !want_dw) return I8MP_OK;
   const size_t need = carve_bwd(nullptr, M, N, K, nullptr);
   if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
   const Range rw = vec_range(ws, (int64_t)need, 1);
-  for (Range o : {rdy, rx, rwt, rdx, rdw})
+  for (Range o : {rdy, rx, rwt, rdx, rdw, rcx, rcw})
     if (overlap(rw, o)) return I8MP_EINVAL;
   i8mp_status st = device_check();
   if (st != I8MP_OK) return st;
@@ -343,28 +419,46 @@ i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_
   const int64_t kp = pad16(K), np = pad16(N);
   const int r = opts->round;
   const uint64_t seed = opts->seed;
+  // dY's column maxima come from its row-wise pass when both GEMMs run
+  const bool dy_colmax = want_dx && want_dw;
   hipError_t e = hipSuccess;
   if (want_dx) {
     // dX = dY @ W: dY row-wise over N, W column-wise over N, NN
-    e = i8mp::launch_quantize_rowwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
-                                      pass_offset(opts->offset, 2), s);
+    e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
+                                                         pass_offset(opts->offset, 2), w.col, s)
+                  : i8mp::launch_quantize_rowwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
+                                                  pass_offset(opts->offset, 2), s);
     if (e == hipSuccess)
-      e = i8mp::launch_quantize_colwise(W, N, K, K, w.qw, kp, w.sw, r, seed,
-                                        pass_offset(opts->offset, 3), w.col, s);
+      e = colmax_w ? i8mp::launch_quantize_colwise_given(W, N, K, K, colmax_w, w.qw, kp, w.sw, r, seed,
+                                                         pass_offset(opts->offset, 3), s)
+                   : i8mp::launch_quantize_colwise(W, N, K, K, w.qw, kp, w.sw, r, seed,
+                                                   pass_offset(opts->offset, 3), w.col, s);
     if (e == hipSuccess)
       e = i8mp::launch_gemm(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, nullptr, K, s);
   }
   if (want_dw && e == hipSuccess) {
     // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
-    e = i8mp::launch_quantize_colwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
-                                      pass_offset(opts->offset, 4), w.col, s);
+    e = dy_colmax ? i8mp::launch_quantize_colwise_given(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, r, seed,
+                                                        pass_offset(opts->offset, 4), s)
+                  : i8mp::launch_quantize_colwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
+                                                  pass_offset(opts->offset, 4), w.col, s);
     if (e == hipSuccess)
-      e = i8mp::launch_quantize_colwise(X, M, K, K, w.qx, kp, w.sx, r, seed,
-                                        pass_offset(opts->offset, 5), w.col, s);
+      e = colmax_x ? i8mp::launch_quantize_colwise_given(X, M, K, K, colmax_x, w.qx, kp, w.sx, r, seed,
+                                                         pass_offset(opts->offset, 5), s)
+                   : i8mp::launch_quantize_colwise(X, M, K, K, w.qx, kp, w.sx, r, seed,
+                                                   pass_offset(opts->offset, 5), w.col, s);
     if (e == hipSuccess)
       e = i8mp::launch_gemm(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, nullptr, K, s);
   }
   return hip_status(e);
+}
+
+i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
+                            uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                            const i8mp_linear_opts* opts, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return i8mp_linear_bwd_colmax(dY, X, W, dX, dW, M, N, K, opts, nullptr, nullptr, ws, ws_bytes,
+                                stream);
 }
 
 }  // extern "C"

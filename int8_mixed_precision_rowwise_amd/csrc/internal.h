@@ -14,12 +14,26 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols
                                    int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
                                    uint64_t offset, hipStream_t stream);
 
-// Column-wise quantization: partial column maxima into ws, a finalize pass
-// writing the scales, then the quantize pass.
+// Column-wise quantization: slab column maxima into ws, then the quantize
+// pass (which reduces the slabs to the scales first).
 size_t colwise_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                    int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
                                    uint64_t offset, void* ws, hipStream_t stream);
+
+// Row-wise quantization that also writes colmax[c] = max_r |x[r,c]| (fp32),
+// via slab maxima in ws.
+size_t rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
+                                          int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                          float* colmax, int round, uint64_t seed, uint64_t offset,
+                                          void* ws, hipStream_t stream);
+
+// Column-wise quantization with the column maxima given: one pass.
+hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ldx, const float* colmax, int8_t* q, int64_t ldq,
+                                         float* scale, int round, uint64_t seed, uint64_t offset,
+                                         hipStream_t stream);
 
 // int8 GEMM in layout 0 = NT, 1 = NN, 2 = TN.  Exactly one of (C_bf16 with
 // both scales) or C_i32 is non-null.

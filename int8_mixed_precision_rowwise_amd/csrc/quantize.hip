@@ -338,7 +338,7 @@ constexpr int kColTile = 512;
 constexpr int kColThreads = 512;
 constexpr int kColWaves = kColThreads / 64;
 constexpr int kColMaxSlabs = 32;
-constexpr int kColLoads = 8;  // rows in flight per wave
+constexpr int kColLoads = 16;  // rows in flight per wave
 
 __device__ __forceinline__ void max_chunk(us2 (&m)[4], uint4 v) {
   m[0] = __builtin_elementwise_max(m[0], as_us2(v.x & 0x7FFF7FFFu));
@@ -402,16 +402,19 @@ __global__ __launch_bounds__(kColThreads) void col_absmax_partial(const uint16_t
   }
 }
 
-template <bool SR, bool ALIGNED4>
+// GIVEN: the column maxima come in as fp32 values (colmax) instead of slab
+// maxima to reduce (part, part_ld, slabs unused).
+template <bool SR, bool ALIGNED4, bool GIVEN>
 __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __restrict__ x, int64_t rows,
                                                           int64_t cols, int64_t ldx,
                                                           int64_t rows_per_block,
                                                           const uint16_t* __restrict__ part,
                                                           int64_t part_ld, int64_t slabs,
+                                                          const float* __restrict__ colmax,
                                                           float* __restrict__ scale,
                                                           int8_t* __restrict__ q, int64_t ldq,
                                                           uint64_t seed, uint64_t offset) {
-  __shared__ uint4 red[kColWaves][64];
+  __shared__ uint4 red[GIVEN ? 1 : kColWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
   const bool active = c0 < cols;
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
   const int64_t rb = (int64_t)gridDim.y - 1 - blockIdx.y;
   const int64_t r_begin = rb * rows_per_block;
   const int64_t r_end = min(rows, r_begin + rows_per_block);
-  constexpr int U = kColLoads;
+  constexpr int U = SR ? kColLoads / 2 : kColLoads;  // SR's Philox state needs the registers
   // the first rows' loads go out before the scales are known
   uint4 v[U];
   int64_t r0 = r_begin + wave;
@@ -429,22 +432,30 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
     const int64_t r = r0 + (int64_t)k * kColWaves;
     v[k] = active && r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
   }
-  // column maxima of the tile from the slab maxima
-  us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
-  if (active) {
-    for (int64_t s = wave; s < slabs; s += kColWaves)
-      max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
-  }
-  red[wave][lane] = pack_max(m);
-  __syncthreads();
-  if (!active) return;
-  reduce_waves(m, red, lane);
-  const int nvalid = (int)min((int64_t)8, cols - c0);
   GroupScale g[8];
+  int nvalid = 0;
+  if constexpr (GIVEN) {
+    if (!active) return;
+    nvalid = (int)min((int64_t)8, cols - c0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t bits = j & 1 ? m[j >> 1].y : m[j >> 1].x;
-    g[j] = make_scale(j < nvalid ? bits : 0u);
+    for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? colmax[c0 + j] / 127.0f : 0.0f);
+  } else {
+    // column maxima of the tile from the slab maxima
+    us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+    if (active) {
+      for (int64_t s = wave; s < slabs; s += kColWaves)
+        max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
+    }
+    red[wave][lane] = pack_max(m);
+    __syncthreads();
+    if (!active) return;
+    reduce_waves(m, red, lane);
+    nvalid = (int)min((int64_t)8, cols - c0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t bits = j & 1 ? m[j >> 1].y : m[j >> 1].x;
+      g[j] = make_scale(j < nvalid ? bits : 0u);
+    }
   }
   if (blockIdx.y == 0 && wave == 0) {
 #pragma unroll
@@ -478,6 +489,107 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
       const int64_t r = rn + (int64_t)k * kColWaves;
       v[k] = r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise with column maxima.  A block of WAVES waves owns a band of
+// rows_per_block rows; wave w quantizes rows band + w, band + w + WAVES, ...
+// exactly as quant_rows_wave does.  Each wave also keeps the running maximum
+// of |x| of every column in its own LDS region (lane l's chunk i covers
+// columns 8 (64 i + l) .. + 7; one 16-byte read-modify-write per chunk and
+// row, so the row in registers is all the per-lane state).  At the end the
+// block folds its waves' regions and writes one slab of column maxima (bf16
+// bit patterns) to the workspace; colmax_finalize reduces the slabs.  So the
+// row-wise pass of a tensor also yields what its column-wise pass needs,
+// without a second read of the tensor.
+
+template <int NV, int WAVES, bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset, int64_t rows_per_block,
+    uint16_t* __restrict__ part, int64_t part_ld) {
+  __shared__ uint4 cm[WAVES][NV * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r_begin = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t r_end = min(rows, r_begin + rows_per_block);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) cm[wave][i * 64 + lane] = make_uint4(0, 0, 0, 0);
+  uint4 v[NV];
+  int64_t r = r_begin + wave;
+  if (r < r_end) load_row<NV>(v, x + r * ldx, cols, lane);
+  for (; r < r_end; r += WAVES) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {  // load_row zeroed the columns past the end
+      us2 m[4];
+      const uint4 o = cm[wave][i * 64 + lane];
+      m[0] = as_us2(o.x), m[1] = as_us2(o.y), m[2] = as_us2(o.z), m[3] = as_us2(o.w);
+      max_chunk(m, v[i]);
+      cm[wave][i * 64 + lane] = pack_max(m);
+    }
+    quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
+    const int64_t rn = r + WAVES;
+    if (rn < r_end) load_row<NV>(v, x + rn * ldx, cols, lane);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < NV * 64; j += 64 * WAVES) {
+    const int64_t c0 = (int64_t)j * 8;
+    if (c0 >= cols) continue;
+    us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) max_chunk(m, cm[w][j]);
+    *reinterpret_cast<uint4*>(part + (int64_t)blockIdx.x * part_ld + c0) = pack_max(m);
+  }
+}
+
+// fp32 column maxima from slab maxima.  A block of 16 waves covers 64
+// columns: lane l reads the 16-byte chunk l % 8 (8 columns) of slab l / 8 of
+// each group of 8 slabs, so one load instruction of a wave covers 8 slabs;
+// wave w takes slab groups w, w + 16, ...  The 8 lanes sharing a chunk, then
+// the 16 waves, are folded.
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
+
+__global__ __launch_bounds__(kFinThreads) void colmax_finalize(const uint16_t* __restrict__ part,
+                                                               int64_t part_ld, int64_t slabs,
+                                                               int64_t cols,
+                                                               float* __restrict__ colmax) {
+  __shared__ uint4 red[kFinWaves][8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = lane & 7, sub = lane >> 3;
+  const int64_t c0 = (int64_t)blockIdx.x * 64 + chunk * 8;
+  us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  if (c0 < cols) {
+    constexpr int U = 4;
+    int64_t s = (int64_t)wave * 8 + sub;
+    constexpr int64_t step = (int64_t)kFinWaves * 8;
+    for (; s + (U - 1) * step < slabs; s += U * step) {
+      uint4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) v[k] = *reinterpret_cast<const uint4*>(part + (s + k * step) * part_ld + c0);
+#pragma unroll
+      for (int k = 0; k < U; ++k) max_chunk(m, v[k]);
+    }
+    for (; s < slabs; s += step) max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
+  }
+  // fold the 8 lanes of each chunk (lanes chunk, chunk + 8, ..., chunk + 56)
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)__builtin_bit_cast(uint32_t, m[k]), off);
+      m[k] = __builtin_elementwise_max(m[k], as_us2(o));
+    }
+  }
+  if (sub == 0) red[wave][chunk] = pack_max(m);
+  __syncthreads();
+  if (wave == 0 && sub == 0 && c0 < cols) {
+#pragma unroll
+    for (int w = 1; w < kFinWaves; ++w) max_chunk(m, red[w][chunk]);
+    const uint32_t b[8] = {m[0].x, m[0].y, m[1].x, m[1].y, m[2].x, m[2].y, m[3].x, m[3].y};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < cols) colmax[c0 + j] = __uint_as_float(b[j] << 16);
   }
 }
 
@@ -521,6 +633,54 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
       quant_rows_wave<NV, true, false, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   } else {
     quant_rows_wave<NV, false, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+  }
+}
+
+// Row-wise with column maxima: 8 waves per block (4 for rows of more than
+// 6144 elements, whose per-lane state and LDS regions are larger), about
+// 256 blocks, each a band of whole rows.  Rows longer than 14336 elements (the block-per-row
+// kernel) get their column maxima from a separate column-maxima pass.
+struct RowColmaxPlan {
+  bool fused;
+  int waves;
+  int64_t rows_per_block, slabs, part_ld;
+};
+
+RowColmaxPlan rcm_plan(int64_t rows, int64_t cols) {
+  RowColmaxPlan p;
+  const int64_t per_lane = (cols + 511) / 512;
+  p.fused = per_lane <= 28;
+  p.part_ld = (cols + 7) / 8 * 8;
+  if (p.fused) {
+    // about one block per CU (a block's registers and LDS fill most of one)
+    p.waves = per_lane > 12 ? 4 : 8;
+    int64_t rpb = (rows + 255) / 256;
+    rpb = (rpb + p.waves - 1) / p.waves * p.waves;
+    p.rows_per_block = max(rpb, (int64_t)p.waves);
+    p.slabs = (rows + p.rows_per_block - 1) / p.rows_per_block;
+  } else {
+    const ColPlan c = col_plan(rows, cols);
+    p.waves = kColWaves;
+    p.rows_per_block = c.rows_per_slab;
+    p.slabs = c.slabs;
+  }
+  return p;
+}
+
+template <int NV>
+void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int64_t cols,
+                   int64_t ldx, int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
+                   uint64_t offset, uint16_t* part, hipStream_t stream) {
+  constexpr int WAVES = NV >= 16 ? 4 : 8;  // LDS: WAVES x NV KiB of column maxima
+  const dim3 grid((unsigned)p.slabs);
+  const bool a4 = (cols % 4) == 0;
+  if (round == 1) {
+    if (a4)
+      quant_rows_colmax<NV, WAVES, true, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+    else
+      quant_rows_colmax<NV, WAVES, true, false><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+  } else {
+    quant_rows_colmax<NV, WAVES, false, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   }
 }
 
@@ -580,11 +740,73 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if (a4)
-      quant_cols<true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
+      quant_cols<true, true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale, q, ldq, seed, offset);
     else
-      quant_cols<true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
+      quant_cols<true, false, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale, q, ldq, seed, offset);
   } else {
-    quant_cols<false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
+    quant_cols<false, true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale, q, ldq, seed, offset);
+  }
+  return hipGetLastError();
+}
+
+
+size_t rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols) {
+  const RowColmaxPlan p = rcm_plan(rows, cols);
+  return (size_t)(max(p.slabs, (int64_t)1) * p.part_ld * 2);
+}
+
+hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
+                                          int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                          float* colmax, int round, uint64_t seed, uint64_t offset,
+                                          void* ws, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const RowColmaxPlan p = rcm_plan(rows, cols);
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  if (rows > 0) {
+    if (p.fused) {
+      const int64_t per_lane = (cols + 511) / 512;
+      if (per_lane <= 1)
+        launch_rcm_nv<1>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else if (per_lane <= 2)
+        launch_rcm_nv<2>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else if (per_lane <= 4)
+        launch_rcm_nv<4>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else if (per_lane <= 8)
+        launch_rcm_nv<8>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else if (per_lane <= 12)
+        launch_rcm_nv<12>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else if (per_lane <= 16)
+        launch_rcm_nv<16>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else
+        launch_rcm_nv<28>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+    } else {
+      const hipError_t e = launch_quantize_rowwise(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+      if (e != hipSuccess) return e;
+      const ColPlan c = col_plan(rows, cols);
+      col_absmax_partial<<<dim3((unsigned)c.col_tiles, (unsigned)c.slabs), kColThreads, 0, stream>>>(
+          x, rows, cols, ldx, c.rows_per_slab, part, c.part_ld);
+    }
+  }
+  colmax_finalize<<<dim3((unsigned)((cols + 63) / 64)), kFinThreads, 0, stream>>>(
+      part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ldx, const float* colmax, int8_t* q, int64_t ldq,
+                                         float* scale, int round, uint64_t seed, uint64_t offset,
+                                         hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const ColPlan p = col_plan(rows, cols);
+  const dim3 grid((unsigned)p.col_tiles, (unsigned)p.row_blocks);
+  const bool a4 = (cols % 4) == 0;
+  if (round == 1) {
+    if (a4)
+      quant_cols<true, true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, nullptr, 0, 0, colmax, scale, q, ldq, seed, offset);
+    else
+      quant_cols<true, false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, nullptr, 0, 0, colmax, scale, q, ldq, seed, offset);
+  } else {
+    quant_cols<false, true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, nullptr, 0, 0, colmax, scale, q, ldq, seed, offset);
   }
   return hipGetLastError();
 }

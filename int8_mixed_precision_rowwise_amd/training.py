@@ -29,7 +29,7 @@ from typing import Callable, Optional
 
 import torch
 
-from . import linear_bwd, linear_fwd
+from . import linear_bwd, linear_fwd, linear_fwd_colmax
 
 __all__ = ["Int8MixedPrecisionConfig", "Int8MixedPrecisionLinearFunction",
            "Int8MixedPrecisionLinear", "swap_linear_modules", "STEP_STRIDE", "module_seed"]
@@ -73,7 +73,9 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
     """y = x @ weight.T (bias-free), x [..., K], weight [N, K], all bf16.
 
     Saved for backward: the bf16 input and weight (what the pages' op keeps;
-    nothing quantized is stored)."""
+    nothing quantized is stored), plus, when the forward GEMM is INT8, the
+    column maxima of both (fp32, K values each) that its row-wise passes
+    produce and the backward's column-wise passes need."""
 
     @staticmethod
     def forward(ctx, x: torch.Tensor, weight: torch.Tensor, config: Int8MixedPrecisionConfig,
@@ -86,17 +88,20 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
         lead = x.shape[:-1]
         x2 = _as_rows(x, x.shape[-1])
         w = weight if weight.is_contiguous() else weight.contiguous()
-        if config.output:
+        cx = cw = None
+        if config.output and (config.grad_input or config.grad_weight):
+            y, cx, cw = linear_fwd_colmax(x2, w, config.rounding, seed, offset)
+        elif config.output:
             y = linear_fwd(x2, w, config.rounding, seed, offset)
         else:
             y = torch.mm(x2, w.t())
-        ctx.save_for_backward(x2, w)
+        ctx.save_for_backward(x2, w, cx, cw)
         ctx.config, ctx.seed, ctx.offset, ctx.lead = config, seed, offset, lead
         return y.view(*lead, w.shape[0])
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
-        x2, w = ctx.saved_tensors
+        x2, w, cx, cw = ctx.saved_tensors
         cfg = ctx.config
         need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         dy2 = _as_rows(dy.to(torch.bfloat16), w.shape[0])
@@ -104,7 +109,7 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
         dx = dw = None
         if int_dx or int_dw:
             dx, dw = linear_bwd(dy2, x2, w, cfg.rounding, ctx.seed, ctx.offset,
-                                want_dx=int_dx, want_dw=int_dw)
+                                want_dx=int_dx, want_dw=int_dw, colmax_x=cx, colmax_w=cw)
         if need_dx and not int_dx:
             dx = torch.mm(dy2, w)
         if need_dw and not int_dw:

@@ -110,7 +110,10 @@ def check_gemm(layout, Y, qa, sa, qb, sb, rng, what):
         raise AssertionError(f"{what}: {bad} of {len(ms)} sampled bf16 outputs differ")
 
 
-def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")):
+def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad"), colmax=False):
+    """All quantized operands in full and the GEMM outputs on samples.  With
+    colmax, the forward also returns X's and W's column maxima (checked in
+    full) and the backward takes them."""
     t = linear_inputs(shape, seed=0, device="cuda")
     X, W, dY = t["X"], t["W"], t["dY"]
     Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
@@ -122,11 +125,21 @@ def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")
         ow = oracle_rowwise(Wb, rounding, seed, po(1))
         check_quant(i8.quantize_rowwise(X, rounding, seed, po(0)), ox, name + " X row")
         check_quant(i8.quantize_rowwise(W, rounding, seed, po(1)), ow, name + " W row")
-        Y = i8.linear_fwd(X, W, rounding, seed, offset)
+        cx = cw = None
+        if colmax:
+            Y, cx, cw = i8.linear_fwd_colmax(X, W, rounding, seed, offset)
+            for got, src, what in ((cx, Xb, " colmax X"), (cw, Wb, " colmax W")):
+                assert np.array_equal(got.cpu().numpy().view(np.uint32),
+                                      oracle.col_absmax(src).view(np.uint32)), name + what
+        else:
+            Y = i8.linear_fwd(X, W, rounding, seed, offset)
         check_gemm("NT", Y, ox[0], ox[1], ow[0], ow[1], rng, name + " Y")
         del Y, ox, ow
+    else:
+        cx = cw = None
     dX, dW = i8.linear_bwd(dY, X, W, rounding, seed, offset,
-                           want_dx="dgrad" in gemms, want_dw="wgrad" in gemms)
+                           want_dx="dgrad" in gemms, want_dw="wgrad" in gemms,
+                           colmax_x=cx, colmax_w=cw)
     if "dgrad" in gemms:
         ody = oracle_rowwise(dYb, rounding, seed, po(2))
         owc = oracle_colwise(Wb, rounding, seed, po(3))
@@ -147,6 +160,21 @@ def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")
 def test_square_4096_step(rounding):
     """The benchmarked workload: one linear step at M = N = K = 4096."""
     run_layer(square(4096), rounding, seed=1234)
+
+
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_square_4096_step_with_column_maxima(rounding):
+    """The benchmarked step through the chains that hand X's and W's column
+    maxima from forward to backward."""
+    run_layer(square(4096), rounding, seed=99, colmax=True)
+
+
+@pytest.mark.parametrize("layer", ["llama1b_down_proj", "llama1b_gate_proj"])
+def test_llama1b_layer_with_column_maxima(layer):
+    """Llama-1B linears at 32768 tokens (5632-wide rows of X, resp. dY) through
+    the column-maxima chains."""
+    shape = next(s for s in llama_1b_layers() if s.name == layer)
+    run_layer(shape, "rne", colmax=True)
 
 
 @pytest.mark.parametrize("layer", [s.name for s in llama_1b_layers()])
