@@ -52,6 +52,16 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [p, i64, i64, i64, p, i64, p, i32, u64, u64]
         f.restype = None
+    lib.oracle_e4m3_to_float.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_float.restype = ctypes.c_float
+    lib.oracle_float_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_e4m3.restype = ctypes.c_uint8
+    for name in ("oracle_quantize_rowwise_fp8", "oracle_quantize_colwise_fp8"):
+        f = getattr(lib, name)
+        f.argtypes = [p, i64, i64, i64, p, i64, p]
+        f.restype = None
+    lib.oracle_fp8_scaled_mm.argtypes = [i32, i64, i64, i64, p, i64, p, p, i64, p, p, i64, p, p]
+    lib.oracle_fp8_scaled_mm.restype = None
     lib.oracle_col_absmax.argtypes = [p, i64, i64, i64, p]
     lib.oracle_col_absmax.restype = None
     lib.oracle_quantize_given_u.argtypes = [p, i64, ctypes.c_float, i32, p, p]
@@ -242,3 +252,53 @@ def linear_bwd(dY, X, W, rounding=RNE, seed=0, offset=0, want_dx=True, want_dw=T
     if bad:
         raise OverflowError("int32 overflow or allocation failure")
     return dX, dW
+
+
+# --------------------------------------------------------------------------- FP8 (E4M3)
+
+
+def e4m3_to_float(codes) -> np.ndarray:
+    """float32 values of E4M3 codes (uint8); 0x7F / 0xFF are NaN."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e4m3_to_float(int(v)) for v in c.ravel()], dtype=np.float32).reshape(c.shape)
+
+
+def float_to_e4m3(values) -> np.ndarray:
+    """Nearest E4M3 codes (ties to even, saturating at +-448) of float32 values."""
+    lib = _load()
+    v = np.asarray(values, dtype=np.float32)
+    return np.array([lib.oracle_float_to_e4m3(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def _quantize_fp8(fn, x, axis_len):
+    assert x.dtype == np.uint16
+    rows, cols, ldx = _rows_ld(x)
+    q = np.zeros((rows, cols), dtype=np.uint8)
+    s = np.zeros(axis_len(rows, cols), dtype=np.float32)
+    fn(_ptr(x), rows, cols, ldx, _ptr(q), cols, _ptr(s))
+    return q, s
+
+
+def quantize_rowwise_fp8(x: np.ndarray):
+    """Row-wise FP8 quantization of bf16 bits ``x`` -> (E4M3 codes uint8, fp32 scale[rows])."""
+    return _quantize_fp8(_load().oracle_quantize_rowwise_fp8, x, lambda r, c: r)
+
+
+def quantize_colwise_fp8(x: np.ndarray):
+    """Column-wise FP8 quantization -> (E4M3 codes in x's layout, fp32 scale[cols])."""
+    return _quantize_fp8(_load().oracle_quantize_colwise_fp8, x, lambda r, c: c)
+
+
+def fp8_scaled_mm(layout: int, A, sa, B, sb, want_acc=False):
+    """bf16 bits of the FP8 scaled matmul (exact dot products rounded once to
+    fp32, then the epilogue); with want_acc also (acc fp32, sum|a*b| fp64)."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, N, K = _mnk(layout, A, B)
+    C = np.zeros((M, N), dtype=np.uint16)
+    acc = np.zeros((M, N), dtype=np.float32) if want_acc else None
+    absdot = np.zeros((M, N), dtype=np.float64) if want_acc else None
+    _load().oracle_fp8_scaled_mm(layout, M, N, K, _ptr(A), A.shape[1], _ptr(_c(sa, np.float32)), _ptr(B),
+                                 B.shape[1], _ptr(_c(sb, np.float32)), _ptr(C), N, _ptr(acc), _ptr(absdot))
+    return (C, acc, absdot) if want_acc else C

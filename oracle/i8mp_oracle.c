@@ -360,3 +360,126 @@ int64_t oracle_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t*
   }
   return bad;
 }
+
+/* ---- row-wise FP8 (E4M3) variant -----------------------------------------
+ *
+ * The pages name FP8 training with row-wise scales beside INT8 ([FP8]
+ * "Can FP8 GEMM be enabled via module hooks instead of module swapping?",
+ * the maintainer's reply: float8 primitives with row-wise scales feeding
+ * scaled matmuls; [QT] "Speed benchmarks > Matmul" times a Triton FP8
+ * matmul in the same three layouts).  They fix no formula; the readings
+ * here mirror the INT8 ones: OCP FP8 E4M3, the same absmax statistic with
+ * divisor 448 (the largest finite E4M3 value), the IEEE quotient clamped to
+ * [-448, 448] and rounded to the nearest E4M3 value with ties to the even
+ * code, fp32 accumulation, and the INT8 epilogue.
+ *
+ * E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3 fraction
+ * bits, no infinities, S.1111.111 is NaN.  Exponent field e > 0:
+ * (1 + f/8) * 2^(e-7); e = 0: f * 2^-9.  The largest finite value is
+ * 1.75 * 2^8 = 448.  Every finite value is an integer multiple of 2^-9. */
+
+/* The value of a finite code as an integer count of 2^-9 (exact). */
+static int64_t e4m3_units(uint8_t c) {
+  const int e = (c >> 3) & 15, f = c & 7;
+  const int64_t mag = e == 0 ? f : (int64_t)(8 + f) << (e - 1);
+  return (c & 0x80) ? -mag : mag;
+}
+
+float oracle_e4m3_to_float(uint8_t c) {
+  if ((c & 0x7F) == 0x7F) return NAN;
+  const float mag = ldexpf((float)e4m3_units(c & 0x7F), -9);
+  return (c & 0x80) ? -mag : mag; /* 0x80 is -0 */
+}
+
+/* Nearest E4M3 value to a finite v, ties to the even code, |v| >= 448
+ * saturating to +-448; the sign of v (also of a zero result) is kept.  By
+ * enumeration: each of the 127 non-negative finite codes is a candidate. */
+uint8_t oracle_float_to_e4m3(float v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs((double)v);
+  if (a >= 448.0) return sign | 0x7E;
+  int best = 0;
+  double best_d = a;  /* distance to code 0 */
+  for (int c = 1; c < 127; ++c) {
+    const double d = fabs(ldexp((double)e4m3_units((uint8_t)c), -9) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return sign | (uint8_t)best;
+}
+
+static float fp8_scale_from_amax(float amax) { return amax / 448.0f; }
+
+/* Code of x under scale s: 0 for an all-zero group or a zero x; else the
+ * IEEE quotient, clamped, rounded to E4M3. */
+static uint8_t fp8_quantize_one(float x, float s) {
+  if (s == 0.0f || x == 0.0f) return 0;
+  float v = x / s;
+  if (v > 448.0f) v = 448.0f;
+  if (v < -448.0f) v = -448.0f;
+  return oracle_float_to_e4m3(v);
+}
+
+void oracle_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* scale) {
+  for (int64_t r = 0; r < rows; ++r) {
+    float amax = 0.0f;
+    for (int64_t c = 0; c < cols; ++c) {
+      float a = fabsf(bf16_to_float(x[r * ldx + c]));
+      if (a > amax) amax = a;
+    }
+    const float s = fp8_scale_from_amax(amax);
+    scale[r] = s;
+    for (int64_t c = 0; c < cols; ++c) q[r * ldq + c] = fp8_quantize_one(bf16_to_float(x[r * ldx + c]), s);
+  }
+}
+
+void oracle_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* scale) {
+  for (int64_t c = 0; c < cols; ++c) {
+    float amax = 0.0f;
+    for (int64_t r = 0; r < rows; ++r) {
+      float a = fabsf(bf16_to_float(x[r * ldx + c]));
+      if (a > amax) amax = a;
+    }
+    scale[c] = fp8_scale_from_amax(amax);
+  }
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) q[r * ldq + c] = fp8_quantize_one(bf16_to_float(x[r * ldx + c]), scale[c]);
+}
+
+static int64_t f8a_at(int layout, const uint8_t* A, int64_t lda, int64_t m, int64_t k) {
+  return e4m3_units(layout == OR_TN ? A[k * lda + m] : A[m * lda + k]);
+}
+static int64_t f8b_at(int layout, const uint8_t* B, int64_t ldb, int64_t k, int64_t n) {
+  return e4m3_units(layout == OR_NT ? B[n * ldb + k] : B[k * ldb + n]);
+}
+
+/* FP8 scaled matmul, same layouts as oracle_scaled_mm.  The dot product is
+ * exact: each code is an integer count of 2^-9, so the sum is an integer
+ * count of 2^-18 (|a*b| < 2^36 of those units, so any K < 2^27 fits int64).
+ * It is then rounded once to binary32 (acc_out, if non-NULL), and the INT8
+ * epilogue follows.  absdot_out (if non-NULL) gets sum_k |a_k * b_k| in
+ * binary64 for error bounds of fp32 accumulation. */
+void oracle_fp8_scaled_mm(int layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                          int64_t lda, const float* sa, const uint8_t* B, int64_t ldb,
+                          const float* sb, uint16_t* C, int64_t ldc, float* acc_out,
+                          double* absdot_out) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t sum = 0, abs_sum = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t p = f8a_at(layout, A, lda, m, k) * f8b_at(layout, B, ldb, k, n);
+        sum += p;
+        abs_sum += p < 0 ? -p : p;
+      }
+      const float acc = ldexpf((float)sum, -18); /* int64 -> float rounds to nearest even */
+      if (acc_out) acc_out[m * N + n] = acc;
+      if (absdot_out) absdot_out[m * N + n] = ldexp((double)abs_sum, -18);
+      float y = acc * sa[m];
+      y = y * sb[n];
+      C[m * ldc + n] = float_to_bf16_rne(y);
+    }
+}
