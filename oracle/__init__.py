@@ -62,6 +62,8 @@ def _load():
         f.restype = None
     lib.oracle_fp8_scaled_mm.argtypes = [i32, i64, i64, i64, p, i64, p, p, i64, p, p, i64, p, p]
     lib.oracle_fp8_scaled_mm.restype = None
+    lib.oracle_fp8_scaled_mm_at.argtypes = [i32, i64, p, i64, p, p, i64, p, p, p, i64, p, p, p]
+    lib.oracle_fp8_scaled_mm_at.restype = None
     lib.oracle_col_absmax.argtypes = [p, i64, i64, i64, p]
     lib.oracle_col_absmax.restype = None
     lib.oracle_quantize_given_u.argtypes = [p, i64, ctypes.c_float, i32, p, p]
@@ -302,3 +304,21 @@ def fp8_scaled_mm(layout: int, A, sa, B, sb, want_acc=False):
     _load().oracle_fp8_scaled_mm(layout, M, N, K, _ptr(A), A.shape[1], _ptr(_c(sa, np.float32)), _ptr(B),
                                  B.shape[1], _ptr(_c(sb, np.float32)), _ptr(C), N, _ptr(acc), _ptr(absdot))
     return (C, acc, absdot) if want_acc else C
+
+
+def fp8_scaled_mm_at(layout: int, A, sa, B, sb, ms, ns):
+    """FP8 scaled matmul at output positions (ms[i], ns[i]) ->
+    (bf16 bits, fp32 accumulators, sum |a*b| in fp64)."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, N, K = _mnk(layout, A, B)
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    assert ((ms >= 0) & (ms < M)).all() and ((ns >= 0) & (ns < N)).all()
+    y = np.zeros(len(ms), dtype=np.uint16)
+    acc = np.zeros(len(ms), dtype=np.float32)
+    absdot = np.zeros(len(ms), dtype=np.float64)
+    _load().oracle_fp8_scaled_mm_at(layout, K, _ptr(A), A.shape[1], _ptr(_c(sa, np.float32)), _ptr(B),
+                                    B.shape[1], _ptr(_c(sb, np.float32)), _ptr(ms), _ptr(ns), len(ms),
+                                    _ptr(y), _ptr(acc), _ptr(absdot))
+    return y, acc, absdot

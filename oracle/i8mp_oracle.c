@@ -392,21 +392,25 @@ float oracle_e4m3_to_float(uint8_t c) {
 }
 
 /* Nearest E4M3 value to a finite v, ties to the even code, |v| >= 448
- * saturating to +-448; the sign of v (also of a zero result) is kept.  By
- * enumeration: each of the 127 non-negative finite codes is a candidate. */
+ * saturating to +-448; the sign of v (also of a zero result) is kept.  The
+ * non-negative finite codes 0..126 have increasing values, so a binary search
+ * finds the largest code whose value does not exceed |v|; the answer is that
+ * code or the next one, whichever value is nearer (the even code on a tie). */
 uint8_t oracle_float_to_e4m3(float v) {
   const uint8_t sign = signbit(v) ? 0x80 : 0x00;
   const double a = fabs((double)v);
   if (a >= 448.0) return sign | 0x7E;
-  int best = 0;
-  double best_d = a;  /* distance to code 0 */
-  for (int c = 1; c < 127; ++c) {
-    const double d = fabs(ldexp((double)e4m3_units((uint8_t)c), -9) - a);
-    if (d < best_d || (d == best_d && (c & 1) == 0)) {
-      best = c;
-      best_d = d;
-    }
+  int lo = 0, hi = 126; /* value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (ldexp((double)e4m3_units((uint8_t)mid), -9) <= a)
+      lo = mid;
+    else
+      hi = mid;
   }
+  const double dlo = a - ldexp((double)e4m3_units((uint8_t)lo), -9);
+  const double dhi = ldexp((double)e4m3_units((uint8_t)hi), -9) - a;
+  const int best = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1) == 0 ? lo : hi);
   return sign | (uint8_t)best;
 }
 
@@ -482,4 +486,27 @@ void oracle_fp8_scaled_mm(int layout, int64_t M, int64_t N, int64_t K, const uin
       y = y * sb[n];
       C[m * ldc + n] = float_to_bf16_rne(y);
     }
+}
+
+/* The same at a list of (m, n) output positions (for outputs too large to
+ * compute whole): bf16 result, fp32 accumulator and sum |a*b| per position. */
+void oracle_fp8_scaled_mm_at(int layout, int64_t K, const uint8_t* A, int64_t lda, const float* sa,
+                             const uint8_t* B, int64_t ldb, const float* sb, const int64_t* ms,
+                             const int64_t* ns, int64_t count, uint16_t* y_out, float* acc_out,
+                             double* absdot_out) {
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t m = ms[i], n = ns[i];
+    int64_t sum = 0, abs_sum = 0;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t p = f8a_at(layout, A, lda, m, k) * f8b_at(layout, B, ldb, k, n);
+      sum += p;
+      abs_sum += p < 0 ? -p : p;
+    }
+    const float acc = ldexpf((float)sum, -18);
+    acc_out[i] = acc;
+    absdot_out[i] = ldexp((double)abs_sum, -18);
+    float y = acc * sa[m];
+    y = y * sb[n];
+    y_out[i] = float_to_bf16_rne(y);
+  }
 }

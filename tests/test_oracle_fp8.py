@@ -123,3 +123,16 @@ def test_fp8_scaled_mm_against_float64_matmul(layout, M, N, K):
     yf = (acc * sa[:, None]).astype(np.float32) * sb[None, :]
     want = torch.from_numpy(yf.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(y, want)
+
+
+def test_sampled_positions_match_full_matmul():
+    rng = np.random.default_rng(11)
+    A = rng.integers(0, 0x7E, (50, 96), dtype=np.uint8) | (rng.integers(0, 2, (50, 96), dtype=np.uint8) << 7)
+    B = rng.integers(0, 0x7E, (40, 96), dtype=np.uint8)
+    sa = rng.uniform(0.1, 1, 50).astype(np.float32)
+    sb = rng.uniform(0.1, 1, 40).astype(np.float32)
+    y, acc, absdot = oracle.fp8_scaled_mm(oracle.NT, A, sa, B, sb, want_acc=True)
+    ms, ns = rng.integers(0, 50, 300), rng.integers(0, 40, 300)
+    y2, acc2, absdot2 = oracle.fp8_scaled_mm_at(oracle.NT, A, sa, B, sb, ms, ns)
+    assert np.array_equal(y2, y[ms, ns]) and np.array_equal(acc2, acc[ms, ns])
+    assert np.array_equal(absdot2, absdot[ms, ns])
