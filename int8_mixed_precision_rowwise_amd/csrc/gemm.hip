@@ -38,6 +38,8 @@ namespace {
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int BK = 64;
@@ -259,6 +261,58 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int64_t m0
   }
 }
 
+// bf16 output from fp32 accumulators of 32 x 32 blocks (FP8 GEMM), without
+// the LDS stage (C not 16-byte aligned, or ldc not a multiple of 8): same
+// index map as store_tile, 4 adjacent outputs per group of registers.
+template <int BM, int TM, int TN>
+__device__ __forceinline__ void store32f_direct(const v16f (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                                int wm, int wn, int64_t M, int64_t N,
+                                                const float* s_lds, __bf16* __restrict__ C,
+                                                int64_t ldc, int lane) {
+  const int mr = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm + 32 * i + mr;
+    if (m >= M) continue;
+    const float sam = s_lds[wm + 32 * i + mr];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cn = wn + 32 * j + 8 * q + nq + e;
+          if (n0 + cn >= N) continue;
+          float y = acc[i][j][4 * q + e];
+          y = y * sam;
+          y = y * s_lds[BM + cn];
+          C[m * ldc + n0 + cn] = (__bf16)y;  // round to nearest even
+        }
+  }
+}
+
+// The fp32 sums of 32 x 32 blocks themselves (FP8 GEMM without epilogue).
+template <int TM, int TN>
+__device__ __forceinline__ void store32f_raw(const v16f (&acc)[TM][TN], int64_t m0, int64_t n0,
+                                             int wm, int wn, int64_t M, int64_t N,
+                                             float* __restrict__ C, int64_t ldc, int lane) {
+  const int mr = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm + 32 * i + mr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t n = n0 + wn + 32 * j + 8 * q + nq + e;
+          if (n < N) C[m * ldc + n] = acc[i][j][4 * q + e];
+        }
+  }
+}
+
 // bf16 epilogue through LDS: each wave scales its WM x WN accumulators,
 // writes them as bf16 into its own LDS region (rows of WN * 2 bytes, 16-byte
 // chunk c of row r at chunk c ^ (r mod chunks-per-row)), then reads whole
@@ -266,8 +320,8 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int64_t m0
 // writes complete rows instead of scattered 8-byte pieces.  Needs C 16-byte
 // aligned and ldc a multiple of 8; `stage` holds at least 4 * WM * WN * 2
 // bytes and no wave reads the slab buffers any more.
-template <int BM, int TM, int TN>
-__device__ __forceinline__ void store_tile_staged(const v16i (&acc)[TM][TN], int64_t m0, int64_t n0,
+template <int BM, int TM, int TN, typename AccV>
+__device__ __forceinline__ void store_tile_staged(const AccV (&acc)[TM][TN], int64_t m0, int64_t n0,
                                                   int wm, int wn, int64_t M, int64_t N,
                                                   const float* s_lds, int8_t* stage,
                                                   __bf16* __restrict__ C, int64_t ldc, int lane,
@@ -656,30 +710,105 @@ __device__ __forceinline__ void store16_staged(const v4i (&acc)[TM][TN], int64_t
   }
 }
 
-// Main-loop schedule of one slab (TM x TN MFMAs of 16 x 16 x 64, A-block
-// major: MFMA m works on A block m / TN and B block m % TN).  The first
-// IA * TN MFMAs run before the workgroup barrier; after it, each MFMA is
-// followed by at most one fragment read of the next slab and at most one
-// slab load.  Fragment reads go A blocks 0 .. IA-1 (free since the barrier),
-// then the TN B blocks (into the other B register set), then A blocks
-// IA .. TM-1, each no earlier than the MFMA that last reads it.
+// Main-loop schedule of one slab (TM x TN MFMAs, A-block major: MFMA m works
+// on A block m / TN and B block m % TN).  The first IA * TN MFMAs run before
+// the workgroup barrier; after it, each MFMA is followed by at most one
+// fragment read of the next slab and at most one slab load.  Fragment reads
+// go A blocks 0 .. IA-1 (free since the barrier), then the TN B blocks (into
+// the other B register set), then A blocks IA .. TM-1, each no earlier than
+// the MFMA that last reads it.  Small tiles run out of MFMAs: whatever is left
+// is issued after the last one.
 template <int TM, int TN, int PER>
 struct SlabSchedule {
   static constexpr int IA = 1;
   static constexpr int HA = IA * TN;        // MFMAs before the barrier
   static constexpr int NM = TM * TN;
   static constexpr int DMA_STEP = (NM - HA) / PER > 0 ? (NM - HA) / PER : 1;
+  static constexpr int last(int m) { return m < NM - 1 ? m : NM - 1; }
   static constexpr int a_read(int i) {  // MFMA index after which A block i is read
-    return i < IA ? HA + i : (HA + TN + i > TN * (i + 1) - 1 ? HA + TN + i : TN * (i + 1) - 1);
+    return last(i < IA ? HA + i : (HA + TN + i > TN * (i + 1) - 1 ? HA + TN + i : TN * (i + 1) - 1));
   }
-  static constexpr int b_read(int j) { return HA + IA + j; }
-  static constexpr int dma_at(int d) { return HA + 1 + DMA_STEP * d; }
+  static constexpr int b_read(int j) { return last(HA + IA + j); }
+  static constexpr int dma_at(int d) { return last(HA + 1 + DMA_STEP * d); }
   static_assert(TM > IA, "need A blocks after the barrier");
-  static_assert(3 * TN + TM <= TM * TN, "reads of the next slab fit in the slab's MFMAs");
-  static_assert(HA + 1 + DMA_STEP * (PER - 1) <= NM - 1, "slab loads fit in the slab's MFMAs");
 };
 
-template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC>
+// The two MFMA forms.  FMT 0: INT8, v_mfma_i32_16x16x64_i8 on 16 x 16 blocks
+// (fragments of 16 bytes per lane, frag16).  FMT 1: FP8 E4M3,
+// v_mfma_f32_32x32x64_f8f6f4 on 32 x 32 blocks: lane l supplies row l % 32 of
+// its first operand block and column l % 32 of its second with 32
+// contraction values (k = 32 (l / 32) + 0..31 of the slab), products summed
+// in fp32; the result layout is that of the 32 x 32 blocks described at the
+// top (register v of lane l: row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32).
+// The FP8 form takes the whole 64-deep slab in one instruction, like the INT8
+// one, so the pipeline is shared.
+
+// FP8 operand (32 contraction bytes) for 32-row block blk0, whole slab.
+template <int R, bool KMAJOR>
+__device__ __forceinline__ v8i frag32f8(const int8_t* lds, int blk0, int lane) {
+  v8i out;
+  if constexpr (KMAJOR) {
+    const int r = blk0 + (lane & 31);
+    const int c = 2 * (lane >> 5);
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + kmajor_off(r, c));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + kmajor_off(r, c + 1));
+    out[0] = lo.x, out[1] = lo.y, out[2] = lo.z, out[3] = lo.w;
+    out[4] = hi.x, out[5] = hi.y, out[6] = hi.z, out[7] = hi.w;
+  } else {
+    const int g = lane >> 4, li = lane & 15;
+    const int c = (blk0 + 16 * (g & 1)) >> 4;  // 16 output columns of this lane group
+    const int krow = 32 * (g >> 1) + (li >> 1);
+    const int half = (li & 1) << 3;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i*)(lds + mnmajor_off<R>(krow + 8 * t, c) + half));
+      out[2 * t] = w.x, out[2 * t + 1] = w.y;
+    }
+  }
+  return out;
+}
+
+template <int FMT>
+struct Mma;
+
+template <>
+struct Mma<0> {
+  static constexpr int BLK = 16;
+  typedef v4i Frag;
+  typedef v4i Acc;
+  template <int R, bool KMAJOR>
+  static __device__ __forceinline__ Frag frag(const int8_t* lds, int blk0, int lane) {
+    return frag16<R, KMAJOR>(lds, blk0, lane);
+  }
+  static __device__ __forceinline__ Acc mma(const Frag& b, const Frag& a, const Acc& c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ Acc zero() { return (v4i){0, 0, 0, 0}; }
+};
+
+template <>
+struct Mma<1> {
+  static constexpr int BLK = 32;
+  typedef v8i Frag;
+  typedef v16f Acc;
+  template <int R, bool KMAJOR>
+  static __device__ __forceinline__ Frag frag(const int8_t* lds, int blk0, int lane) {
+    return frag32f8<R, KMAJOR>(lds, blk0, lane);
+  }
+  static __device__ __forceinline__ Acc mma(const Frag& b, const Frag& a, const Acc& c) {
+    // operand formats 0, 0: FP8 E4M3 for both; no block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
+  }
+  static __device__ __forceinline__ Acc zero() {
+    v16f z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+    return z;
+  }
+};
+
+template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC, int FMT = 0>
 __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
                                                               const int8_t* __restrict__ A, int64_t lda,
                                                               const float* __restrict__ sa,
@@ -688,7 +817,10 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
                                                               void* __restrict__ Cv, int64_t ldc) {
   constexpr int NW = 2 * WGN, NT = 64 * NW;  // 2 x WGN waves
   constexpr int WM = BM / 2, WN = BN / WGN;
-  constexpr int TM = WM / 16, TN = WN / 16;
+  typedef Mma<FMT> T;
+  typedef typename T::Frag Frag;
+  typedef typename T::Acc Acc;
+  constexpr int TM = WM / T::BLK, TN = WN / T::BLK;
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SLAB = A_BYTES + B_BYTES;
   constexpr int NA = Dma<BM, A_KMAJOR, NW>::kInst;
   constexpr int PER = NA + Dma<BN, B_KMAJOR, NW>::kInst;  // loads per wave per slab
@@ -725,14 +857,14 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   da.init(A, lda, m0, M, K, wave, lane);
   db.init(B, ldb, n0, N, K, wave, lane);
 
-  v4i acc[TM][TN];
+  Acc acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+    for (int j = 0; j < TN; ++j) acc[i][j] = T::zero();
 
   const int nk = (int)((K + BK - 1) / BK);
-  v4i a[TM], b0[TN], b1[TN];
+  Frag a[TM], b0[TN], b1[TN];
   // Slabs 0 .. STAGES-1 go out first.  Slabs past the end are still
   // "loaded", with out-of-range offsets (the buffer unit writes zeros into a
   // buffer nobody reads), so every slab costs the same PER loads per wave and
@@ -745,9 +877,9 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 1) * PER));  // slab 0 has landed
   lds_barrier();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) a[i] = frag16<BM, A_KMAJOR>(lds, wm0 + 16 * i, lane);
+  for (int i = 0; i < TM; ++i) a[i] = T::template frag<BM, A_KMAJOR>(lds, wm0 + T::BLK * i, lane);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b0[j] = frag16<BN, B_KMAJOR>(lds + A_BYTES, wn0 + 16 * j, lane);
+  for (int j = 0; j < TN; ++j) b0[j] = T::template frag<BN, B_KMAJOR>(lds + A_BYTES, wn0 + T::BLK * j, lane);
 
   // One slab: MFMAs on the fragments of slab kt (registers a, bc) while the
   // fragments of slab kt + 1 are read into a and bn and slab kt + STAGES is
@@ -756,13 +888,13 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   // kt, whose fragments were read during the previous slab.  A sched_barrier
   // after each step keeps the matrix core fed while the LDS and memory units
   // work.
-  auto slab = [&](v4i (&bc)[TN], v4i (&bn)[TN], int kt) __attribute__((always_inline)) {
+  auto slab = [&](Frag (&bc)[TN], Frag (&bn)[TN], int kt) __attribute__((always_inline)) {
     const int8_t* nxt = lds + ((kt + 1) % STAGES) * SLAB;
     int8_t* dst = lds + (kt % STAGES) * SLAB;
     const int ns = kt + STAGES;
 #pragma unroll
     for (int m = 0; m < S::HA; ++m) {
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bc[m % TN], a[m / TN], acc[m / TN][m % TN], 0, 0, 0);
+      acc[m / TN][m % TN] = T::mma(bc[m % TN], a[m / TN], acc[m / TN][m % TN]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // slab kt+1 has landed once only slabs kt+2 .. kt+STAGES-1 are pending
@@ -770,13 +902,13 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
     lds_barrier();
 #pragma unroll
     for (int m = S::HA; m < S::NM; ++m) {
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bc[m % TN], a[m / TN], acc[m / TN][m % TN], 0, 0, 0);
+      acc[m / TN][m % TN] = T::mma(bc[m % TN], a[m / TN], acc[m / TN][m % TN]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        if (m == S::a_read(i)) a[i] = frag16<BM, A_KMAJOR>(nxt, wm0 + 16 * i, lane);
+        if (m == S::a_read(i)) a[i] = T::template frag<BM, A_KMAJOR>(nxt, wm0 + T::BLK * i, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        if (m == S::b_read(j)) bn[j] = frag16<BN, B_KMAJOR>(nxt + A_BYTES, wn0 + 16 * j, lane);
+        if (m == S::b_read(j)) bn[j] = T::template frag<BN, B_KMAJOR>(nxt + A_BYTES, wn0 + T::BLK * j, lane);
 #pragma unroll
       for (int d = 0; d < PER; ++d)
         if (m == S::dma_at(d)) {
@@ -801,18 +933,25 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
     const bool odd = kt & 1;
 #pragma unroll
     for (int m = 0; m < S::NM; ++m)
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_i32_16x16x64_i8(odd ? b1[m % TN] : b0[m % TN], a[m / TN],
-                                                                 acc[m / TN][m % TN], 0, 0, 0);
+      acc[m / TN][m % TN] = T::mma(odd ? b1[m % TN] : b0[m % TN], a[m / TN], acc[m / TN][m % TN]);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing zero-fill loads and the scales
 #pragma unroll
   for (int r = 0; r < NPRE; ++r)
     if (!OUT_I32 && t + r * NT < BM + BN) s_lds[t + r * NT] = s_pre[r];
   __syncthreads();
-  if constexpr (!OUT_I32 && VEC)
+  if constexpr (FMT == 1) {
+    if constexpr (OUT_I32)  // the raw fp32 sums (C holds floats)
+      store32f_raw<TM, TN>(acc, m0, n0, wm0, wn0, M, N, static_cast<float*>(Cv), ldc, lane);
+    else if constexpr (VEC)
+      store_tile_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
+    else
+      store32f_direct<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, static_cast<__bf16*>(Cv), ldc, lane);
+  } else if constexpr (!OUT_I32 && VEC) {
     store16_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
-  else
+  } else {
     store16_direct<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
+  }
 }
 
 
@@ -841,7 +980,11 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
   const int64_t lim = int64_t(1) << 31;
   const int64_t a_ext = AK ? (int64_t)BM * lda : K * lda;
   const int64_t b_ext = BKM ? (int64_t)BN * ldb : K * ldb;
-  const bool fast = K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024;
+  // An operand whose contraction runs down its rows is range-checked at its
+  // last byte, and the buffer unit checks whole dwords: its output extent must
+  // be a multiple of 4 or the last row's final dword would read as zero.
+  const bool mn_ok = (AK || M % 4 == 0) && (BKM || N % 4 == 0);
+  const bool fast = K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024 && mn_ok;
   // packed stores of adjacent outputs need 16-byte aligned rows
   const uintptr_t c = Ci ? reinterpret_cast<uintptr_t>(Ci) : reinterpret_cast<uintptr_t>(Cb);
   const bool vec = Ci ? (ldc % 4 == 0 && c % 16 == 0) : (ldc % 8 == 0 && c % 16 == 0);
@@ -865,6 +1008,52 @@ hipError_t pick(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, c
   return run<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, stream);
 }
 
+template <int BM, int BN, bool AK, bool BKM>
+hipError_t run_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sa,
+                   const uint8_t* B, int64_t ldb, const float* sb, uint16_t* C, float* Cf,
+                   int64_t ldc, hipStream_t stream) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const dim3 grid((unsigned)tiles);
+  constexpr int WGN = BM >= 256 ? 4 : 2;
+  const bool vec = ldc % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
+  const int8_t* a = reinterpret_cast<const int8_t*>(A);
+  const int8_t* b = reinterpret_cast<const int8_t*>(B);
+  if (Cf)
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, true, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc);
+  else if (vec)
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc);
+  else
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc);
+  return hipGetLastError();
+}
+
+template <bool AK, bool BKM>
+hipError_t pick_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sa,
+                    const uint8_t* B, int64_t ldb, const float* sb, uint16_t* C, float* Cf,
+                    int64_t ldc, hipStream_t stream) {
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 200) return run_fp8<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
+  return run_fp8<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp8(int layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                           int64_t lda, const float* sa, const uint8_t* B, int64_t ldb,
+                           const float* sb, uint16_t* C, float* C_f32, int64_t ldc,
+                           hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  switch (layout) {
+    case 0:
+      return pick_fp8<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, stream);
+    case 1:
+      return pick_fp8<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, stream);
+    default:
+      return pick_fp8<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, stream);
+  }
+}
+
+namespace {
 }  // namespace
 
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,

@@ -130,8 +130,12 @@ def make_operands(layout, M, N, K, seed, pad=True):
     return A, B, sa, sb, Ag, Bg
 
 
+# the contraction a multiple of 16 with ragged output extents, down to one
+# row or column, takes the pipelined kernel (or, for extents that are not a
+# multiple of 4 along an operand read down its rows, the general one)
 GEMM_SHAPES = [(1, 1, 1), (17, 33, 65), (255, 130, 513), (256, 512, 512), (300, 257, 1000),
-               (513, 255, 17), (129, 1025, 200), (40, 24, 4100)]
+               (513, 255, 17), (129, 1025, 200), (40, 24, 4100), (1, 1, 16), (17, 33, 64),
+               (5, 130, 48), (37, 36, 80), (300, 260, 1008)]
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
