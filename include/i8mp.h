@@ -225,6 +225,58 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
                                    const i8mp_linear_opts* opts, const float* colmax_x,
                                    const float* colmax_w, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Row-wise FP8 variant.  The pages name FP8 training with row-wise scales
+ * beside INT8 ("Can FP8 GEMM be enabled via module hooks instead of module
+ * swapping?", the maintainer's reply: row-wise scaled float8 matmuls;
+ * "Quantized model training", section "Speed benchmarks > Matmul": FP8
+ * matmuls in the same three layouts).  Codes are OCP FP8 E4M3 bytes (1 sign,
+ * 4 exponent bits with bias 7, 3 fraction bits, largest finite 448):
+ *   scale = RN32(amax / 448), code = E4M3_RNE(clamp(RN32(x / scale), -448, 448))
+ * with ties to the even code, a zero x coded +0 and an all-zero group scale 0
+ * and codes 0.  Round to nearest only (no stochastic rounding).  Layouts and
+ * leading dimensions as for the INT8 entry points.
+ */
+i8mp_status i8mp_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* scale, void* stream);
+/* ws: at least i8mp_quantize_colwise_workspace_bytes(rows, cols) bytes, 256-aligned. */
+i8mp_status i8mp_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* scale, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/*
+ * FP8 scaled matmul: acc[m,n] = sum_k A(m,k) * B(k,n) over E4M3 values in
+ * fp32 (the matrix core's summation: each product is exact, the sums are
+ * rounded), then C = bf16_RNE(RN32(RN32(acc) * scale_a[m]) * scale_b[n]).
+ * Same layouts and scale indexing as i8mp_int8_scaled_mm.  K must be a
+ * multiple of 16; the output extents along operands whose contraction runs
+ * down their rows (M in TN, N in NN and TN) multiples of 4; and the bytes
+ * spanned by 256 rows of a K-contiguous operand (K rows of the others) below
+ * 2^31 (I8MP_EINVAL otherwise).
+ */
+i8mp_status i8mp_fp8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                               int64_t lda, const float* scale_a, const uint8_t* B, int64_t ldb,
+                               const float* scale_b, uint16_t* C, int64_t ldc, void* stream);
+
+/* The fp32 sums alone, C = float [M x N] (same layouts and kernel without the
+ * scale epilogue).  For characterizing the matrix core's FP8 summation. */
+i8mp_status i8mp_fp8_mm_f32(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                            int64_t lda, const uint8_t* B, int64_t ldb, float* C, int64_t ldc,
+                            void* stream);
+
+/*
+ * The linear layer's forward and backward with FP8 codes in place of INT8
+ * (same passes, layouts and outputs as i8mp_linear_fwd / i8mp_linear_bwd;
+ * workspace sizes from i8mp_linear_workspace_bytes).  Each GEMM must meet
+ * i8mp_fp8_scaled_mm's shape rules: K a multiple of 16 (forward); for dX, N a
+ * multiple of 16 and K of 4; for dW, M a multiple of 16 and N, K of 4.
+ */
+i8mp_status i8mp_linear_fwd_fp8(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream);
+i8mp_status i8mp_linear_bwd_fp8(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

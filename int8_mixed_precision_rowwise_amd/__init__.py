@@ -23,7 +23,9 @@ __all__ = [
     "quantize_rowwise", "quantize_colwise", "int8_scaled_mm", "int8_mm_i32",
     "philox4x32_10", "linear_fwd", "linear_bwd", "linear_workspace_bytes",
     "colwise_workspace_bytes", "quantize_rowwise_colmax", "quantize_colwise_given_colmax",
-    "rowwise_colmax_workspace_bytes", "linear_fwd_colmax", "EXPORTED_SYMBOLS",
+    "rowwise_colmax_workspace_bytes", "linear_fwd_colmax", "quantize_rowwise_fp8",
+    "quantize_colwise_fp8", "fp8_scaled_mm", "fp8_mm_f32", "linear_fwd_fp8", "linear_bwd_fp8",
+    "EXPORTED_SYMBOLS",
 ]
 
 RNE, SR = 0, 1
@@ -38,7 +40,8 @@ EXPORTED_SYMBOLS = (
     "i8mp_int8_mm_i32", "i8mp_philox4x32_10", "i8mp_linear_workspace_bytes", "i8mp_linear_fwd",
     "i8mp_linear_bwd", "i8mp_quantize_rowwise_colmax_workspace_bytes",
     "i8mp_quantize_rowwise_colmax", "i8mp_quantize_colwise_given_colmax", "i8mp_linear_fwd_colmax",
-    "i8mp_linear_bwd_colmax",
+    "i8mp_linear_bwd_colmax", "i8mp_quantize_rowwise_fp8", "i8mp_quantize_colwise_fp8",
+    "i8mp_fp8_scaled_mm", "i8mp_fp8_mm_f32", "i8mp_linear_fwd_fp8", "i8mp_linear_bwd_fp8",
 )
 
 
@@ -78,6 +81,12 @@ def _load() -> ctypes.CDLL:
         "i8mp_linear_fwd_colmax": ([p, p, p, i64, i64, i64, ctypes.POINTER(_Opts), p, p, p, sz, p], i32),
         "i8mp_linear_bwd_colmax": ([p, p, p, p, p, i64, i64, i64, ctypes.POINTER(_Opts), p, p, p, sz, p],
                                    i32),
+        "i8mp_quantize_rowwise_fp8": ([p, i64, i64, i64, p, i64, p, p], i32),
+        "i8mp_quantize_colwise_fp8": ([p, i64, i64, i64, p, i64, p, p, sz, p], i32),
+        "i8mp_fp8_scaled_mm": ([i32, i64, i64, i64, p, i64, p, p, i64, p, p, i64, p], i32),
+        "i8mp_fp8_mm_f32": ([i32, i64, i64, i64, p, i64, p, i64, p, i64, p], i32),
+        "i8mp_linear_fwd_fp8": ([p, p, p, i64, i64, i64, p, sz, p], i32),
+        "i8mp_linear_bwd_fp8": ([p, p, p, p, p, i64, i64, i64, p, sz, p], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -349,3 +358,104 @@ def linear_bwd(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, rounding="rne
                                         workspace.numel(), _stream(dY.device))
     _check(st, "i8mp_linear_bwd_colmax")
     return (dX if want_dx else None), (dW if want_dw else None)
+
+
+# --------------------------------------------------------------------------- FP8 (E4M3) variant
+
+
+def quantize_rowwise_fp8(x: torch.Tensor, q: torch.Tensor | None = None,
+                         scale: torch.Tensor | None = None):
+    """Row-wise FP8 quantization of bf16 ``x`` [R, C] -> (E4M3 codes as uint8 [R, C],
+    fp32 scale [R]); ``codes.view(torch.float8_e4m3fn)`` gives torch's view of them."""
+    _bits(x)
+    R, C = x.shape
+    q = _empty_2d(R, C, torch.uint8, x.device) if q is None else q
+    scale = torch.empty(R, dtype=torch.float32, device=x.device) if scale is None else scale
+    with torch.cuda.device(x.device):
+        st = lib.i8mp_quantize_rowwise_fp8(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
+                                           _stream(x.device))
+    _check(st, "i8mp_quantize_rowwise_fp8")
+    return q, scale
+
+
+def quantize_colwise_fp8(x: torch.Tensor, q: torch.Tensor | None = None,
+                         scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Column-wise FP8 quantization -> (E4M3 codes uint8 [R, C] in x's layout, fp32 scale [C])."""
+    _bits(x)
+    R, C = x.shape
+    q = _empty_2d(R, C, torch.uint8, x.device) if q is None else q
+    scale = torch.empty(C, dtype=torch.float32, device=x.device) if scale is None else scale
+    need = colwise_workspace_bytes(R, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        st = lib.i8mp_quantize_colwise_fp8(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
+                                           _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check(st, "i8mp_quantize_colwise_fp8")
+    return q, scale
+
+
+def fp8_scaled_mm(layout, A: torch.Tensor, scale_a: torch.Tensor, B: torch.Tensor,
+                  scale_b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 C[M,N] from E4M3 codes (uint8): fp32 sums of the exact products, then
+    bf16((sum * scale_a[m]) * scale_b[n]).  Layouts as for int8_scaled_mm; K % 16 == 0."""
+    layout = _LAYOUTS[layout]
+    _bits(A, torch.uint8), _bits(B, torch.uint8)
+    M, N, K = _mnk(layout, A, B)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if out is None else out
+    with torch.cuda.device(A.device):
+        st = lib.i8mp_fp8_scaled_mm(layout, M, N, K, _ptr(A), _ld(A), _ptr(scale_a), _ptr(B),
+                                    _ld(B), _ptr(scale_b), _ptr(out), _ld(out), _stream(A.device))
+    _check(st, "i8mp_fp8_scaled_mm")
+    return out
+
+
+def fp8_mm_f32(layout, A: torch.Tensor, B: torch.Tensor,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """float32 C[M,N]: the matrix core's fp32 sums of E4M3 products (same layouts
+    as fp8_scaled_mm, no scales)."""
+    layout = _LAYOUTS[layout]
+    _bits(A, torch.uint8), _bits(B, torch.uint8)
+    M, N, K = _mnk(layout, A, B)
+    out = torch.empty((M, N), dtype=torch.float32, device=A.device) if out is None else out
+    with torch.cuda.device(A.device):
+        st = lib.i8mp_fp8_mm_f32(layout, M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(out),
+                                 _ld(out), _stream(A.device))
+    _check(st, "i8mp_fp8_mm_f32")
+    return out
+
+
+def linear_fwd_fp8(X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None):
+    """Y = X @ W.T with both operands quantized row-wise to FP8 (E4M3) over K."""
+    _bits(X), _bits(W)
+    M, K = X.shape
+    N = W.shape[0]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device) if out is None else out
+    need = linear_workspace_bytes(M, N, K, False)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    with torch.cuda.device(X.device):
+        st = lib.i8mp_linear_fwd_fp8(_ptr(X), _ptr(W), _ptr(Y), M, N, K, _ptr(workspace),
+                                     workspace.numel(), _stream(X.device))
+    _check(st, "i8mp_linear_fwd_fp8")
+    return Y
+
+
+def linear_bwd_fp8(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, want_dx: bool = True,
+                   want_dw: bool = True, workspace: torch.Tensor | None = None):
+    """(dX = dY @ W, dW = dY.T @ X) with FP8 (E4M3) operands, each quantized along
+    its own contraction."""
+    _bits(dY), _bits(X), _bits(W)
+    M, N = dY.shape
+    K = W.shape[1]
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device) if want_dx else None
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dY.device) if want_dw else None
+    need = linear_workspace_bytes(M, N, K, True)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dY.device)
+    with torch.cuda.device(dY.device):
+        st = lib.i8mp_linear_bwd_fp8(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX), _ptr(dW), M, N, K,
+                                     _ptr(workspace), workspace.numel(), _stream(dY.device))
+    _check(st, "i8mp_linear_bwd_fp8")
+    return dX, dW

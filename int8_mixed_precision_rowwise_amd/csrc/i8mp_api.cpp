@@ -461,4 +461,156 @@ i8mp_status i8mp_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_
                                 stream);
 }
 
+// ---- FP8 (E4M3) variant -------------------------------------------------
+
+i8mp_status i8mp_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* scale, void* stream) {
+  const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q8, ldq, scale, rows, I8MP_RNE);
+  if (st != I8MP_OK) return st;
+  if (rows == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_rowwise_fp8(x, rows, cols, ldx, q, ldq, scale, as_stream(stream)));
+}
+
+i8mp_status i8mp_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* scale, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q8, ldq, scale, cols, I8MP_RNE);
+  if (st != I8MP_OK) return st;
+  if (cols == 0) return I8MP_OK;
+  const size_t need = i8mp_quantize_colwise_workspace_bytes(rows, cols);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  if (overlap(rw, mat_range(x, rows, cols, ldx, 2)) || overlap(rw, mat_range(q, rows, cols, ldq, 1)) ||
+      overlap(rw, vec_range(scale, cols, 4)))
+    return I8MP_EINVAL;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_colwise_fp8(x, rows, cols, ldx, q, ldq, scale, ws,
+                                                      as_stream(stream)));
+}
+
+// FP8 GEMM shape rules (one kernel, the pipelined one): K a multiple of 16,
+// output extents along operands whose contraction runs down their rows (M
+// for TN, N for NN and TN) multiples of 4.
+bool fp8_shape_ok(int32_t layout, int64_t M, int64_t N, int64_t K) {
+  return K % 16 == 0 && (layout != I8MP_TN || M % 4 == 0) && (layout == I8MP_NT || N % 4 == 0);
+}
+
+i8mp_status i8mp_fp8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                               int64_t lda, const float* scale_a, const uint8_t* B, int64_t ldb,
+                               const float* scale_b, uint16_t* C, int64_t ldc, void* stream) {
+  if (!fp8_shape_ok(layout, M, N, K)) return I8MP_EINVAL;
+  // the extents a tile's buffer offsets reach must stay below 2^31
+  const int64_t lim = (int64_t(1) << 31) - 1024;
+  if ((layout == I8MP_TN ? K * lda : 256 * lda) >= lim || (layout == I8MP_NT ? 256 * ldb : K * ldb) >= lim)
+    return I8MP_EINVAL;
+  i8mp_status st = validate_mm(layout, M, N, K, reinterpret_cast<const int8_t*>(A), lda,
+                               reinterpret_cast<const int8_t*>(B), ldb, C, ldc, 2, scale_a, scale_b,
+                               true);
+  if (st == I8MP_ERANGE) st = I8MP_OK;  // fp32 accumulation: no integer bound
+  if (st != I8MP_OK) return st;
+  if (M == 0 || N == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_gemm_fp8(layout, M, N, K, A, lda, scale_a, B, ldb, scale_b, C, nullptr,
+                                          ldc, as_stream(stream)));
+}
+
+i8mp_status i8mp_fp8_mm_f32(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                            int64_t lda, const uint8_t* B, int64_t ldb, float* C, int64_t ldc,
+                            void* stream) {
+  if (!fp8_shape_ok(layout, M, N, K)) return I8MP_EINVAL;
+  const int64_t lim = (int64_t(1) << 31) - 1024;
+  if ((layout == I8MP_TN ? K * lda : 256 * lda) >= lim || (layout == I8MP_NT ? 256 * ldb : K * ldb) >= lim)
+    return I8MP_EINVAL;
+  i8mp_status st = validate_mm(layout, M, N, K, reinterpret_cast<const int8_t*>(A), lda,
+                               reinterpret_cast<const int8_t*>(B), ldb, C, ldc, 4, nullptr, nullptr,
+                               false);
+  if (st == I8MP_ERANGE) st = I8MP_OK;
+  if (st != I8MP_OK) return st;
+  if (M == 0 || N == 0) return I8MP_OK;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_gemm_fp8(layout, M, N, K, A, lda, nullptr, B, ldb, nullptr, nullptr,
+                                          C, ldc, as_stream(stream)));
+}
+
+i8mp_status i8mp_linear_fwd_fp8(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  if (!dims_ok(M, N, K)) return I8MP_EINVAL;
+  if (K % 16 != 0) return I8MP_EINVAL;
+  if (!chunked_ok(X, M, K, K, 2) || !chunked_ok(W, N, K, K, 2) || !elementwise_ok(Y, M, N, N, 2))
+    return I8MP_EINVAL;
+  const Range ry = mat_range(Y, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
+              rwt = mat_range(W, N, K, K, 2);
+  if (overlap(ry, rx) || overlap(ry, rwt)) return I8MP_EINVAL;
+  if (M == 0 || N == 0) return I8MP_OK;
+  const size_t need = carve_fwd(nullptr, M, N, K, nullptr);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  for (Range o : {ry, rx, rwt})
+    if (overlap(rw, o)) return I8MP_EINVAL;
+  if (256 * pad16(K) >= (int64_t(1) << 31) - 1024) return I8MP_EINVAL;
+  i8mp_status st = device_check();
+  if (st != I8MP_OK) return st;
+  FwdWs w;
+  carve_fwd(ws, M, N, K, &w);
+  const hipStream_t s = as_stream(stream);
+  const int64_t kp = pad16(K);
+  uint8_t* qx = reinterpret_cast<uint8_t*>(w.qx);
+  uint8_t* qw = reinterpret_cast<uint8_t*>(w.qw);
+  hipError_t e = i8mp::launch_quantize_rowwise_fp8(X, M, K, K, qx, kp, w.sx, s);
+  if (e == hipSuccess) e = i8mp::launch_quantize_rowwise_fp8(W, N, K, K, qw, kp, w.sw, s);
+  if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_NT, M, N, K, qx, kp, w.sx, qw, kp, w.sw, Y, nullptr, N, s);
+  return hip_status(e);
+}
+
+i8mp_status i8mp_linear_bwd_fp8(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (!dims_ok(M, N, K)) return I8MP_EINVAL;
+  if ((dX && !fp8_shape_ok(I8MP_NN, M, K, N)) || (dW && !fp8_shape_ok(I8MP_TN, N, K, M))) return I8MP_EINVAL;
+  if (!chunked_ok(dY, M, N, N, 2)) return I8MP_EINVAL;
+  if (dX && (!chunked_ok(W, N, K, K, 2) || !elementwise_ok(dX, M, K, K, 2))) return I8MP_EINVAL;
+  if (dW && (!chunked_ok(X, M, K, K, 2) || !elementwise_ok(dW, N, K, K, 2))) return I8MP_EINVAL;
+  if (dX && dW && dX == dW && M * K > 0 && N * K > 0) return I8MP_EINVAL;
+  const Range rdy = mat_range(dY, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
+              rwt = mat_range(W, N, K, K, 2), rdx = dX ? mat_range(dX, M, K, K, 2) : Range{},
+              rdw = dW ? mat_range(dW, N, K, K, 2) : Range{};
+  for (Range o : {rdx, rdw})
+    if (overlap(o, rdy) || overlap(o, rx) || overlap(o, rwt)) return I8MP_EINVAL;
+  if (overlap(rdx, rdw)) return I8MP_EINVAL;
+  const bool want_dx = dX && M > 0 && K > 0, want_dw = dW && N > 0 && K > 0;
+  if (!want_dx && !want_dw) return I8MP_OK;
+  const size_t need = carve_bwd(nullptr, M, N, K, nullptr);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
+  const Range rw = vec_range(ws, (int64_t)need, 1);
+  for (Range o : {rdy, rx, rwt, rdx, rdw})
+    if (overlap(rw, o)) return I8MP_EINVAL;
+  const int64_t kp = pad16(K), np = pad16(N);
+  const int64_t lim = (int64_t(1) << 31) - 1024;
+  if ((want_dx && (256 * np >= lim || N * kp >= lim)) || (want_dw && (M * np >= lim || M * kp >= lim)))
+    return I8MP_EINVAL;
+  i8mp_status st = device_check();
+  if (st != I8MP_OK) return st;
+  BwdWs w;
+  carve_bwd(ws, M, N, K, &w);
+  const hipStream_t s = as_stream(stream);
+  uint8_t* qdy = reinterpret_cast<uint8_t*>(w.qdy);
+  uint8_t* qw = reinterpret_cast<uint8_t*>(w.qw);
+  uint8_t* qx = reinterpret_cast<uint8_t*>(w.qx);
+  hipError_t e = hipSuccess;
+  if (want_dx) {
+    e = i8mp::launch_quantize_rowwise_fp8(dY, M, N, N, qdy, np, w.sdy, s);
+    if (e == hipSuccess) e = i8mp::launch_quantize_colwise_fp8(W, N, K, K, qw, kp, w.sw, w.col, s);
+    if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_NN, M, K, N, qdy, np, w.sdy, qw, kp, w.sw, dX, nullptr, K, s);
+  }
+  if (want_dw && e == hipSuccess) {
+    e = i8mp::launch_quantize_colwise_fp8(dY, M, N, N, qdy, np, w.sdy, w.col, s);
+    if (e == hipSuccess) e = i8mp::launch_quantize_colwise_fp8(X, M, K, K, qx, kp, w.sx, w.col, s);
+    if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_TN, N, K, M, qdy, np, w.sdy, qx, kp, w.sx, dW, nullptr, K, s);
+  }
+  return hip_status(e);
+}
+
 }  // extern "C"

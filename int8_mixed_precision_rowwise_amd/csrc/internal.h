@@ -35,6 +35,23 @@ hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_
                                          float* scale, int round, uint64_t seed, uint64_t offset,
                                          hipStream_t stream);
 
+// FP8 (E4M3) quantization, round to nearest: codes q8 in x's layout,
+// scales per row (row-wise) or per column (column-wise, slab maxima in ws,
+// colwise_workspace_bytes).
+hipError_t launch_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                       uint8_t* q8, int64_t ldq, float* scale, hipStream_t stream);
+hipError_t launch_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                       uint8_t* q8, int64_t ldq, float* scale, void* ws,
+                                       hipStream_t stream);
+
+// FP8 (E4M3) scaled GEMM with fp32 accumulation, same layouts; needs
+// K % 16 == 0.  Exactly one of C (bf16, with both scales) or C_f32 (the raw
+// fp32 sums) is non-null.
+hipError_t launch_gemm_fp8(int layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                           int64_t lda, const float* sa, const uint8_t* B, int64_t ldb,
+                           const float* sb, uint16_t* C, float* C_f32, int64_t ldc,
+                           hipStream_t stream);
+
 // int8 GEMM in layout 0 = NT, 1 = NN, 2 = TN.  Exactly one of (C_bf16 with
 // both scales) or C_i32 is non-null.
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,

@@ -85,10 +85,17 @@ __device__ __forceinline__ GroupScale scale_from_s(float s) {
   return g;
 }
 
-// amax is the bit pattern of a non-negative bf16; the scale is RN32(amax/127)
-// (an IEEE division, correctly rounded), 0 only for amax = 0.
+// Code formats: 0 = INT8 (codes in [-127, 127]), 1 = FP8 E4M3 (OCP "e4m3fn",
+// values in [-448, 448]).  The scale divides amax by the largest code.
+template <int FMT>
+constexpr float code_max() { return FMT == 1 ? 448.0f : 127.0f; }
+
+// amax is the bit pattern of a non-negative bf16; the scale is
+// RN32(amax / code max) (an IEEE division, correctly rounded), 0 only for
+// amax = 0.
+template <int FMT = 0>
 __device__ __forceinline__ GroupScale make_scale(uint32_t amax_bits) {
-  return scale_from_s(__uint_as_float(amax_bits << 16) / 127.0f);
+  return scale_from_s(__uint_as_float(amax_bits << 16) / code_max<FMT>());
 }
 
 // Quotient x / s under a known evaluation mode (1: FMA form, 2: division).
@@ -122,6 +129,30 @@ __device__ __forceinline__ int code_any(float x, const GroupScale& g, float u) {
   if (g.mode == 1) return code_of<SR, 1>(x, g.s, g.rcp, u);
   if (g.mode == 2) return code_of<SR, 2>(x, g.s, g.rcp, u);
   return 0;
+}
+
+// FP8 value of x under scale s with a known mode (1 or 2): the quotient
+// clamped to [-448, 448]; a zero x gives +0 (the FMA form already does: the
+// quotient of -0 comes out +0).  v_cvt_pk_fp8_f32 then rounds it to the
+// nearest E4M3 value, ties to even.
+template <int MODE>
+__device__ __forceinline__ float f8_value(float x, float s, float rcp) {
+  if constexpr (MODE == 2) {
+    if (x == 0.0f) return 0.0f;
+  }
+  return __builtin_amdgcn_fmed3f(quotient<MODE>(x, s, rcp), -448.0f, 448.0f);
+}
+
+__device__ __forceinline__ float f8_any(float x, const GroupScale& g) {
+  if (g.mode == 1) return f8_value<1>(x, g.s, g.rcp);
+  if (g.mode == 2) return f8_value<2>(x, g.s, g.rcp);
+  return 0.0f;
+}
+
+// Four E4M3 codes, first value in the lowest byte.
+__device__ __forceinline__ uint32_t pack_f8x4(float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
@@ -163,9 +194,21 @@ __device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, u
 // Codes of one chunk.  MODE 1 or 2: every element uses that quotient form
 // with scale g[0] (g[j] when PER_ELEM_SCALE); MODE -1: each element's own
 // GroupScale decides.  Returns 8 bytes.
-template <bool SR, bool ALIGNED4, bool PER_ELEM_SCALE, int MODE>
+template <bool SR, bool ALIGNED4, bool PER_ELEM_SCALE, int MODE, int FMT = 0>
 __device__ __forceinline__ uint2 quantize_chunk(const uint4& v, const GroupScale* g,
                                                 uint64_t seed, uint64_t offset, uint64_t e0) {
+  if constexpr (FMT == 1) {  // FP8: round to nearest only
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const GroupScale& gj = g[PER_ELEM_SCALE ? j : 0];
+      if constexpr (MODE < 0)
+        f[j] = f8_any(elem(v, j), gj);
+      else
+        f[j] = f8_value<MODE>(elem(v, j), gj.s, gj.rcp);
+    }
+    return make_uint2(pack_f8x4(f[0], f[1], f[2], f[3]), pack_f8x4(f[4], f[5], f[6], f[7]));
+  }
   float u[8];
   if constexpr (SR) {
     chunk_uniforms<ALIGNED4>(seed, offset, e0, u);
@@ -212,7 +255,7 @@ __device__ __forceinline__ void load_row(uint4 (&v)[NV], const uint16_t* __restr
   }
 }
 
-template <int NV, bool SR, bool ALIGNED4, int MODE>
+template <int NV, bool SR, bool ALIGNED4, int MODE, int FMT = 0>
 __device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const GroupScale& g,
                                                   int64_t r, int64_t cols, int8_t* __restrict__ qr,
                                                   uint64_t seed, uint64_t offset, int lane) {
@@ -222,7 +265,7 @@ __device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const Gr
     if (c0 < cols) {
       uint2 codes = make_uint2(0, 0);
       if constexpr (MODE > 0)
-        codes = quantize_chunk<SR, ALIGNED4, false, MODE>(v[i], &g, seed, offset, (uint64_t)(r * cols + c0));
+        codes = quantize_chunk<SR, ALIGNED4, false, MODE, FMT>(v[i], &g, seed, offset, (uint64_t)(r * cols + c0));
       if (c0 + 8 <= cols)
         *reinterpret_cast<uint2*>(qr + c0) = codes;
       else
@@ -231,7 +274,7 @@ __device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const Gr
   }
 }
 
-template <int NV, bool SR, bool ALIGNED4>
+template <int NV, bool SR, bool ALIGNED4, int FMT = 0>
 __device__ __forceinline__ void quantize_row(const uint4 (&v)[NV], int64_t r, int64_t cols,
                                              int8_t* __restrict__ q, int64_t ldq,
                                              float* __restrict__ scale, uint64_t seed,
@@ -242,18 +285,18 @@ __device__ __forceinline__ void quantize_row(const uint4 (&v)[NV], int64_t r, in
   // the row maximum is the same in every lane: read it from lane 0 so the
   // mode branch below is a scalar branch
   const uint32_t amax = __builtin_amdgcn_readfirstlane(wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y)));
-  const GroupScale g = make_scale(amax);
+  const GroupScale g = make_scale<FMT>(amax);
   if (lane == 0) scale[r] = g.s;
   int8_t* qr = q + r * ldq;
   if (g.mode == 1)
-    quantize_row_mode<NV, SR, ALIGNED4, 1>(v, g, r, cols, qr, seed, offset, lane);
+    quantize_row_mode<NV, SR, ALIGNED4, 1, FMT>(v, g, r, cols, qr, seed, offset, lane);
   else if (g.mode == 2)
-    quantize_row_mode<NV, SR, ALIGNED4, 2>(v, g, r, cols, qr, seed, offset, lane);
+    quantize_row_mode<NV, SR, ALIGNED4, 2, FMT>(v, g, r, cols, qr, seed, offset, lane);
   else
-    quantize_row_mode<NV, SR, ALIGNED4, 0>(v, g, r, cols, qr, seed, offset, lane);
+    quantize_row_mode<NV, SR, ALIGNED4, 0, FMT>(v, g, r, cols, qr, seed, offset, lane);
 }
 
-template <int NV, bool SR, bool ALIGNED4, bool PREFETCH>
+template <int NV, bool SR, bool ALIGNED4, bool PREFETCH, int FMT = 0>
 __global__ __launch_bounds__(kThreads) void quant_rows_wave(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
@@ -268,11 +311,11 @@ __global__ __launch_bounds__(kThreads) void quant_rows_wave(
     if constexpr (PREFETCH) {
       uint4 nv[NV];
       if (rn < rows) load_row<NV>(nv, x + rn * ldx, cols, lane);
-      quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
+      quantize_row<NV, SR, ALIGNED4, FMT>(v, r, cols, q, ldq, scale, seed, offset, lane);
 #pragma unroll
       for (int i = 0; i < NV; ++i) v[i] = nv[i];
     } else {
-      quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
+      quantize_row<NV, SR, ALIGNED4, FMT>(v, r, cols, q, ldq, scale, seed, offset, lane);
       if (rn < rows) load_row<NV>(v, x + rn * ldx, cols, lane);
     }
   }
@@ -280,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_wave(
 
 // Row-wise, one block per row, for rows longer than a wave holds: an absmax
 // sweep, then a quantize sweep that re-reads the row (from L2 / MALL).
-template <bool SR, bool ALIGNED4>
+template <bool SR, bool ALIGNED4, int FMT = 0>
 __global__ __launch_bounds__(kThreads) void quant_rows_block(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
@@ -310,15 +353,15 @@ __global__ __launch_bounds__(kThreads) void quant_rows_block(
   m = red[0];
 #pragma unroll
   for (int w = 1; w < kWavesPerBlock; ++w) m = max(m, red[w]);
-  const GroupScale g = make_scale(__builtin_amdgcn_readfirstlane(m));
+  const GroupScale g = make_scale<FMT>(__builtin_amdgcn_readfirstlane(m));
   if (threadIdx.x == 0) scale[r] = g.s;
   int8_t* qr = q + r * ldq;
   for (int64_t ch = threadIdx.x; ch < nchunks; ch += kThreads) {
     const int64_t c0 = ch * 8;
     uint4 v = *reinterpret_cast<const uint4*>(xr + c0);
     const uint2 codes =
-        g.mode == 1 ? quantize_chunk<SR, ALIGNED4, false, 1>(v, &g, seed, offset, (uint64_t)(r * cols + c0))
-                    : quantize_chunk<SR, ALIGNED4, false, -1>(v, &g, seed, offset, (uint64_t)(r * cols + c0));
+        g.mode == 1 ? quantize_chunk<SR, ALIGNED4, false, 1, FMT>(v, &g, seed, offset, (uint64_t)(r * cols + c0))
+                    : quantize_chunk<SR, ALIGNED4, false, -1, FMT>(v, &g, seed, offset, (uint64_t)(r * cols + c0));
     if (c0 + 8 <= cols)
       *reinterpret_cast<uint2*>(qr + c0) = codes;
     else
@@ -404,7 +447,7 @@ __global__ __launch_bounds__(kColThreads) void col_absmax_partial(const uint16_t
 
 // GIVEN: the column maxima come in as fp32 values (colmax) instead of slab
 // maxima to reduce (part, part_ld, slabs unused).
-template <bool SR, bool ALIGNED4, bool GIVEN>
+template <bool SR, bool ALIGNED4, bool GIVEN, int FMT = 0>
 __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __restrict__ x, int64_t rows,
                                                           int64_t cols, int64_t ldx,
                                                           int64_t rows_per_block,
@@ -438,7 +481,7 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
     if (!active) return;
     nvalid = (int)min((int64_t)8, cols - c0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? colmax[c0 + j] / 127.0f : 0.0f);
+    for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? colmax[c0 + j] / code_max<FMT>() : 0.0f);
   } else {
     // column maxima of the tile from the slab maxima
     us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
@@ -454,7 +497,7 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t bits = j & 1 ? m[j >> 1].y : m[j >> 1].x;
-      g[j] = make_scale(j < nvalid ? bits : 0u);
+      g[j] = make_scale<FMT>(j < nvalid ? bits : 0u);
     }
   }
   if (blockIdx.y == 0 && wave == 0) {
@@ -475,8 +518,8 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
       const int64_t r = r0 + (int64_t)k * kColWaves;
       if (r >= r_end) break;
       const uint64_t e0 = (uint64_t)(r * cols + c0);
-      const uint2 codes = all_fma ? quantize_chunk<SR, ALIGNED4, true, 1>(v[k], g, seed, offset, e0)
-                                  : quantize_chunk<SR, ALIGNED4, true, -1>(v[k], g, seed, offset, e0);
+      const uint2 codes = all_fma ? quantize_chunk<SR, ALIGNED4, true, 1, FMT>(v[k], g, seed, offset, e0)
+                                  : quantize_chunk<SR, ALIGNED4, true, -1, FMT>(v[k], g, seed, offset, e0);
       int8_t* dst = q + r * ldq + c0;
       if (nvalid == 8)
         *reinterpret_cast<uint2*>(dst) = codes;
@@ -717,6 +760,56 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols
       quant_rows_block<false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
     }
   }
+  return hipGetLastError();
+}
+
+namespace {
+template <int NV>
+void launch_rows_f8_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
+                       int64_t ldq, float* scale, hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + kWavesPerBlock - 1) / kWavesPerBlock));
+  quant_rows_wave<NV, false, true, false, 1><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0);
+}
+}  // namespace
+
+hipError_t launch_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                       uint8_t* q8, int64_t ldq, float* scale, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  int8_t* q = reinterpret_cast<int8_t*>(q8);
+  const int64_t per_lane = (cols + 511) / 512;
+  if (per_lane <= 1)
+    launch_rows_f8_nv<1>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane <= 2)
+    launch_rows_f8_nv<2>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane <= 4)
+    launch_rows_f8_nv<4>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane <= 8)
+    launch_rows_f8_nv<8>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane <= 12)
+    launch_rows_f8_nv<12>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane <= 16)
+    launch_rows_f8_nv<16>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane <= 28)
+    launch_rows_f8_nv<28>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else
+    quant_rows_block<false, true, 1><<<dim3((unsigned)rows), kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                       uint8_t* q8, int64_t ldq, float* scale, void* ws,
+                                       hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const ColPlan p = col_plan(rows, cols);
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  if (p.slabs > 0) {
+    col_absmax_partial<<<dim3((unsigned)p.col_tiles, (unsigned)p.slabs), kColThreads, 0, stream>>>(
+        x, rows, cols, ldx, p.rows_per_slab, part, p.part_ld);
+  }
+  const dim3 grid((unsigned)p.col_tiles, (unsigned)p.row_blocks);
+  quant_cols<false, true, false, 1><<<grid, kColThreads, 0, stream>>>(
+      x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale,
+      reinterpret_cast<int8_t*>(q8), ldq, 0, 0);
   return hipGetLastError();
 }
 
