@@ -287,6 +287,31 @@ def main():
         autograd_ms[tag] = round(e0.elapsed_time(e1) / 20, 4)
     autograd_ms["speedup_vs_bf16"] = round(autograd_ms["bf16"] / autograd_ms["int8"], 3)
 
+    # context: the same step with FP8 (E4M3) codes in place of INT8 (the
+    # library's FP8 chains: same passes, FP8 matrix-core GEMMs)
+    fp8 = None
+    if K % 16 == 0 and N % 16 == 0 and M % 16 == 0:
+        wsf = torch.empty(max(i8.linear_workspace_bytes(M, N, K, False),
+                              i8.linear_workspace_bytes(M, N, K, True)), dtype=torch.uint8, device=dev)
+
+        def fp8_step(i):
+            X, W, dY = sets[i % args.sets]
+            i8.linear_fwd_fp8(X, W, out=Y, workspace=wsf)
+            i8.linear_bwd_fp8(dY, X, W, workspace=wsf)
+
+        for i in range(5):
+            fp8_step(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(20):
+            fp8_step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fp8_ms = e0.elapsed_time(e1) / 20
+        fp8 = {"ms_per_step": round(fp8_ms, 4), "tops": round(3 * gemm_ops / (fp8_ms * 1e-3) / 1e12, 1),
+               "note": "linear_fwd_fp8 + linear_bwd_fp8 (allocating their dX, dW), same inputs"}
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -323,6 +348,7 @@ def main():
         "step_gemm_frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
         "context_torch_bf16_matmul_tflops": ctx,
         "context_autograd_layer_step_ms": autograd_ms,
+        "context_fp8_step": fp8,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
