@@ -13,7 +13,10 @@ This is the user boundary the pages describe, restated for this library:
 Every INT8 GEMM and its quantization passes run in ``libi8mp``'s kernels
 (``linear_fwd`` / ``linear_bwd``).  A GEMM switched to BF16 is a plain bf16
 matmul by torch (hipBLASLt): that is the configuration's meaning, not a
-fallback.  Inputs, weights and gradients are bf16.
+fallback.  Inputs, weights and gradients are bf16.  With ``fp8`` set, the
+quantized GEMMs take the row-wise FP8 (E4M3) path instead (``linear_fwd_fp8``
+/ ``linear_bwd_fp8``; round to nearest), the row-wise FP8 recipe that
+"Quantized model training" sets beside INT8 mixed precision.
 
 Stochastic rounding draws from Philox4x32-10 keyed by a per-module seed; the
 layer's step counter advances the counter offset by ``STEP_STRIDE`` per forward
@@ -29,7 +32,7 @@ from typing import Callable, Optional
 
 import torch
 
-from . import linear_bwd, linear_fwd, linear_fwd_colmax
+from . import linear_bwd, linear_bwd_fp8, linear_fwd, linear_fwd_colmax, linear_fwd_fp8
 
 __all__ = ["Int8MixedPrecisionConfig", "Int8MixedPrecisionLinearFunction",
            "Int8MixedPrecisionLinear", "swap_linear_modules", "STEP_STRIDE", "module_seed"]
@@ -42,13 +45,22 @@ class Int8MixedPrecisionConfig:
     """Which GEMMs of a linear layer run in INT8, and how codes are rounded.
 
     output: forward Y = X @ W.T; grad_input: dX = dY @ W; grad_weight:
-    dW = dY.T @ X.  A GEMM left False runs as a bf16 matmul.
+    dW = dY.T @ X.  A GEMM left False runs as a bf16 matmul.  fp8: the
+    quantized GEMMs use FP8 (E4M3) codes and the FP8 matrix core instead of
+    INT8 (round to nearest only; every quantized GEMM's contraction length a
+    multiple of 16 and its output extents along operands read down their
+    rows multiples of 4).
     """
     output: bool = True
     grad_input: bool = True
     grad_weight: bool = True
     stochastic_rounding: bool = False
     seed: int = 0
+    fp8: bool = False
+
+    def __post_init__(self):
+        if self.fp8 and self.stochastic_rounding:
+            raise ValueError("the FP8 variant rounds to nearest only")
 
     @property
     def rounding(self) -> str:
@@ -89,7 +101,9 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
         x2 = _as_rows(x, x.shape[-1])
         w = weight if weight.is_contiguous() else weight.contiguous()
         cx = cw = None
-        if config.output and (config.grad_input or config.grad_weight):
+        if config.output and config.fp8:
+            y = linear_fwd_fp8(x2, w)
+        elif config.output and (config.grad_input or config.grad_weight):
             y, cx, cw = linear_fwd_colmax(x2, w, config.rounding, seed, offset)
         elif config.output:
             y = linear_fwd(x2, w, config.rounding, seed, offset)
@@ -107,7 +121,9 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
         dy2 = _as_rows(dy.to(torch.bfloat16), w.shape[0])
         int_dx, int_dw = need_dx and cfg.grad_input, need_dw and cfg.grad_weight
         dx = dw = None
-        if int_dx or int_dw:
+        if (int_dx or int_dw) and cfg.fp8:
+            dx, dw = linear_bwd_fp8(dy2, x2, w, want_dx=int_dx, want_dw=int_dw)
+        elif int_dx or int_dw:
             dx, dw = linear_bwd(dy2, x2, w, cfg.rounding, ctx.seed, ctx.offset,
                                 want_dx=int_dx, want_dw=int_dw, colmax_x=cx, colmax_w=cw)
         if need_dx and not int_dx:
@@ -158,7 +174,8 @@ class Int8MixedPrecisionLinear(torch.nn.Linear):
         c = self.config
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"output={'int8' if c.output else 'bf16'}, grad_input={'int8' if c.grad_input else 'bf16'}, "
-                f"grad_weight={'int8' if c.grad_weight else 'bf16'}, rounding={c.rounding}")
+                f"grad_weight={'int8' if c.grad_weight else 'bf16'}, rounding={c.rounding}"
+                + (", codes=fp8_e4m3" if c.fp8 else ""))
 
 
 def swap_linear_modules(model: torch.nn.Module, config: Optional[Int8MixedPrecisionConfig] = None,

@@ -113,3 +113,31 @@ def test_weight_gradient_only_and_sr_steps():
     y1 = lin(X)
     same(y1, oracle.linear_fwd(Xb, Wb, oracle.SR, 41, T.STEP_STRIDE), "step 1 y")
     assert not torch.equal(y0, y1)
+
+
+def test_fp8_mlp_matches_fp8_chains():
+    """The FP8 switch: the MLP's output and gradients equal the library's FP8
+    chains run directly (whose parity with the oracle is in test_gpu_fp8.py)."""
+    B, S, K1, H, N = 2, 64, 256, 512, 192
+    x = gaussian_bf16(B * S, K1, seed=31).view(B, S, K1).cuda().requires_grad_()
+    W1 = gaussian_bf16(H, K1, seed=32, std=0.02).cuda()
+    W2 = gaussian_bf16(N, H, seed=33, std=0.02).cuda()
+    G = gaussian_bf16(B * S, N, seed=34, std=1e-3).view(B, S, N).cuda()
+    model = torch.nn.Sequential(torch.nn.Linear(K1, H, bias=False), torch.nn.ReLU(),
+                                torch.nn.Linear(H, N, bias=False)).to(torch.bfloat16).cuda()
+    with torch.no_grad():
+        model[0].weight.copy_(W1)
+        model[2].weight.copy_(W2)
+    T.swap_linear_modules(model, T.Int8MixedPrecisionConfig(fp8=True))
+    y = model(x)
+    y.backward(G)
+    X2 = x.detach().view(-1, K1)
+    Y1 = i8.linear_fwd_fp8(X2, W1)
+    Hh = torch.relu(Y1)
+    Y2 = i8.linear_fwd_fp8(Hh, W2)
+    dH, dW2 = i8.linear_bwd_fp8(G.view(-1, N), Hh, W2)
+    dY1 = torch.where(Y1 > 0, dH, torch.zeros_like(dH))
+    dX, dW1 = i8.linear_bwd_fp8(dY1, X2, W1)
+    for got, want, what in ((y.view(-1, N), Y2, "y"), (x.grad.view(-1, K1), dX, "dX"),
+                            (model[0].weight.grad, dW1, "dW1"), (model[2].weight.grad, dW2, "dW2")):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), what

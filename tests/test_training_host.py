@@ -74,3 +74,11 @@ def test_config_and_argument_checks():
         T.Int8MixedPrecisionLinearFunction.apply(torch.zeros(2, 4, dtype=torch.bfloat16),
                                                  torch.zeros(3, 5, dtype=torch.bfloat16), c, 0, 0)
     assert "grad_weight=int8" in repr(T.Int8MixedPrecisionLinear(4, 4))
+
+
+def test_fp8_config():
+    c = T.Int8MixedPrecisionConfig(fp8=True)
+    assert c.fp8 and c.rounding == "rne"
+    with pytest.raises(ValueError):
+        T.Int8MixedPrecisionConfig(fp8=True, stochastic_rounding=True)
+    assert "codes=fp8_e4m3" in repr(T.Int8MixedPrecisionLinear(4, 4, c))
