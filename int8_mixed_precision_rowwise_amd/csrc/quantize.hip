@@ -110,22 +110,27 @@ __device__ __forceinline__ float quotient(float x, float s, float rcp) {
   }
 }
 
-// int8 code of x (as an int) under scale s with a known mode (1 or 2).
+// int8 code of x under scale s with a known mode (1 or 2), in the low byte
+// of the result (the upper bytes are not part of the code).
+//
+// Round half to even: rounding is monotone and +-127 are integers, so
+// clamping the quotient first gives the same code.  Adding 1.5 * 2^23 to a
+// value in [-127, 127] rounds it to an integer n (ties to even: the added
+// constant is even), and the sum's bit pattern is that of 1.5 * 2^23 plus n,
+// so its low byte is n in two's complement.
 template <bool SR, int MODE>
-__device__ __forceinline__ int code_of(float x, float s, float rcp, float u) {
+__device__ __forceinline__ uint32_t code_of(float x, float s, float rcp, float u) {
   const float v = quotient<MODE>(x, s, rcp);
-  float r;
   if constexpr (SR) {
-    r = floorf(v + u);
+    return (uint32_t)(int)__builtin_amdgcn_fmed3f(floorf(v + u), -127.0f, 127.0f);
   } else {
-    r = rintf(v);  // round half to even
+    return __float_as_uint(__builtin_amdgcn_fmed3f(v, -127.0f, 127.0f) + 0x1.8p23f);
   }
-  return (int)__builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
 }
 
 // Any mode, decided per element (0 gives code 0).
 template <bool SR>
-__device__ __forceinline__ int code_any(float x, const GroupScale& g, float u) {
+__device__ __forceinline__ uint32_t code_any(float x, const GroupScale& g, float u) {
   if (g.mode == 1) return code_of<SR, 1>(x, g.s, g.rcp, u);
   if (g.mode == 2) return code_of<SR, 2>(x, g.s, g.rcp, u);
   return 0;
@@ -155,9 +160,9 @@ __device__ __forceinline__ uint32_t pack_f8x4(float a, float b, float c, float d
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
-         ((uint32_t)d << 24);
+// Low bytes of four words, a's in the lowest byte.
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return (a & 0xFFu) | ((b & 0xFFu) << 8) | ((c & 0xFFu) << 16) | (d << 24);
 }
 
 __device__ __forceinline__ float elem(const uint4& v, int j) {
@@ -216,7 +221,7 @@ __device__ __forceinline__ uint2 quantize_chunk(const uint4& v, const GroupScale
 #pragma unroll
     for (int j = 0; j < 8; ++j) u[j] = 0.0f;
   }
-  int c[8];
+  uint32_t c[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const GroupScale& gj = g[PER_ELEM_SCALE ? j : 0];
@@ -445,66 +450,80 @@ __global__ __launch_bounds__(kColThreads) void col_absmax_partial(const uint16_t
   }
 }
 
-// GIVEN: the column maxima come in as fp32 values (colmax) instead of slab
-// maxima to reduce (part, part_ld, slabs unused).
-template <bool SR, bool ALIGNED4, bool GIVEN, int FMT = 0>
+// Pass 2 of the two-pass column quantize: a block is rows_per_block rows of
+// one column tile, its waves interleaved over the rows; it starts by reducing
+// the tile's slab maxima (at most kColMaxSlabs slabs) into the scales.
+template <bool SR, bool ALIGNED4, int FMT = 0>
 __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __restrict__ x, int64_t rows,
                                                           int64_t cols, int64_t ldx,
                                                           int64_t rows_per_block,
                                                           const uint16_t* __restrict__ part,
                                                           int64_t part_ld, int64_t slabs,
-                                                          const float* __restrict__ colmax,
                                                           float* __restrict__ scale,
                                                           int8_t* __restrict__ q, int64_t ldq,
                                                           uint64_t seed, uint64_t offset) {
-  __shared__ uint4 red[GIVEN ? 1 : kColWaves][64];
+  __shared__ uint4 red[kColWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
-  const bool active = c0 < cols;
   // row blocks run last-to-first, so the rows pass 1 touched last (still in
   // L2 / MALL) are read first
-  const int64_t rb = (int64_t)gridDim.y - 1 - blockIdx.y;
-  const int64_t r_begin = rb * rows_per_block;
+  const int64_t r_begin = ((int64_t)gridDim.y - 1 - blockIdx.y) * rows_per_block;
   const int64_t r_end = min(rows, r_begin + rows_per_block);
-  constexpr int U = SR ? kColLoads / 2 : kColLoads;  // SR's Philox state needs the registers
-  // the first rows' loads go out before the scales are known
-  uint4 v[U];
   int64_t r0 = r_begin + wave;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTile + lane * 8;
+  const bool active = c0 < cols;
+  // Loads carry no branches: lanes past the last column read column 0 and
+  // rows past the block's end read its last row (values never used), so
+  // each wait for a value covers only the loads issued before it.  The slab
+  // maxima go out first and are ready while the rows still arrive.
+  const int64_t cl = active ? c0 : 0;
+  constexpr int kSlabLoads = kColMaxSlabs / kColWaves;
+  uint4 pv[kSlabLoads];
+  {
+    // the workspace holds at least one slab; a slab read twice leaves the
+    // maximum unchanged
+    const int64_t s_last = max(slabs, (int64_t)1) - 1;
 #pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const int64_t r = r0 + (int64_t)k * kColWaves;
-    v[k] = active && r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kSlabLoads; ++i)
+      pv[i] = *reinterpret_cast<const uint4*>(part + min((int64_t)(wave + i * kColWaves), s_last) * part_ld + cl);
   }
   GroupScale g[8];
-  int nvalid = 0;
-  if constexpr (GIVEN) {
-    if (!active) return;
-    nvalid = (int)min((int64_t)8, cols - c0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? colmax[c0 + j] / code_max<FMT>() : 0.0f);
-  } else {
-    // column maxima of the tile from the slab maxima
+  const int nvalid = active ? (int)min((int64_t)8, cols - c0) : 0;
+  auto make_scales = [&]() {
     us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
-    if (active) {
-      for (int64_t s = wave; s < slabs; s += kColWaves)
-        max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
+    if (slabs > 0) {
+#pragma unroll
+      for (int i = 0; i < kSlabLoads; ++i) max_chunk(m, pv[i]);
     }
     red[wave][lane] = pack_max(m);
     __syncthreads();
-    if (!active) return;
     reduce_waves(m, red, lane);
-    nvalid = (int)min((int64_t)8, cols - c0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t bits = j & 1 ? m[j >> 1].y : m[j >> 1].x;
       g[j] = make_scale<FMT>(j < nvalid ? bits : 0u);
     }
-  }
-  if (blockIdx.y == 0 && wave == 0) {
+    if (blockIdx.y == 0 && wave == 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < nvalid) scale[c0 + j] = g[j].s;
+      for (int j = 0; j < 8; ++j)
+        if (j < nvalid) scale[c0 + j] = g[j].s;
+    }
+  };
+  if (r_end <= r_begin) {  // no rows: only the (zero) scales are stored
+    make_scales();
+    return;
   }
+  constexpr int U = SR ? kColLoads / 2 : kColLoads;  // SR's Philox state needs the registers
+  uint4 v[U];
+  auto load_rows = [&](int64_t first) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t r = first + (int64_t)k * kColWaves;
+      v[k] = *reinterpret_cast<const uint4*>(x + min(r, r_end - 1) * ldx + cl);
+    }
+  };
+  load_rows(r0);
+  make_scales();
+  if (!active) return;
   // almost always every column of the wave takes the FMA quotient: then no
   // per-element mode test is needed (padding columns give zero codes that are
   // never stored)
@@ -527,12 +546,87 @@ __global__ __launch_bounds__(kColThreads) void quant_cols(const uint16_t* __rest
         store_partial(dst, codes, nvalid);
     }
     const int64_t rn = r0 + (int64_t)U * kColWaves;
+    if (rn < r_end) load_rows(rn);
+  }
+}
+
+// Column-wise with the column maxima given (fp32, one per column).  A block is
+// a band of kColBand consecutive rows (blockIdx.x) across kColWaves column
+// tiles (blockIdx.y), one 512-column tile per wave, so each block reads one
+// contiguous stretch of the tensor.  Measured at 4096 x 4096 on MI355X: bands
+// of 4-16 rows run 10.7-11.5 us, against 16.1 us for blocks of 128 rows of
+// one tile; the many small blocks keep more waves per CU busy converting
+// while the rows arrive.  A wave whose band and tile are whole takes a body
+// without range checks (FULL); the ragged edges take the checked one.
+constexpr int kColBand = 8;
+
+template <bool FULL, bool SR, bool ALIGNED4, int FMT>
+__device__ __forceinline__ void given_band(const uint16_t* __restrict__ x, int64_t cols, int64_t ldx,
+                                           const float* __restrict__ colmax,
+                                           float* __restrict__ scale, int8_t* __restrict__ q,
+                                           int64_t ldq, uint64_t seed, uint64_t offset,
+                                           int64_t r_begin, int64_t nrows, int64_t c0,
+                                           bool store_scales) {
+  const bool active = FULL || c0 < cols;
+  const int64_t cl = active ? c0 : 0;  // lanes past the last column read column 0
+  uint4 v[kColBand];
+  if (FULL || nrows > 0) {
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int64_t r = rn + (int64_t)k * kColWaves;
-      v[k] = r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < kColBand; ++k) {
+      const int64_t r = r_begin + (FULL ? k : min((int64_t)k, nrows - 1));
+      v[k] = *reinterpret_cast<const uint4*>(x + r * ldx + cl);
     }
   }
+  float cm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cm[j] = colmax[FULL ? c0 + j : min(c0 + j, cols - 1)];
+  const int nvalid = FULL ? 8 : (active ? (int)min((int64_t)8, cols - c0) : 0);
+  GroupScale g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g[j] = scale_from_s(j < nvalid ? cm[j] / code_max<FMT>() : 0.0f);
+  if (store_scales) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < nvalid) scale[c0 + j] = g[j].s;
+  }
+  if (!active) return;
+  bool mine = true;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mine = mine && (j >= nvalid || g[j].mode == 1);
+  const bool all_fma = __all(mine);
+#pragma unroll
+  for (int k = 0; k < kColBand; ++k) {
+    if (!FULL && k >= nrows) break;
+    const int64_t r = r_begin + k;
+    const uint64_t e0 = (uint64_t)(r * cols + c0);
+    const uint2 codes = all_fma ? quantize_chunk<SR, ALIGNED4, true, 1, FMT>(v[k], g, seed, offset, e0)
+                                : quantize_chunk<SR, ALIGNED4, true, -1, FMT>(v[k], g, seed, offset, e0);
+    int8_t* dst = q + r * ldq + c0;
+    if (FULL || nvalid == 8)
+      *reinterpret_cast<uint2*>(dst) = codes;
+    else
+      store_partial(dst, codes, nvalid);
+  }
+}
+
+template <bool SR, bool ALIGNED4, int FMT = 0>
+__global__ __launch_bounds__(kColThreads) void quant_cols_given(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    const float* __restrict__ colmax, float* __restrict__ scale, int8_t* __restrict__ q,
+    int64_t ldq, uint64_t seed, uint64_t offset) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = (int64_t)blockIdx.y * kColWaves + (threadIdx.x >> 6);
+  if (tile * kColTile >= cols) return;  // a wave past the last tile
+  const int64_t c0 = tile * kColTile + lane * 8;
+  const int64_t r_begin = (int64_t)blockIdx.x * kColBand;
+  const int64_t nrows = min((int64_t)kColBand, rows - r_begin);  // 0 only when rows == 0
+  const bool store_scales = blockIdx.x == 0;
+  if (nrows == kColBand && (tile + 1) * kColTile <= cols)
+    given_band<true, SR, ALIGNED4, FMT>(x, cols, ldx, colmax, scale, q, ldq, seed, offset, r_begin,
+                                        nrows, c0, store_scales);
+  else
+    given_band<false, SR, ALIGNED4, FMT>(x, cols, ldx, colmax, scale, q, ldq, seed, offset, r_begin,
+                                         nrows, c0, store_scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -562,6 +656,10 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
   int64_t r = r_begin + wave;
   if (r < r_end) load_row<NV>(v, x + r * ldx, cols, lane);
   for (; r < r_end; r += WAVES) {
+    // the wave's next row is in flight while this one is reduced and quantized
+    uint4 nv[NV];
+    const int64_t rn = r + WAVES;
+    if (rn < r_end) load_row<NV>(nv, x + rn * ldx, cols, lane);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {  // load_row zeroed the columns past the end
       us2 m[4];
@@ -571,8 +669,8 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
       cm[wave][i * 64 + lane] = pack_max(m);
     }
     quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
-    const int64_t rn = r + WAVES;
-    if (rn < r_end) load_row<NV>(v, x + rn * ldx, cols, lane);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = nv[i];
   }
   __syncthreads();
   for (int j = threadIdx.x; j < NV * 64; j += 64 * WAVES) {
@@ -807,8 +905,8 @@ hipError_t launch_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t 
         x, rows, cols, ldx, p.rows_per_slab, part, p.part_ld);
   }
   const dim3 grid((unsigned)p.col_tiles, (unsigned)p.row_blocks);
-  quant_cols<false, true, false, 1><<<grid, kColThreads, 0, stream>>>(
-      x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale,
+  quant_cols<false, true, 1><<<grid, kColThreads, 0, stream>>>(
+      x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale,
       reinterpret_cast<int8_t*>(q8), ldq, 0, 0);
   return hipGetLastError();
 }
@@ -833,11 +931,11 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if (a4)
-      quant_cols<true, true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale, q, ldq, seed, offset);
+      quant_cols<true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
     else
-      quant_cols<true, false, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale, q, ldq, seed, offset);
+      quant_cols<true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
   } else {
-    quant_cols<false, true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, nullptr, scale, q, ldq, seed, offset);
+    quant_cols<false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale, q, ldq, seed, offset);
   }
   return hipGetLastError();
 }
@@ -890,16 +988,20 @@ hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_
                                          float* scale, int round, uint64_t seed, uint64_t offset,
                                          hipStream_t stream) {
   if (cols == 0) return hipSuccess;
-  const ColPlan p = col_plan(rows, cols);
-  const dim3 grid((unsigned)p.col_tiles, (unsigned)p.row_blocks);
+  // bands of kColBand rows (at least one, so the scales are written for an
+  // empty tensor too) x groups of kColWaves column tiles
+  const int64_t bands = max((int64_t)1, (rows + kColBand - 1) / kColBand);
+  const int64_t groups = (cols + (int64_t)kColTile * kColWaves - 1) / ((int64_t)kColTile * kColWaves);
+  if (bands > 0x7FFFFFFF || groups > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)bands, (unsigned)groups);
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if (a4)
-      quant_cols<true, true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, nullptr, 0, 0, colmax, scale, q, ldq, seed, offset);
+      quant_cols_given<true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, colmax, scale, q, ldq, seed, offset);
     else
-      quant_cols<true, false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, nullptr, 0, 0, colmax, scale, q, ldq, seed, offset);
+      quant_cols_given<true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, colmax, scale, q, ldq, seed, offset);
   } else {
-    quant_cols<false, true, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, nullptr, 0, 0, colmax, scale, q, ldq, seed, offset);
+    quant_cols_given<false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, colmax, scale, q, ldq, seed, offset);
   }
   return hipGetLastError();
 }
