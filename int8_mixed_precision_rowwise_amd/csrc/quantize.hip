@@ -56,10 +56,30 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int n) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Maximum over the 64 lanes of a wave (all lanes active), the same value in
+// every lane.  DPP: within each row of 16 lanes DPP moves combine neighbours
+// (quad permutes [1,0,3,2] and [2,3,0,1], then the half-row and row
+// mirrors) and the four row maxima are read out with readlane, all in VALU /
+// SALU latency; otherwise butterfly shuffles through LDS permutes.  Which is
+// faster depends on the kernel (measured at 4096 x 4096: the one-row-per-wave
+// pass, at 59 VGPRs and 8 waves per SIMD, runs 0.5 us faster with shuffles;
+// the pass with column maxima, at 2-3 waves per SIMD, 0.3 us faster with DPP).
+template <bool DPP>
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  if constexpr (!DPP) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  return m;
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    return m;
+  }
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Scale of one group and how its quotients are evaluated.
@@ -243,35 +263,36 @@ __device__ __forceinline__ void store_partial(int8_t* dst, uint2 codes, int n) {
 // and the quantize sweep, so it is read from HBM once.  NV chunks per lane
 // cover rows of up to NV * 512 elements.  Waves walk rows with a grid stride;
 // with PREFETCH the next row's loads are in flight while the current row is
-// reduced, quantized and stored.
+// reduced, quantized and stored.  FULL: the row is exactly NV * 512 elements,
+// so no chunk needs a range check.
 
-template <int NV>
+template <int NV, bool FULL = false>
 __device__ __forceinline__ void load_row(uint4 (&v)[NV], const uint16_t* __restrict__ xr,
                                          int64_t cols, int lane) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t c0 = (int64_t)(i * 64 + lane) * 8;
-    if (c0 < cols) {
+    if (FULL || c0 < cols) {
       v[i] = *reinterpret_cast<const uint4*>(xr + c0);
-      if (c0 + 8 > cols) v[i] = keep_first(v[i], (int)(cols - c0));
+      if (!FULL && c0 + 8 > cols) v[i] = keep_first(v[i], (int)(cols - c0));
     } else {
       v[i] = make_uint4(0, 0, 0, 0);
     }
   }
 }
 
-template <int NV, bool SR, bool ALIGNED4, int MODE, int FMT = 0>
+template <int NV, bool SR, bool ALIGNED4, int MODE, int FMT = 0, bool FULL = false>
 __device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const GroupScale& g,
                                                   int64_t r, int64_t cols, int8_t* __restrict__ qr,
                                                   uint64_t seed, uint64_t offset, int lane) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t c0 = (int64_t)(i * 64 + lane) * 8;
-    if (c0 < cols) {
+    if (FULL || c0 < cols) {
       uint2 codes = make_uint2(0, 0);
       if constexpr (MODE > 0)
         codes = quantize_chunk<SR, ALIGNED4, false, MODE, FMT>(v[i], &g, seed, offset, (uint64_t)(r * cols + c0));
-      if (c0 + 8 <= cols)
+      if (FULL || c0 + 8 <= cols)
         *reinterpret_cast<uint2*>(qr + c0) = codes;
       else
         store_partial(qr + c0, codes, (int)(cols - c0));
@@ -279,7 +300,7 @@ __device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const Gr
   }
 }
 
-template <int NV, bool SR, bool ALIGNED4, int FMT = 0>
+template <int NV, bool SR, bool ALIGNED4, int FMT = 0, bool FULL = false, bool DPP = false>
 __device__ __forceinline__ void quantize_row(const uint4 (&v)[NV], int64_t r, int64_t cols,
                                              int8_t* __restrict__ q, int64_t ldq,
                                              float* __restrict__ scale, uint64_t seed,
@@ -289,19 +310,19 @@ __device__ __forceinline__ void quantize_row(const uint4 (&v)[NV], int64_t r, in
   for (int i = 0; i < NV; ++i) m2 = absmax_bits(m2, v[i]);
   // the row maximum is the same in every lane: read it from lane 0 so the
   // mode branch below is a scalar branch
-  const uint32_t amax = __builtin_amdgcn_readfirstlane(wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y)));
+  const uint32_t amax = __builtin_amdgcn_readfirstlane(wave_max_u32<DPP>(max((uint32_t)m2.x, (uint32_t)m2.y)));
   const GroupScale g = make_scale<FMT>(amax);
   if (lane == 0) scale[r] = g.s;
   int8_t* qr = q + r * ldq;
   if (g.mode == 1)
-    quantize_row_mode<NV, SR, ALIGNED4, 1, FMT>(v, g, r, cols, qr, seed, offset, lane);
+    quantize_row_mode<NV, SR, ALIGNED4, 1, FMT, FULL>(v, g, r, cols, qr, seed, offset, lane);
   else if (g.mode == 2)
-    quantize_row_mode<NV, SR, ALIGNED4, 2, FMT>(v, g, r, cols, qr, seed, offset, lane);
+    quantize_row_mode<NV, SR, ALIGNED4, 2, FMT, FULL>(v, g, r, cols, qr, seed, offset, lane);
   else
-    quantize_row_mode<NV, SR, ALIGNED4, 0, FMT>(v, g, r, cols, qr, seed, offset, lane);
+    quantize_row_mode<NV, SR, ALIGNED4, 0, FMT, FULL>(v, g, r, cols, qr, seed, offset, lane);
 }
 
-template <int NV, bool SR, bool ALIGNED4, bool PREFETCH, int FMT = 0>
+template <int NV, bool SR, bool ALIGNED4, bool PREFETCH, int FMT = 0, bool FULL = false>
 __global__ __launch_bounds__(kThreads) void quant_rows_wave(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset) {
@@ -310,18 +331,18 @@ __global__ __launch_bounds__(kThreads) void quant_rows_wave(
   int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (r >= rows) return;
   uint4 v[NV];
-  load_row<NV>(v, x + r * ldx, cols, lane);
+  load_row<NV, FULL>(v, x + r * ldx, cols, lane);
   for (; r < rows; r += stride) {
     const int64_t rn = r + stride;
     if constexpr (PREFETCH) {
       uint4 nv[NV];
-      if (rn < rows) load_row<NV>(nv, x + rn * ldx, cols, lane);
-      quantize_row<NV, SR, ALIGNED4, FMT>(v, r, cols, q, ldq, scale, seed, offset, lane);
+      if (rn < rows) load_row<NV, FULL>(nv, x + rn * ldx, cols, lane);
+      quantize_row<NV, SR, ALIGNED4, FMT, FULL>(v, r, cols, q, ldq, scale, seed, offset, lane);
 #pragma unroll
       for (int i = 0; i < NV; ++i) v[i] = nv[i];
     } else {
-      quantize_row<NV, SR, ALIGNED4, FMT>(v, r, cols, q, ldq, scale, seed, offset, lane);
-      if (rn < rows) load_row<NV>(v, x + rn * ldx, cols, lane);
+      quantize_row<NV, SR, ALIGNED4, FMT, FULL>(v, r, cols, q, ldq, scale, seed, offset, lane);
+      if (rn < rows) load_row<NV, FULL>(v, x + rn * ldx, cols, lane);
     }
   }
 }
@@ -352,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_block(
       m2 = absmax_bits(m2, v[k]);
     }
   }
-  uint32_t m = wave_max_u32(max((uint32_t)m2.x, (uint32_t)m2.y));
+  uint32_t m = wave_max_u32<false>(max((uint32_t)m2.x, (uint32_t)m2.y));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   m = red[0];
@@ -641,7 +662,7 @@ __global__ __launch_bounds__(kColThreads) void quant_cols_given(
 // row-wise pass of a tensor also yields what its column-wise pass needs,
 // without a second read of the tensor.
 
-template <int NV, int WAVES, bool SR, bool ALIGNED4>
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false>
 __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset, int64_t rows_per_block,
@@ -654,12 +675,12 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
   for (int i = 0; i < NV; ++i) cm[wave][i * 64 + lane] = make_uint4(0, 0, 0, 0);
   uint4 v[NV];
   int64_t r = r_begin + wave;
-  if (r < r_end) load_row<NV>(v, x + r * ldx, cols, lane);
+  if (r < r_end) load_row<NV, FULL>(v, x + r * ldx, cols, lane);
   for (; r < r_end; r += WAVES) {
     // the wave's next row is in flight while this one is reduced and quantized
     uint4 nv[NV];
     const int64_t rn = r + WAVES;
-    if (rn < r_end) load_row<NV>(nv, x + rn * ldx, cols, lane);
+    if (rn < r_end) load_row<NV, FULL>(nv, x + rn * ldx, cols, lane);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {  // load_row zeroed the columns past the end
       us2 m[4];
@@ -668,7 +689,7 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
       max_chunk(m, v[i]);
       cm[wave][i * 64 + lane] = pack_max(m);
     }
-    quantize_row<NV, SR, ALIGNED4>(v, r, cols, q, ldq, scale, seed, offset, lane);
+    quantize_row<NV, SR, ALIGNED4, 0, FULL, true>(v, r, cols, q, ldq, scale, seed, offset, lane);
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = nv[i];
   }
@@ -772,6 +793,8 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
       quant_rows_wave<NV, true, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
     else
       quant_rows_wave<NV, true, false, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+  } else if (cols == NV * 512) {
+    quant_rows_wave<NV, false, true, PF, 0, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   } else {
     quant_rows_wave<NV, false, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   }
@@ -820,6 +843,8 @@ void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int6
       quant_rows_colmax<NV, WAVES, true, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
     else
       quant_rows_colmax<NV, WAVES, true, false><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+  } else if (cols == NV * 512) {
+    quant_rows_colmax<NV, WAVES, false, true, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   } else {
     quant_rows_colmax<NV, WAVES, false, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   }
@@ -866,7 +891,10 @@ template <int NV>
 void launch_rows_f8_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
                        int64_t ldq, float* scale, hipStream_t stream) {
   const dim3 grid((unsigned)((rows + kWavesPerBlock - 1) / kWavesPerBlock));
-  quant_rows_wave<NV, false, true, false, 1><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0);
+  if (cols == NV * 512)
+    quant_rows_wave<NV, false, true, false, 1, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0);
+  else
+    quant_rows_wave<NV, false, true, false, 1><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0);
 }
 }  // namespace
 
