@@ -677,10 +677,6 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
   int64_t r = r_begin + wave;
   if (r < r_end) load_row<NV, FULL>(v, x + r * ldx, cols, lane);
   for (; r < r_end; r += WAVES) {
-    // the wave's next row is in flight while this one is reduced and quantized
-    uint4 nv[NV];
-    const int64_t rn = r + WAVES;
-    if (rn < r_end) load_row<NV, FULL>(nv, x + rn * ldx, cols, lane);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {  // load_row zeroed the columns past the end
       us2 m[4];
@@ -690,8 +686,8 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
       cm[wave][i * 64 + lane] = pack_max(m);
     }
     quantize_row<NV, SR, ALIGNED4, 0, FULL, true>(v, r, cols, q, ldq, scale, seed, offset, lane);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = nv[i];
+    const int64_t rn = r + WAVES;
+    if (rn < r_end) load_row<NV, FULL>(v, x + rn * ldx, cols, lane);
   }
   __syncthreads();
   for (int j = threadIdx.x; j < NV * 64; j += 64 * WAVES) {
@@ -704,39 +700,40 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
   }
 }
 
-// fp32 column maxima from slab maxima.  A block of 16 waves covers 64
-// columns: lane l reads the 16-byte chunk l % 8 (8 columns) of slab l / 8 of
-// each group of 8 slabs, so one load instruction of a wave covers 8 slabs;
-// wave w takes slab groups w, w + 16, ...  The 8 lanes sharing a chunk, then
-// the 16 waves, are folded.
-constexpr int kFinThreads = 1024;
+// fp32 column maxima from slab maxima.  A block of 8 waves covers 32
+// columns: lane l reads the 16-byte chunk l % 4 (8 columns) of slab l / 4 of
+// each group of 16 slabs, so one load instruction of a wave covers 16 slabs;
+// wave w takes slab groups w, w + 8, ...  Each lane's first two loads go out
+// together.  The 16 lanes sharing a chunk, then the 8 waves, are folded.
+constexpr int kFinThreads = 512;
 constexpr int kFinWaves = kFinThreads / 64;
 
 __global__ __launch_bounds__(kFinThreads) void colmax_finalize(const uint16_t* __restrict__ part,
                                                                int64_t part_ld, int64_t slabs,
                                                                int64_t cols,
                                                                float* __restrict__ colmax) {
-  __shared__ uint4 red[kFinWaves][8];
+  __shared__ uint4 red[kFinWaves][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunk = lane & 7, sub = lane >> 3;
-  const int64_t c0 = (int64_t)blockIdx.x * 64 + chunk * 8;
+  const int chunk = lane & 3, sub = lane >> 2;
+  const int64_t c0 = (int64_t)blockIdx.x * 32 + chunk * 8;
   us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
   if (c0 < cols) {
-    constexpr int U = 4;
-    int64_t s = (int64_t)wave * 8 + sub;
-    constexpr int64_t step = (int64_t)kFinWaves * 8;
-    for (; s + (U - 1) * step < slabs; s += U * step) {
-      uint4 v[U];
+    constexpr int64_t step = (int64_t)kFinWaves * 16;
+    const int64_t s0 = (int64_t)wave * 16 + sub;
+    uint4 v[2];
 #pragma unroll
-      for (int k = 0; k < U; ++k) v[k] = *reinterpret_cast<const uint4*>(part + (s + k * step) * part_ld + c0);
-#pragma unroll
-      for (int k = 0; k < U; ++k) max_chunk(m, v[k]);
+    for (int k = 0; k < 2; ++k) {
+      const int64_t s = s0 + k * step;
+      v[k] = s < slabs ? *reinterpret_cast<const uint4*>(part + s * part_ld + c0) : make_uint4(0, 0, 0, 0);
     }
-    for (; s < slabs; s += step) max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
+    max_chunk(m, v[0]);
+    max_chunk(m, v[1]);
+    for (int64_t s = s0 + 2 * step; s < slabs; s += step)
+      max_chunk(m, *reinterpret_cast<const uint4*>(part + s * part_ld + c0));
   }
-  // fold the 8 lanes of each chunk (lanes chunk, chunk + 8, ..., chunk + 56)
+  // fold the 16 lanes of each chunk (lanes chunk, chunk + 4, ..., chunk + 60)
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int off = 4; off < 64; off <<= 1) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t o = (uint32_t)__shfl_xor((int)__builtin_bit_cast(uint32_t, m[k]), off);
@@ -800,9 +797,9 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
   }
 }
 
-// Row-wise with column maxima: 8 waves per block (4 for rows of more than
-// 6144 elements, whose per-lane state and LDS regions are larger), about
-// 256 blocks, each a band of whole rows.  Rows longer than 14336 elements (the block-per-row
+// Row-wise with column maxima: 16 waves per block for rows of up to 4096
+// elements, 8 up to 6144 and 4 beyond (per-lane state and LDS regions grow
+// with the row), about 256 blocks, each a band of whole rows.  Rows longer than 14336 elements (the block-per-row
 // kernel) get their column maxima from a separate column-maxima pass.
 struct RowColmaxPlan {
   bool fused;
@@ -817,7 +814,7 @@ RowColmaxPlan rcm_plan(int64_t rows, int64_t cols) {
   p.part_ld = (cols + 7) / 8 * 8;
   if (p.fused) {
     // about one block per CU (a block's registers and LDS fill most of one)
-    p.waves = per_lane > 12 ? 4 : 8;
+    p.waves = per_lane > 12 ? 4 : (per_lane > 8 ? 8 : 16);
     int64_t rpb = (rows + 255) / 256;
     rpb = (rpb + p.waves - 1) / p.waves * p.waves;
     p.rows_per_block = max(rpb, (int64_t)p.waves);
@@ -835,7 +832,7 @@ template <int NV>
 void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int64_t cols,
                    int64_t ldx, int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
                    uint64_t offset, uint16_t* part, hipStream_t stream) {
-  constexpr int WAVES = NV >= 16 ? 4 : 8;  // LDS: WAVES x NV KiB of column maxima
+  constexpr int WAVES = NV >= 16 ? 4 : (NV > 8 ? 8 : 16);  // LDS: WAVES x NV KiB of column maxima
   const dim3 grid((unsigned)p.slabs);
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
@@ -1006,7 +1003,7 @@ hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64
           x, rows, cols, ldx, c.rows_per_slab, part, c.part_ld);
     }
   }
-  colmax_finalize<<<dim3((unsigned)((cols + 63) / 64)), kFinThreads, 0, stream>>>(
+  colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(
       part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
   return hipGetLastError();
 }
