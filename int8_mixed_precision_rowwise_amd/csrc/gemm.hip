@@ -30,6 +30,8 @@
 // of the first operand), column l % 32 (of the second).
 #include "internal.h"
 
+#include <algorithm>
+
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is set by the slab loads
 
 namespace i8mp {
@@ -814,7 +816,8 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
                                                               const float* __restrict__ sa,
                                                               const int8_t* __restrict__ B, int64_t ldb,
                                                               const float* __restrict__ sb,
-                                                              void* __restrict__ Cv, int64_t ldc) {
+                                                              void* __restrict__ Cv, int64_t ldc,
+                                                              int64_t kchunk, int64_t split_stride) {
   constexpr int NW = 2 * WGN, NT = 64 * NW;  // 2 x WGN waves
   constexpr int WM = BM / 2, WN = BN / WGN;
   typedef Mma<FMT> T;
@@ -832,8 +835,26 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  int wg = blockIdx.x, nwg = gridDim.x;
+  if constexpr (OUT_I32) {
+    // Contraction split: the grid holds `splits` copies of the tile grid and
+    // copy s sums contraction indices [s kchunk, (s+1) kchunk) into its own
+    // int32 output plane (Cv + s split_stride).  Unsplit: one copy, kchunk = K.
+    // Consecutive workgroups take consecutive copies, so the 8 XCDs (which
+    // receive workgroups in turn) mostly read disjoint contraction ranges.
+    const int tiles = tiles_m * tiles_n;
+    const int splits = nwg / tiles;
+    const int split = wg % splits;
+    const int64_t k0 = (int64_t)split * kchunk;
+    wg /= splits;
+    nwg = tiles;
+    K = min(kchunk, K - k0);
+    A += A_KMAJOR ? k0 : k0 * lda;
+    B += B_KMAJOR ? k0 : k0 * ldb;
+    Cv = static_cast<int32_t*>(Cv) + split * split_stride;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of(wg, nwg, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   // the epilogue's scales, fetched now so their latency hides under the main loop
@@ -963,9 +984,24 @@ void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t*
   // run while the other waits on its slab-load issue; 128 x 128: 4 waves.
   constexpr int WGN = BM >= 256 ? 4 : 2;
   if (fast)
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0);
   else
     gemm_i8_general<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
+}
+
+// Whether the pipelined kernel can take a BM x BN tiling of this problem.
+// It addresses each operand tile with 32-bit buffer offsets and zero-fills
+// whole 16-byte chunks, so it needs K % 16 == 0 and tile extents below 2^31
+// bytes.  An operand whose contraction runs down its rows is range-checked at
+// its last byte, and the buffer unit checks whole dwords: its output extent
+// must be a multiple of 4 or the last row's final dword would read as zero.
+template <int BM, int BN, bool AK, bool BKM>
+bool pipelined_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t a_ext = AK ? (int64_t)BM * lda : K * lda;
+  const int64_t b_ext = BKM ? (int64_t)BN * ldb : K * ldb;
+  const bool mn_ok = (AK || M % 4 == 0) && (BKM || N % 4 == 0);
+  return K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024 && mn_ok;
 }
 
 template <int BM, int BN, bool AK, bool BKM>
@@ -974,17 +1010,7 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
                int64_t ldc, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
-  // the pipelined kernel addresses each operand tile with 32-bit buffer
-  // offsets and zero-fills whole 16-byte chunks, so it needs K % 16 == 0 and
-  // tile extents below 2^31 bytes
-  const int64_t lim = int64_t(1) << 31;
-  const int64_t a_ext = AK ? (int64_t)BM * lda : K * lda;
-  const int64_t b_ext = BKM ? (int64_t)BN * ldb : K * ldb;
-  // An operand whose contraction runs down its rows is range-checked at its
-  // last byte, and the buffer unit checks whole dwords: its output extent must
-  // be a multiple of 4 or the last row's final dword would read as zero.
-  const bool mn_ok = (AK || M % 4 == 0) && (BKM || N % 4 == 0);
-  const bool fast = K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024 && mn_ok;
+  const bool fast = pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
   // packed stores of adjacent outputs need 16-byte aligned rows
   const uintptr_t c = Ci ? reinterpret_cast<uintptr_t>(Ci) : reinterpret_cast<uintptr_t>(Cb);
   const bool vec = Ci ? (ldc % 4 == 0 && c % 16 == 0) : (ldc % 8 == 0 && c % 16 == 0);
@@ -998,14 +1024,112 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
   return hipGetLastError();
 }
 
+// Tile choice.  A 256 x 256 tile does four times the work of a 128 x 128
+// one at about 1.5x its per-operation rate (fewer LDS and memory bytes per
+// MFMA), so 256 x 256 wins whenever its tiles fill at least half the 256 CUs;
+// below that the 128 x 128 tiling keeps more CUs busy.  (Measured over the
+// Llama-1B and Llama-3-8B layer GEMMs: e.g. 176 big tiles at contraction
+// 32768 run in 330 us against 505 us as 704 small tiles.)
+constexpr int64_t kBigTileMin = 128;
+int64_t big_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+
 template <bool AK, bool BKM>
 hipError_t pick(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const float* sa,
                 const int8_t* B, int64_t ldb, const float* sb, uint16_t* Cb, int32_t* Ci,
                 int64_t ldc, hipStream_t stream) {
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 200)
+  if (big_tiles(M, N) >= kBigTileMin)
     return run<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, stream);
   return run<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, stream);
+}
+
+// ---- contraction split (the linear chains) -------------------------------
+//
+// A problem with fewer 256 x 256 tiles than half the CUs and a long
+// contraction (the grad-weight GEMM of a narrow layer contracts over all
+// tokens) splits the contraction over `splits` copies of the tile grid.  Each
+// copy writes exact int32 partial sums into its own plane; splitk_reduce adds
+// the planes (integer addition: exact and order-free, and every partial sum is
+// a sum over a subset of the contraction, bounded like the full one) and
+// applies the same fp32 epilogue, so the output is bit-identical to the
+// unsplit GEMM's.
+constexpr int64_t kSplitMinK = 1024;  // contraction per split, at least
+
+struct SplitPlan {
+  int splits;      // 1: no split
+  int64_t kchunk;  // contraction per copy (whole 64-deep slabs; the last copy takes the rest)
+  int64_t ldp;     // row pitch of a partial plane (int32 elements, multiple of 4)
+};
+
+template <bool AK, bool BKM>
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+  SplitPlan p{1, K, 0};
+  const int64_t t = big_tiles(M, N);
+  if (t >= kBigTileMin || !pipelined_ok<256, 256, AK, BKM>(M, N, K, lda, ldb)) return p;
+  int64_t s = std::min<int64_t>(256 / t, K / kSplitMinK);
+  if (s < 2) return p;
+  int64_t kc = (K + s - 1) / s;
+  kc = (kc + BK - 1) / BK * BK;
+  s = (K + kc - 1) / kc;  // every copy gets a non-empty range; K % 16 == 0 carries to the last
+  if (s < 2) return p;
+  p.splits = (int)s;
+  p.kchunk = kc;
+  p.ldp = (N + 3) / 4 * 4;
+  return p;
+}
+
+size_t plan_bytes(const SplitPlan& p, int64_t M) {
+  return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)p.ldp * 4 : 0;
+}
+
+// C[m, n] = bf16_RNE(RN32(RN32(float(sum_s P[s][m][n]) * sa[m]) * sb[n]));
+// one thread per 4 adjacent outputs of a row, rows over blockIdx.y.
+__global__ __launch_bounds__(256) void splitk_reduce(const int32_t* __restrict__ P, int64_t ldp,
+                                                     int64_t plane, int splits, int64_t M,
+                                                     int64_t N, const float* __restrict__ sa,
+                                                     const float* __restrict__ sb,
+                                                     __bf16* __restrict__ C, int64_t ldc) {
+  const int64_t n = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (n >= N) return;
+  const bool vec = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 8 == 0 && n + 4 <= N;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    const int32_t* p = P + m * ldp + n;  // columns up to n + 3 < ldp: inside the plane
+    v4i acc = *reinterpret_cast<const v4i*>(p);
+#pragma unroll 8
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4i*>(p + s * plane);
+    const float sam = sa[m];
+    __bf16 h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float y = (float)acc[e];
+      y = y * sam;
+      y = y * (n + e < N ? sb[n + e] : 0.0f);
+      h[e] = (__bf16)y;  // round to nearest even
+    }
+    __bf16* row = C + m * ldc;
+    if (vec) {
+      *reinterpret_cast<uint2*>(row + n) = __builtin_bit_cast(uint2, h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) row[n + e] = h[e];
+    }
+  }
+}
+
+template <bool AK, bool BKM>
+hipError_t run_split(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                     int64_t lda, const float* sa, const int8_t* B, int64_t ldb, const float* sb,
+                     uint16_t* C, int64_t ldc, int32_t* P, hipStream_t stream) {
+  const int64_t tiles = big_tiles(M, N);
+  const int64_t plane = M * p.ldp;
+  gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true><<<dim3((unsigned)(tiles * p.splits)), 512, 0, stream>>>(
+      M, N, K, A, lda, nullptr, B, ldb, nullptr, P, p.ldp, p.kchunk, plane);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((N + 1023) / 1024), (unsigned)std::min<int64_t>(M, 65535));
+  splitk_reduce<<<grid, 256, 0, stream>>>(P, p.ldp, plane, p.splits, M, N, sa, sb,
+                                          reinterpret_cast<__bf16*>(C), ldc);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, bool AK, bool BKM>
@@ -1019,11 +1143,11 @@ hipError_t run_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t ld
   const int8_t* a = reinterpret_cast<const int8_t*>(A);
   const int8_t* b = reinterpret_cast<const int8_t*>(B);
   if (Cf)
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, true, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, true, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc, K, 0);
   else if (vec)
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0);
   else
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0);
   return hipGetLastError();
 }
 
@@ -1031,8 +1155,7 @@ template <bool AK, bool BKM>
 hipError_t pick_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sa,
                     const uint8_t* B, int64_t ldb, const float* sb, uint16_t* C, float* Cf,
                     int64_t ldc, hipStream_t stream) {
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 200) return run_fp8<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
+  if (big_tiles(M, N) >= kBigTileMin) return run_fp8<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
   return run_fp8<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
 }
 
@@ -1054,7 +1177,38 @@ hipError_t launch_gemm_fp8(int layout, int64_t M, int64_t N, int64_t K, const ui
 }
 
 namespace {
+
+SplitPlan plan_for(int layout, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+  switch (layout) {
+    case 0: return plan_split<true, true>(M, N, K, lda, ldb);
+    case 1: return plan_split<true, false>(M, N, K, lda, ldb);
+    default: return plan_split<false, false>(M, N, K, lda, ldb);
+  }
+}
+
 }  // namespace
+
+size_t gemm_split_workspace_bytes(int layout, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                  int64_t ldb) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return plan_bytes(plan_for(layout, M, N, K, lda, ldb), M);
+}
+
+hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                             int64_t lda, const float* sa, const int8_t* B, int64_t ldb,
+                             const float* sb, uint16_t* C, int64_t ldc, void* ws,
+                             hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const SplitPlan p = K > 0 ? plan_for(layout, M, N, K, lda, ldb) : SplitPlan{1, K, 0};
+  if (p.splits < 2 || !ws)
+    return launch_gemm(layout, M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, stream);
+  int32_t* P = static_cast<int32_t*>(ws);
+  switch (layout) {
+    case 0: return run_split<true, true>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, stream);
+    case 1: return run_split<true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, stream);
+    default: return run_split<false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, stream);
+  }
+}
 
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
                        const float* sa, const int8_t* B, int64_t ldb, const float* sb,

@@ -148,7 +148,8 @@ struct Carver {
 struct FwdWs {
   int8_t *qx, *qw;
   float *sx, *sw;
-  void* part;  // slab column maxima of the row-wise passes
+  void* part;   // slab column maxima of the row-wise passes
+  void* split;  // int32 partial planes of a contraction-split GEMM (or null)
 };
 size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   Carver c{static_cast<char*>(ws)};
@@ -162,6 +163,8 @@ size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   const size_t p2 = i8mp::rowwise_colmax_workspace_bytes(N, K);
   if (p2 > part) part = p2;
   w.part = c.take(part);
+  const size_t split = i8mp::gemm_split_workspace_bytes(I8MP_NT, M, N, K, kp, kp);
+  w.split = split ? c.take(split) : nullptr;
   if (out) *out = w;
   return c.used;
 }
@@ -169,7 +172,8 @@ size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
 struct BwdWs {
   int8_t *qdy, *qw, *qx;
   float *sdy, *sw, *sx, *cdy;
-  void* col;  // slab column maxima (column-wise passes, dY's row-wise pass)
+  void* col;    // slab column maxima (column-wise passes, dY's row-wise pass)
+  void* split;  // int32 partial planes of a contraction-split GEMM (or null)
 };
 size_t carve_bwd(void* ws, int64_t M, int64_t N, int64_t K, BwdWs* out) {
   Carver c{static_cast<char*>(ws)};
@@ -187,6 +191,10 @@ size_t carve_bwd(void* ws, int64_t M, int64_t N, int64_t K, BwdWs* out) {
                    i8mp::rowwise_colmax_workspace_bytes(M, N)})
     if (n > col) col = n;
   w.col = c.take(col);
+  size_t split = i8mp::gemm_split_workspace_bytes(I8MP_NN, M, K, N, np, kp);
+  const size_t s2 = i8mp::gemm_split_workspace_bytes(I8MP_TN, N, K, M, np, kp);
+  if (s2 > split) split = s2;
+  w.split = split ? c.take(split) : nullptr;
   if (out) *out = w;
   return c.used;
 }
@@ -372,7 +380,7 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
                  : i8mp::launch_quantize_rowwise(W, N, K, K, w.qw, kp, w.sw, r, opts->seed,
                                                  pass_offset(opts->offset, 1), s);
   if (e == hipSuccess)
-    e = i8mp::launch_gemm(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, nullptr, N, s);
+    e = i8mp::launch_gemm_split(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, N, w.split, s);
   return hip_status(e);
 }
 
@@ -434,7 +442,7 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
                    : i8mp::launch_quantize_colwise(W, N, K, K, w.qw, kp, w.sw, r, seed,
                                                    pass_offset(opts->offset, 3), w.col, s);
     if (e == hipSuccess)
-      e = i8mp::launch_gemm(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, nullptr, K, s);
+      e = i8mp::launch_gemm_split(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, K, w.split, s);
   }
   if (want_dw && e == hipSuccess) {
     // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
@@ -448,7 +456,7 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
                    : i8mp::launch_quantize_colwise(X, M, K, K, w.qx, kp, w.sx, r, seed,
                                                    pass_offset(opts->offset, 5), w.col, s);
     if (e == hipSuccess)
-      e = i8mp::launch_gemm(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, nullptr, K, s);
+      e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, s);
   }
   return hip_status(e);
 }

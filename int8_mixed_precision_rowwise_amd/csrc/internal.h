@@ -58,6 +58,18 @@ hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t
                        const float* sa, const int8_t* B, int64_t ldb, const float* sb,
                        uint16_t* C_bf16, int32_t* C_i32, int64_t ldc, hipStream_t stream);
 
+// The linear chains' GEMM (bf16 output): a problem with few output tiles and
+// a long contraction splits the contraction into int32 partial planes in ws
+// (gemm_split_workspace_bytes; 0 when the problem is not split, and then ws
+// may be null) and reduces them exactly before the epilogue.  Same results as
+// launch_gemm.  lda/ldb as in launch_gemm.
+size_t gemm_split_workspace_bytes(int layout, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                  int64_t ldb);
+hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                             int64_t lda, const float* sa, const int8_t* B, int64_t ldb,
+                             const float* sb, uint16_t* C, int64_t ldc, void* ws,
+                             hipStream_t stream);
+
 hipError_t launch_philox(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
                          hipStream_t stream);
 

@@ -245,7 +245,11 @@ def test_linear_single_layer_full(rounding, rc):
     assert torch.equal(dX2, dX) and torch.equal(dW2, dW)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (17, 24, 40), (130, 264, 72), (1000, 8, 520)])
+# (300, 264, 2048): the forward GEMM splits its contraction in two;
+# (300, 2048, 264): the grad-input GEMM does; (3088, 200, 296): the
+# grad-weight GEMM splits its 3088 tokens in three (1088 + 1088 + 912).
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (17, 24, 40), (130, 264, 72), (1000, 8, 520),
+                                   (300, 264, 2048), (300, 2048, 264), (3088, 200, 296)])
 def test_linear_ragged(M, N, K):
     from workloads import LinearShape, bf16_bits, linear_inputs
     t = linear_inputs(LinearShape("ragged", M, N, K), seed=M + N + K)
@@ -258,6 +262,29 @@ def test_linear_ragged(M, N, K):
     dXo, dWo = oracle.linear_bwd(dYb, Xb, Wb, oracle.SR, 3, 9)
     assert_bf16_equal(tensor_bits(dX), dXo, "dX")
     assert_bf16_equal(tensor_bits(dW), dWo, "dW")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 2048), (3088, 200, 296), (2048, 256, 32768)])
+def test_contraction_split_equals_unsplit_gemm(M, N, K):
+    """The linear chains split the contraction of few-tile GEMMs into int32
+    partial planes; their outputs equal the public unsplit GEMM's on the same
+    codes, bit for bit."""
+    from workloads import LinearShape, linear_inputs
+    t = linear_inputs(LinearShape("split", M, N, K), seed=5, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    Y = i8.linear_fwd(X, W, "rne")
+    dX, dW = i8.linear_bwd(dY, X, W, "rne")
+    qx, sx = i8.quantize_rowwise(X)
+    qw, sw = i8.quantize_rowwise(W)
+    qdy, sdy = i8.quantize_rowwise(dY)
+    qwc, swc = i8.quantize_colwise(W)
+    qdyc, sdyc = i8.quantize_colwise(dY)
+    qxc, sxc = i8.quantize_colwise(X)
+    for got, want, what in ((Y, i8.int8_scaled_mm("NT", qx, sx, qw, sw), "Y"),
+                            (dX, i8.int8_scaled_mm("NN", qdy, sdy, qwc, swc), "dX"),
+                            (dW, i8.int8_scaled_mm("TN", qdyc, sdyc, qxc, sxc), "dW")):
+        torch.cuda.synchronize()
+        assert_bf16_equal(tensor_bits(got), tensor_bits(want), f"{what} {M}x{N}x{K}")
 
 
 def test_repeat_runs_are_byte_identical():

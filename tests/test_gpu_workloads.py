@@ -169,6 +169,13 @@ def test_square_4096_step_with_column_maxima(rounding):
     run_layer(square(4096), rounding, seed=99, colmax=True)
 
 
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_square_2048_step_contraction_split(rounding):
+    """M = N = K = 2048 has 64 big output tiles, so each GEMM of the chains
+    splits its contraction in two int32 partial planes."""
+    run_layer(square(2048), rounding, seed=7, offset=3, colmax=True)
+
+
 @pytest.mark.parametrize("layer", ["llama1b_down_proj", "llama1b_gate_proj"])
 def test_llama1b_layer_with_column_maxima(layer):
     """Llama-1B linears at 32768 tokens (5632-wide rows of X, resp. dY) through
