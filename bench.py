@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the square-sweep and Llama-1B context measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy one 256 MiB buffer with torch (a plain "
                          "copy kernel of known size for scaling HBM byte counters)")
@@ -312,6 +314,9 @@ def main():
         fp8 = {"ms_per_step": round(fp8_ms, 4), "tops": round(3 * gemm_ops / (fp8_ms * 1e-3) / 1e12, 1),
                "note": "linear_fwd_fp8 + linear_bwd_fp8 (allocating their dX, dW), same inputs"}
 
+    sweep = None if args.no_context else context_square_sweep(i8, dev, stream)
+    llama = None if args.no_context else context_llama1b_layers(i8, dev, stream)
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -349,9 +354,96 @@ def main():
         "context_torch_bf16_matmul_tflops": ctx,
         "context_autograd_layer_step_ms": autograd_ms,
         "context_fp8_step": fp8,
+        "context_square_sweep_vs_torch_bf16": sweep,
+        "context_llama1b_7_linears_fwd_bwd": llama,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def _time_us(fn, stream, iters):
+    import torch
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e3
+
+
+def context_square_sweep(i8, dev, stream):
+    """The square GEMM sweep M = N = K in {1024, 2048, 4096} in the three
+    layouts: the scaled INT8 GEMM on quantized Gaussian operands against
+    torch's bf16 matmul on the same bf16 operands (the form of the pages'
+    speed-up tables; quantization not included on either side)."""
+    import torch
+    from workloads import gaussian_bf16
+    out = {}
+    for n in (1024, 2048, 4096):
+        a = gaussian_bf16(n, n, seed=11, device=dev)
+        b = gaussian_bf16(n, n, seed=12, device=dev)
+        y = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+        ops = 2.0 * n * n * n
+        it = 50 if n < 4096 else 20
+        row = {}
+        for lay in ("NT", "NN", "TN"):
+            qa, sa = i8.quantize_rowwise(a) if lay != "TN" else i8.quantize_colwise(a)
+            qb, sb = i8.quantize_rowwise(b) if lay == "NT" else i8.quantize_colwise(b)
+            t8 = _time_us(lambda: i8.int8_scaled_mm(lay, qa, sa, qb, sb, y), stream, it)
+            f16 = {"NT": lambda: torch.matmul(a, b.t(), out=y), "NN": lambda: torch.matmul(a, b, out=y),
+                   "TN": lambda: torch.matmul(a.t(), b, out=y)}[lay]
+            t16 = _time_us(f16, stream, it)
+            row[lay] = {"int8_us": round(t8, 2), "int8_tops": round(ops / t8 / 1e6, 1),
+                        "bf16_us": round(t16, 2), "speedup": round(t16 / t8, 3)}
+        out[str(n)] = row
+    return out
+
+
+def context_llama1b_layers(i8, dev, stream):
+    """The seven Llama-1B decoder linears at 16 x 2048 = 32768 tokens, one
+    training step each through the chains (forward with column maxima, then
+    both gradients: 6 quantize passes + 3 INT8 GEMMs), against the three bf16
+    torch matmuls of the same step (no quantization)."""
+    import torch
+    from workloads import linear_inputs, llama_1b_layers
+    tot8 = tot16 = 0.0
+    ops = 0.0
+    per = {}
+    for shape in llama_1b_layers():
+        M, N, K = shape.M, shape.N, shape.K
+        t = linear_inputs(shape, seed=0, device=dev)
+        X, W, dY = t["X"], t["W"], t["dY"]
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        wsf = torch.empty(i8.linear_workspace_bytes(M, N, K, False), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(i8.linear_workspace_bytes(M, N, K, True), dtype=torch.uint8, device=dev)
+
+        def step8():
+            _, cx, cw = i8.linear_fwd_colmax(X, W, out=Y, workspace=wsf)
+            i8.linear_bwd(dY, X, W, dX=dX, dW=dW, workspace=wsb, colmax_x=cx, colmax_w=cw)
+
+        def step16():
+            torch.matmul(X, W.t(), out=Y)
+            torch.matmul(dY, W, out=dX)
+            torch.matmul(dY.t(), X, out=dW)
+
+        t8 = _time_us(step8, stream, 10)
+        t16 = _time_us(step16, stream, 10)
+        per[shape.name.replace("llama1b_", "")] = {"int8_us": round(t8, 1), "bf16_us": round(t16, 1)}
+        tot8 += t8
+        tot16 += t16
+        ops += 3 * 2.0 * M * N * K
+        del t, X, W, dY, Y, dX, dW, wsf, wsb
+    torch.cuda.empty_cache()
+    return {"int8_us": round(tot8, 1), "bf16_gemms_us": round(tot16, 1),
+            "speedup_vs_bf16": round(tot16 / tot8, 3), "int8_tops": round(ops / tot8 / 1e6, 1),
+            "per_linear": per,
+            "note": "tokens 32768; int8 includes all quantize passes, bf16 is the GEMMs alone"}
 
 
 def cpu_baseline(tokens: int, N: int, K: int, rounding: str):
