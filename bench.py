@@ -315,6 +315,7 @@ def main():
                "note": "linear_fwd_fp8 + linear_bwd_fp8 (allocating their dX, dW), same inputs"}
 
     sweep = None if args.no_context else context_square_sweep(i8, dev, stream)
+    qctx = None if args.no_context else context_quantize_large(i8, dev, stream)
     llama = None if args.no_context else context_llama1b_layers(i8, dev, stream)
 
     if args.copy_calibration:
@@ -355,6 +356,7 @@ def main():
         "context_autograd_layer_step_ms": autograd_ms,
         "context_fp8_step": fp8,
         "context_square_sweep_vs_torch_bf16": sweep,
+        "context_quantize_llama1b_sizes": qctx,
         "context_llama1b_7_linears_fwd_bwd": llama,
         "wall_s_timed": round(wall, 3),
     }
@@ -400,6 +402,59 @@ def context_square_sweep(i8, dev, stream):
             row[lay] = {"int8_us": round(t8, 2), "int8_tops": round(ops / t8 / 1e6, 1),
                         "bf16_us": round(t16, 2), "speedup": round(t16 / t8, 3)}
         out[str(n)] = row
+    return out
+
+
+def context_quantize_large(i8, dev, stream):
+    """The quantize passes at the Llama-1B activation sizes (X 32768 x 2048,
+    dY 32768 x 5632), in algorithmic GB/s (3 bytes per element + 4 per scale)
+    against the 8 TB/s HBM peak, with a torch bf16 copy of the same tensor
+    (4 bytes per element moved) for scale.  Inputs rotate over more bytes than
+    the 256 MB MALL, so every pass reads HBM."""
+    import ctypes
+    import torch
+    from workloads import gaussian_bf16
+    L = i8.lib
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = {}
+    for name, (R, C) in (("X_32768x2048", (32768, 2048)), ("dY_32768x5632", (32768, 5632))):
+        nset = max(2, (3 << 28) // (R * C * 2) + 1)
+        xs = [gaussian_bf16(R, C, seed=20 + i, device=dev) for i in range(nset)]
+        q = torch.empty((R, C), dtype=torch.int8, device=dev)
+        srow = torch.empty(R, device=dev)
+        scol = torch.empty(C, device=dev)
+        cm = torch.empty(C, device=dev)
+        ws = torch.empty(i8.rowwise_colmax_workspace_bytes(R, C), dtype=torch.uint8, device=dev)
+        y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+        k = [0]
+
+        def nxt():
+            k[0] += 1
+            return xs[k[0] % nset]
+
+        def chk(st):
+            if st != 0:
+                raise RuntimeError(f"quantize context: status {st}")
+
+        passes = {
+            "row": lambda: chk(L.i8mp_quantize_rowwise(P(nxt()), R, C, C, P(q), C, P(srow), 0, 0, 0, sp)),
+            "row_with_colmax": lambda: chk(L.i8mp_quantize_rowwise_colmax(
+                P(nxt()), R, C, C, P(q), C, P(srow), P(cm), 0, 0, 0, P(ws), ws.numel(), sp)),
+            "col_given_colmax": lambda: chk(L.i8mp_quantize_colwise_given_colmax(
+                P(nxt()), R, C, C, P(cm), P(q), C, P(scol), 0, 0, 0, sp)),
+        }
+        row = {}
+        for pn, fn in passes.items():
+            us = _time_us(fn, stream, 20)
+            nscale = R if pn.startswith("row") else C
+            gbs = (3.0 * R * C + 4.0 * nscale) / us / 1e3
+            row[pn] = {"us": round(us, 1), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        us = _time_us(lambda: y.copy_(nxt()), stream, 20)
+        row["torch_bf16_copy"] = {"us": round(us, 1), "gbs": round(4.0 * R * C / us / 1e3, 1)}
+        out[name] = row
+        del xs, q, y, ws
+    torch.cuda.empty_cache()
     return out
 
 
