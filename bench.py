@@ -143,7 +143,7 @@ def main():
     names = ["quant_row_X", "quant_row_W", "gemm_NT_fwd", "quant_row_dY", "quant_col_W",
              "gemm_NN_dgrad", "quant_col_dY", "quant_col_X", "gemm_TN_wgrad"]
 
-    def launches(X, W, dY, step):
+    def launches(X, W, dY, step, r=r):
         off = step << 44
         ro = lambda j: off + (j << 40)  # noqa: E731  (per-pass Philox offsets)
         return [
@@ -314,6 +314,27 @@ def main():
         fp8 = {"ms_per_step": round(fp8_ms, 4), "tops": round(3 * gemm_ops / (fp8_ms * 1e-3) / 1e12, 1),
                "note": "linear_fwd_fp8 + linear_bwd_fp8 (allocating their dX, dW), same inputs"}
 
+    # context: the same step with the other rounding mode (stochastic rounding
+    # draws Philox4x32-10 words in every quantize pass)
+    other = 1 - r
+    plans_other = [launches(*sets[s], 0, r=other) for s in range(args.sets)]
+    for i in range(args.warmup):
+        for f in plans_other[i % args.sets]:
+            f()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        for f in plans_other[i % args.sets]:
+            if f() != 0:
+                raise RuntimeError("step with the other rounding mode failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    other_ms = e0.elapsed_time(e1) / args.steps
+    rounding_ctx = {"rounding": "sr" if other == 1 else "rne", "ms_per_step": round(other_ms, 4),
+                    "tops": round(3 * gemm_ops / (other_ms * 1e-3) / 1e12, 1),
+                    "time_vs_this_step": round(other_ms / step_ms, 3)}
+
     sweep = None if args.no_context else context_square_sweep(i8, dev, stream)
     qctx = None if args.no_context else context_quantize_large(i8, dev, stream)
     llama = None if args.no_context else context_llama1b_layers(i8, dev, stream)
@@ -355,6 +376,7 @@ def main():
         "context_torch_bf16_matmul_tflops": ctx,
         "context_autograd_layer_step_ms": autograd_ms,
         "context_fp8_step": fp8,
+        "context_other_rounding_step": rounding_ctx,
         "context_square_sweep_vs_torch_bf16": sweep,
         "context_quantize_llama1b_sizes": qctx,
         "context_llama1b_7_linears_fwd_bwd": llama,

@@ -7,11 +7,13 @@
 // or the raw int32 accumulators.
 //
 // Structure: one workgroup per BM x BN output tile, K in slabs of 64 bytes
-// through LDS, v_mfma_i32_32x32x32_i8 on 32 x 32 blocks.  Two kernels: a
-// pipelined one (slabs loaded memory -> LDS by the buffer unit, several slabs
-// in flight; 8 waves for 256 x 256 tiles, 4 for 128 x 128) for contraction
+// through LDS.  Two kernels: a pipelined one (slabs loaded memory -> LDS by
+// the buffer unit, several slabs in flight; v_mfma_i32_16x16x64_i8 on 16 x 16
+// blocks; 8 waves for 256 x 256 tiles, 4 for 128 x 128) for contraction
 // lengths that are multiples of 16, and a register-staged double-buffered one
-// (4 waves) for every other shape.
+// (4 waves, v_mfma_i32_32x32x32_i8 on 32 x 32 blocks) for every other shape.
+// The linear chains may split a long contraction of a few-tile output over
+// several copies of the tile grid (int32 partial planes, then splitk_reduce).
 // An operand whose contraction dimension is contiguous in memory (A in NT and
 // NN, B in NT) is staged K-major and fed to the MFMA with ds_read_b128; an
 // operand whose contraction runs down its rows (B in NN and TN, A in TN) is

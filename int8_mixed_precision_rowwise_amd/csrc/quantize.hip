@@ -798,9 +798,12 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
 }
 
 // Row-wise with column maxima: 16 waves per block for rows of up to 4096
-// elements, 8 up to 6144 and 4 beyond (per-lane state and LDS regions grow
-// with the row), about 256 blocks, each a band of whole rows.  Rows longer than 14336 elements (the block-per-row
-// kernel) get their column maxima from a separate column-maxima pass.
+// elements (8 for rows of 3585 .. 4096 elements with stochastic rounding or a
+// range-checked tail), 8 up to 6144 and 4 beyond (per-lane state and LDS
+// regions grow with the row), about 256 blocks, each a band of whole rows
+// (a multiple of 16 rows, so the bands do not depend on the wave count).
+// Rows longer than 14336 elements (the block-per-row kernel) get their column
+// maxima from a separate column-maxima pass.
 struct RowColmaxPlan {
   bool fused;
   int waves;
@@ -832,18 +835,23 @@ template <int NV>
 void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int64_t cols,
                    int64_t ldx, int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
                    uint64_t offset, uint16_t* part, hipStream_t stream) {
-  constexpr int WAVES = NV >= 16 ? 4 : (NV > 8 ? 8 : 16);  // LDS: WAVES x NV KiB of column maxima
+  // LDS: WAVES x NV KiB of column maxima.  16 waves (at most 128 VGPRs per
+  // lane) hold the range-check-free round-to-nearest body of rows of 4096;
+  // stochastic rounding (two Philox blocks per chunk) and range-checked rows of
+  // 8 chunks per lane need more registers and take 8 waves instead of spilling.
+  constexpr int WAVES = NV >= 16 ? 4 : (NV > 8 ? 8 : 16);
+  constexpr int WAVES_WIDE = NV >= 16 ? 4 : (NV >= 8 ? 8 : 16);
   const dim3 grid((unsigned)p.slabs);
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if (a4)
-      quant_rows_colmax<NV, WAVES, true, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+      quant_rows_colmax<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
     else
-      quant_rows_colmax<NV, WAVES, true, false><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+      quant_rows_colmax<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   } else if (cols == NV * 512) {
     quant_rows_colmax<NV, WAVES, false, true, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   } else {
-    quant_rows_colmax<NV, WAVES, false, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+    quant_rows_colmax<NV, WAVES_WIDE, false, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   }
 }
 

@@ -119,6 +119,43 @@ def test_linear_validation_and_workspace():
     assert bwd(dY, X, W, None, None, 64, 32, 48, ctypes.byref(o), None, 0, None) == 0
 
 
+def _split_planes_bytes(M, N, K):
+    """Bytes of int32 partial planes the forward chain's NT GEMM (both operands
+    K-contiguous, rows padded to 16 bytes) takes: the output has fewer than 128
+    tiles of 256 x 256 and the contraction is a multiple of 16, so it splits
+    into min(256 // tiles, K // 1024) ranges of whole 64-deep slabs."""
+    tiles = -(-M // 256) * -(-N // 256)
+    if tiles >= 128 or K % 16 or K == 0:
+        return 0
+    s = min(256 // tiles, K // 1024)
+    if s < 2:
+        return 0
+    kc = -(-K // s)
+    kc = -(-kc // 64) * 64
+    s = -(-K // kc)
+    if s < 2:
+        return 0
+    return s * M * (-(-N // 4) * 4) * 4
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 256, 32768), (300, 264, 2048), (4096, 4096, 4096),
+                                   (256, 512, 512), (64, 32, 48), (1000, 8, 4096)])
+def test_linear_workspace_holds_contraction_split_planes(M, N, K):
+    """The forward chain's workspace: int8 codes and scales of X and W, the
+    row passes' slab maxima, and the split GEMM's int32 partial planes, each
+    region 256-byte aligned."""
+    up = lambda n: -(-n // 256) * 256  # noqa: E731
+    kp = -(-K // 16) * 16
+    part = max(L.i8mp_quantize_rowwise_colmax_workspace_bytes(M, K),
+               L.i8mp_quantize_rowwise_colmax_workspace_bytes(N, K))
+    want = up(M * kp) + up(N * kp) + up(4 * M) + up(4 * N) + part + up(_split_planes_bytes(M, N, K))
+    assert L.i8mp_linear_workspace_bytes(M, N, K, 0) == want
+    if (M, N, K) == (2048, 256, 32768):  # 8 tiles: 32 ranges of 1024
+        assert _split_planes_bytes(M, N, K) == 32 * 2048 * 256 * 4
+    if (M, N, K) == (4096, 4096, 4096):  # 256 tiles: no split
+        assert _split_planes_bytes(M, N, K) == 0
+
+
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
     """The package refuses to import without its library instead of falling back."""
     import importlib
