@@ -700,6 +700,107 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
   }
 }
 
+// Row-wise with column maxima for rows longer than 14336 elements (a row no
+// longer fits in one wave's registers).  The tensor is cut into tiles of a
+// band of rows by a segment of kLongSeg columns; a block of 8 waves walks the
+// band's rows, one row segment per wave at a time (8 chunks per lane).
+// rows_long_stats reads each tile once and writes the absmax of every row
+// segment (bf16 bit patterns, [rows][segments]) and the band's column maxima
+// (one slab per band, as quant_rows_colmax does).  rows_long_quant reads the
+// tile again, takes each row's absmax as the maximum of its segment maxima
+// (order-free, so exact) and quantizes with the same arithmetic as every other
+// row-wise pass.  Two reads of the tensor instead of three (row absmax, row
+// quantize, column maxima).
+constexpr int kLongSeg = 4096;
+constexpr int kLongThreads = 512;
+constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kLongNV = kLongSeg / 512;  // 16-byte chunks per lane and row segment
+
+__device__ __forceinline__ void load_segment(uint4 (&v)[kLongNV], const uint16_t* __restrict__ xr,
+                                             int64_t c_begin, int64_t cols, int lane) {
+#pragma unroll
+  for (int i = 0; i < kLongNV; ++i) {
+    const int64_t c0 = c_begin + (int64_t)(i * 64 + lane) * 8;
+    if (c0 < cols) {
+      v[i] = *reinterpret_cast<const uint4*>(xr + c0);
+      if (c0 + 8 > cols) v[i] = keep_first(v[i], (int)(cols - c0));
+    } else {
+      v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kLongThreads) void rows_long_stats(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int64_t rows_per_band,
+    uint16_t* __restrict__ segmax, int64_t nseg, uint16_t* __restrict__ part, int64_t part_ld) {
+  __shared__ uint4 red[kLongWaves][kLongNV * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seg = blockIdx.x, band = blockIdx.y;
+  const int64_t c_begin = seg * kLongSeg;
+  const int64_t r_begin = band * rows_per_band;
+  const int64_t r_end = min(rows, r_begin + rows_per_band);
+  us2 cm[kLongNV][4];
+#pragma unroll
+  for (int i = 0; i < kLongNV; ++i) cm[i][0] = cm[i][1] = cm[i][2] = cm[i][3] = us2{0, 0};
+  for (int64_t r = r_begin + wave; r < r_end; r += kLongWaves) {
+    uint4 v[kLongNV];
+    load_segment(v, x + r * ldx, c_begin, cols, lane);
+    us2 m2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < kLongNV; ++i) {
+      m2 = absmax_bits(m2, v[i]);
+      max_chunk(cm[i], v[i]);
+    }
+    const uint32_t amax = wave_max_u32<false>(max((uint32_t)m2.x, (uint32_t)m2.y));
+    if (lane == 0) segmax[r * nseg + seg] = (uint16_t)amax;
+  }
+#pragma unroll
+  for (int i = 0; i < kLongNV; ++i) red[wave][i * 64 + lane] = pack_max(cm[i]);
+  __syncthreads();
+  // one chunk of the segment per thread: fold the 8 waves, write the band's slab
+  const int j = threadIdx.x;
+  const int64_t c0 = c_begin + (int64_t)j * 8;
+  if (c0 < cols) {
+    us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+    for (int w = 0; w < kLongWaves; ++w) max_chunk(m, red[w][j]);
+    *reinterpret_cast<uint4*>(part + band * part_ld + c0) = pack_max(m);
+  }
+}
+
+template <bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(kLongThreads) void rows_long_quant(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int64_t rows_per_band,
+    const uint16_t* __restrict__ segmax, int64_t nseg, int8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ scale, uint64_t seed, uint64_t offset) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seg = blockIdx.x, band = blockIdx.y;
+  const int64_t c_begin = seg * kLongSeg;
+  const int64_t r_begin = band * rows_per_band;
+  const int64_t r_end = min(rows, r_begin + rows_per_band);
+  for (int64_t r = r_begin + wave; r < r_end; r += kLongWaves) {
+    uint4 v[kLongNV];
+    load_segment(v, x + r * ldx, c_begin, cols, lane);
+    uint32_t m = 0;
+    for (int64_t k = lane; k < nseg; k += 64) m = max(m, (uint32_t)segmax[r * nseg + k]);
+    const GroupScale g = make_scale<0>(__builtin_amdgcn_readfirstlane(wave_max_u32<false>(m)));
+    if (seg == 0 && lane == 0) scale[r] = g.s;
+    int8_t* qr = q + r * ldq;
+#pragma unroll
+    for (int i = 0; i < kLongNV; ++i) {
+      const int64_t c0 = c_begin + (int64_t)(i * 64 + lane) * 8;
+      if (c0 >= cols) continue;
+      const uint64_t e0 = (uint64_t)(r * cols + c0);
+      const uint2 codes = g.mode == 1 ? quantize_chunk<SR, ALIGNED4, false, 1>(v[i], &g, seed, offset, e0)
+                                      : quantize_chunk<SR, ALIGNED4, false, -1>(v[i], &g, seed, offset, e0);
+      if (c0 + 8 <= cols)
+        *reinterpret_cast<uint2*>(qr + c0) = codes;
+      else
+        store_partial(qr + c0, codes, (int)(cols - c0));
+    }
+  }
+}
+
 // fp32 column maxima from slab maxima.  A block of 8 waves covers 32
 // columns: lane l reads the 16-byte chunk l % 4 (8 columns) of slab l / 4 of
 // each group of 16 slabs, so one load instruction of a wave covers 16 slabs;
@@ -802,12 +903,14 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
 // range-checked tail), 8 up to 6144 and 4 beyond (per-lane state and LDS
 // regions grow with the row), about 256 blocks, each a band of whole rows
 // (a multiple of 16 rows, so the bands do not depend on the wave count).
-// Rows longer than 14336 elements (the block-per-row kernel) get their column
-// maxima from a separate column-maxima pass.
+// Rows longer than 14336 elements go through rows_long_stats and
+// rows_long_quant (bands of rows by segments of 4096 columns).
 struct RowColmaxPlan {
   bool fused;
   int waves;
   int64_t rows_per_block, slabs, part_ld;
+  int64_t nseg;        // long rows: column segments of kLongSeg
+  size_t part_bytes;   // slab maxima; the segment maxima ([rows][nseg] bf16 bits) follow
 };
 
 RowColmaxPlan rcm_plan(int64_t rows, int64_t cols) {
@@ -822,12 +925,18 @@ RowColmaxPlan rcm_plan(int64_t rows, int64_t cols) {
     rpb = (rpb + p.waves - 1) / p.waves * p.waves;
     p.rows_per_block = max(rpb, (int64_t)p.waves);
     p.slabs = (rows + p.rows_per_block - 1) / p.rows_per_block;
+    p.nseg = 0;
   } else {
-    const ColPlan c = col_plan(rows, cols);
-    p.waves = kColWaves;
-    p.rows_per_block = c.rows_per_slab;
-    p.slabs = c.slabs;
+    // bands of whole rows by segments of kLongSeg columns: at most 128 bands
+    // (the slab maxima stay small next to the tensor), a multiple of 8 rows
+    p.waves = kLongWaves;
+    p.nseg = (cols + kLongSeg - 1) / kLongSeg;
+    int64_t rpb = (rows + 127) / 128;
+    rpb = (rpb + kLongWaves - 1) / kLongWaves * kLongWaves;
+    p.rows_per_block = max(rpb, (int64_t)kLongWaves);
+    p.slabs = (rows + p.rows_per_block - 1) / p.rows_per_block;
   }
+  p.part_bytes = (size_t)(max(p.slabs, (int64_t)1) * p.part_ld * 2);
   return p;
 }
 
@@ -976,7 +1085,8 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
 
 size_t rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols) {
   const RowColmaxPlan p = rcm_plan(rows, cols);
-  return (size_t)(max(p.slabs, (int64_t)1) * p.part_ld * 2);
+  if (p.fused) return p.part_bytes;
+  return (p.part_bytes + 255) / 256 * 256 + (size_t)(max(rows, (int64_t)1) * p.nseg * 2);
 }
 
 hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
@@ -1004,11 +1114,17 @@ hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64
       else
         launch_rcm_nv<28>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
     } else {
-      const hipError_t e = launch_quantize_rowwise(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
-      if (e != hipSuccess) return e;
-      const ColPlan c = col_plan(rows, cols);
-      col_absmax_partial<<<dim3((unsigned)c.col_tiles, (unsigned)c.slabs), kColThreads, 0, stream>>>(
-          x, rows, cols, ldx, c.rows_per_slab, part, c.part_ld);
+      uint16_t* segmax = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + (p.part_bytes + 255) / 256 * 256);
+      const dim3 grid((unsigned)p.nseg, (unsigned)p.slabs);
+      rows_long_stats<<<grid, kLongThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, segmax,
+                                                         p.nseg, part, p.part_ld);
+      const bool a4 = (cols % 4) == 0;
+      if (round == 1 && a4)
+        rows_long_quant<true, true><<<grid, kLongThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, segmax, p.nseg, q, ldq, scale, seed, offset);
+      else if (round == 1)
+        rows_long_quant<true, false><<<grid, kLongThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, segmax, p.nseg, q, ldq, scale, seed, offset);
+      else
+        rows_long_quant<false, true><<<grid, kLongThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, segmax, p.nseg, q, ldq, scale, seed, offset);
     }
   }
   colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(

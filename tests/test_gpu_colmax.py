@@ -3,7 +3,8 @@
 * Row-wise quantization that also reports column maxima: codes and scales as
   the oracle's row-wise pass, maxima as the oracle's column maxima, over
   widths that take every kernel variant (one chunk per lane up to 28, the
-  4-wave variant above 6144 columns, and the separate-pass path past 14336),
+  4-wave variant above 6144 columns, and the banded two-pass path past 14336:
+  one band and many, a partial last 4096-column segment, odd widths),
   padded leading dimensions, canary bytes after every output row.
 * Column-wise quantization given those maxima: as the oracle's column-wise
   pass.
@@ -28,7 +29,7 @@ if not torch.cuda.is_available():
 ROUNDINGS = [("rne", oracle.RNE), ("sr", oracle.SR)]
 SHAPES = [(1, 1), (3, 17), (9, 255), (40, 513), (257, 2048), (100, 4096), (5000, 512),
           (33, 5000), (17, 6144), (21, 6152), (3000, 6200), (12, 8192), (9, 14336),
-          (600, 14336), (3, 16385), (2, 30001)]
+          (600, 14336), (3, 16385), (2, 30001), (300, 16392), (1030, 20001)]
 
 
 def same_f32(t: torch.Tensor, want: np.ndarray, what: str):
