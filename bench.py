@@ -9,10 +9,14 @@ M = N = K = 4096 (X ~ N(0,1) with outlier channels, W ~ N(0,0.02),
 dY ~ N(0,1e-3), bf16, synthetic, seeded).
 
 Every launch goes through the C ABI on torch's current stream.  Two timed
-regions run the same steps: the first with nothing between the launches gives
-the step time (`value`, `ms_per_step`); the second records a HIP event on that
-stream between every two launches and gives each kernel's duration
-(`breakdown`, `roofline`).  Recording an event costs a few microseconds of
+regions run the same steps.  The first runs them as the library's linear
+chains (i8mp_linear_fwd_colmax, i8mp_linear_bwd_colmax: the forward's two
+row-wise passes share one launch, the backward's two column-wise passes too)
+with nothing between the launches, and gives the step time (`value`,
+`ms_per_step`).  The second runs the same computation as separate primitive
+launches with a HIP event on that stream between every two, and gives each
+kernel's duration (`breakdown`, `roofline`).  Both produce the same bytes
+(checked before timing).  Recording an event costs a few microseconds of
 stream time, which is why the step time comes from the event-free region.
 Inputs rotate over several sets (more bytes than the 256 MB MALL) so every
 step reads its operands from HBM.
@@ -143,7 +147,7 @@ def main():
     names = ["quant_row_X", "quant_row_W", "gemm_NT_fwd", "quant_row_dY", "quant_col_W",
              "gemm_NN_dgrad", "quant_col_dY", "quant_col_X", "gemm_TN_wgrad"]
 
-    def launches(X, W, dY, step, r=r):
+    def launches(X, W, dY, step):
         off = step << 44
         ro = lambda j: off + (j << 40)  # noqa: E731  (per-pass Philox offsets)
         return [
@@ -190,16 +194,40 @@ def main():
     if not ok:
         raise RuntimeError("primitive chain differs from linear_fwd_colmax/linear_bwd")
 
+    # The step as the library runs it: i8mp_linear_fwd_colmax then
+    # i8mp_linear_bwd_colmax (the forward's two row-wise passes share one
+    # launch, the backward's two column-wise passes too: 9 launches).  Same
+    # kernels' arithmetic as the 12 primitive launches above, same outputs.
+    ws_fwd = torch.empty(L.i8mp_linear_workspace_bytes(M, N, K, 0), dtype=torch.uint8, device=dev)
+    ws_bwd = torch.empty(L.i8mp_linear_workspace_bytes(M, N, K, 1), dtype=torch.uint8, device=dev)
+
+    def chain_step(i, rr=r):
+        X, W, dY = sets[i % args.sets]
+        o = i8._Opts(rr, seed, 0)
+        st = L.i8mp_linear_fwd_colmax(p(X), p(W), p(Y), M, N, K, ctypes.byref(o), p(cX), p(cW), p(ws_fwd),
+                                      ws_fwd.numel(), sp)
+        st = st or L.i8mp_linear_bwd_colmax(p(dY), p(X), p(W), p(dX), p(dW), M, N, K, ctypes.byref(o),
+                                            p(cX), p(cW), p(ws_bwd), ws_bwd.numel(), sp)
+        if st != 0:
+            raise RuntimeError(f"linear chain step failed with status {st}")
+
+    chain_step(0)
+    if not (torch.equal(Y.view(torch.int16), Yc.view(torch.int16))
+            and torch.equal(dX.view(torch.int16), dXc.view(torch.int16))
+            and torch.equal(dW.view(torch.int16), dWc.view(torch.int16))):
+        raise RuntimeError("the chains' step differs from the primitive launches")
+
     for i in range(args.warmup):
+        chain_step(i)
         run_step(i)
-    # timed region 1: the step time, nothing between the launches
+    # timed region 1: the step time through the chains, nothing between the launches
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(args.steps):
-        run_step(i)
+        chain_step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -317,17 +345,13 @@ def main():
     # context: the same step with the other rounding mode (stochastic rounding
     # draws Philox4x32-10 words in every quantize pass)
     other = 1 - r
-    plans_other = [launches(*sets[s], 0, r=other) for s in range(args.sets)]
     for i in range(args.warmup):
-        for f in plans_other[i % args.sets]:
-            f()
+        chain_step(i, other)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        for f in plans_other[i % args.sets]:
-            if f() != 0:
-                raise RuntimeError("step with the other rounding mode failed")
+        chain_step(i, other)
     e1.record(stream)
     torch.cuda.synchronize()
     other_ms = e0.elapsed_time(e1) / args.steps

@@ -148,8 +148,8 @@ struct Carver {
 struct FwdWs {
   int8_t *qx, *qw;
   float *sx, *sw;
-  void* part;   // slab column maxima of the row-wise passes
-  void* split;  // int32 partial planes of a contraction-split GEMM (or null)
+  void *part_x, *part_w;  // slab column maxima of the two row-wise passes
+  void* split;            // int32 partial planes of a contraction-split GEMM (or null)
 };
 size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   Carver c{static_cast<char*>(ws)};
@@ -159,10 +159,8 @@ size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   w.qw = static_cast<int8_t*>(c.take((size_t)(N * kp)));
   w.sx = static_cast<float*>(c.take((size_t)M * 4));
   w.sw = static_cast<float*>(c.take((size_t)N * 4));
-  size_t part = i8mp::rowwise_colmax_workspace_bytes(M, K);
-  const size_t p2 = i8mp::rowwise_colmax_workspace_bytes(N, K);
-  if (p2 > part) part = p2;
-  w.part = c.take(part);
+  w.part_x = c.take(i8mp::rowwise_colmax_workspace_bytes(M, K));
+  w.part_w = c.take(i8mp::rowwise_colmax_workspace_bytes(N, K));
   const size_t split = i8mp::gemm_split_workspace_bytes(I8MP_NT, M, N, K, kp, kp);
   w.split = split ? c.take(split) : nullptr;
   if (out) *out = w;
@@ -369,16 +367,22 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
   const hipStream_t s = as_stream(stream);
   const int64_t kp = pad16(K);
   const int r = opts->round;
-  hipError_t e =
-      colmax_x ? i8mp::launch_quantize_rowwise_colmax(X, M, K, K, w.qx, kp, w.sx, colmax_x, r, opts->seed,
-                                                      pass_offset(opts->offset, 0), w.part, s)
-               : i8mp::launch_quantize_rowwise(X, M, K, K, w.qx, kp, w.sx, r, opts->seed,
-                                               pass_offset(opts->offset, 0), s);
-  if (e == hipSuccess)
-    e = colmax_w ? i8mp::launch_quantize_rowwise_colmax(W, N, K, K, w.qw, kp, w.sw, colmax_w, r, opts->seed,
-                                                        pass_offset(opts->offset, 1), w.part, s)
-                 : i8mp::launch_quantize_rowwise(W, N, K, K, w.qw, kp, w.sw, r, opts->seed,
-                                                 pass_offset(opts->offset, 1), s);
+  hipError_t e = hipSuccess;
+  if (colmax_x && colmax_w) {  // both row-wise passes (same width K) in one launch
+    e = i8mp::launch_quantize_rowwise_colmax_pair(X, M, K, w.qx, kp, w.sx, colmax_x, pass_offset(opts->offset, 0),
+                                                  w.part_x, W, N, K, w.qw, kp, w.sw, colmax_w,
+                                                  pass_offset(opts->offset, 1), w.part_w, K, r, opts->seed, s);
+  } else {
+    e = colmax_x ? i8mp::launch_quantize_rowwise_colmax(X, M, K, K, w.qx, kp, w.sx, colmax_x, r, opts->seed,
+                                                        pass_offset(opts->offset, 0), w.part_x, s)
+                 : i8mp::launch_quantize_rowwise(X, M, K, K, w.qx, kp, w.sx, r, opts->seed,
+                                                 pass_offset(opts->offset, 0), s);
+    if (e == hipSuccess)
+      e = colmax_w ? i8mp::launch_quantize_rowwise_colmax(W, N, K, K, w.qw, kp, w.sw, colmax_w, r, opts->seed,
+                                                          pass_offset(opts->offset, 1), w.part_w, s)
+                   : i8mp::launch_quantize_rowwise(W, N, K, K, w.qw, kp, w.sw, r, opts->seed,
+                                                   pass_offset(opts->offset, 1), s);
+  }
   if (e == hipSuccess)
     e = i8mp::launch_gemm_split(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, N, w.split, s);
   return hip_status(e);
@@ -446,15 +450,21 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
   }
   if (want_dw && e == hipSuccess) {
     // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
-    e = dy_colmax ? i8mp::launch_quantize_colwise_given(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, r, seed,
-                                                        pass_offset(opts->offset, 4), s)
-                  : i8mp::launch_quantize_colwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
-                                                  pass_offset(opts->offset, 4), w.col, s);
-    if (e == hipSuccess)
-      e = colmax_x ? i8mp::launch_quantize_colwise_given(X, M, K, K, colmax_x, w.qx, kp, w.sx, r, seed,
-                                                         pass_offset(opts->offset, 5), s)
-                   : i8mp::launch_quantize_colwise(X, M, K, K, w.qx, kp, w.sx, r, seed,
-                                                   pass_offset(opts->offset, 5), w.col, s);
+    if (dy_colmax && colmax_x) {  // both column-wise passes in one launch
+      e = i8mp::launch_quantize_colwise_given_pair(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, pass_offset(opts->offset, 4),
+                                                   X, M, K, K, colmax_x, w.qx, kp, w.sx, pass_offset(opts->offset, 5),
+                                                   r, seed, s);
+    } else {
+      e = dy_colmax ? i8mp::launch_quantize_colwise_given(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, r, seed,
+                                                          pass_offset(opts->offset, 4), s)
+                    : i8mp::launch_quantize_colwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
+                                                    pass_offset(opts->offset, 4), w.col, s);
+      if (e == hipSuccess)
+        e = colmax_x ? i8mp::launch_quantize_colwise_given(X, M, K, K, colmax_x, w.qx, kp, w.sx, r, seed,
+                                                           pass_offset(opts->offset, 5), s)
+                     : i8mp::launch_quantize_colwise(X, M, K, K, w.qx, kp, w.sx, r, seed,
+                                                     pass_offset(opts->offset, 5), w.col, s);
+    }
     if (e == hipSuccess)
       e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, s);
   }

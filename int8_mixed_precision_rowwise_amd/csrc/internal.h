@@ -35,6 +35,23 @@ hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_
                                          float* scale, int round, uint64_t seed, uint64_t offset,
                                          hipStream_t stream);
 
+// Two tensors of the same width quantized row-wise with column maxima in one
+// launch (and one finalize); each has its own workspace of
+// rowwise_colmax_workspace_bytes(rows, cols).  Same results as two calls.
+hipError_t launch_quantize_rowwise_colmax_pair(
+    const uint16_t* xa, int64_t rows_a, int64_t ldxa, int8_t* qa, int64_t ldqa, float* scale_a,
+    float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
+    int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
+    void* ws_b, int64_t cols, int round, uint64_t seed, hipStream_t stream);
+
+// Two tensors quantized column-wise with their column maxima given, in one
+// launch.  Same results as two calls.
+hipError_t launch_quantize_colwise_given_pair(
+    const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, const float* colmax_a,
+    int8_t* qa, int64_t ldqa, float* scale_a, uint64_t offset_a, const uint16_t* xb,
+    int64_t rows_b, int64_t cols_b, int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb,
+    float* scale_b, uint64_t offset_b, int round, uint64_t seed, hipStream_t stream);
+
 // FP8 (E4M3) quantization, round to nearest: codes q8 in x's layout,
 // scales per row (row-wise) or per column (column-wise, slab maxima in ws,
 // colwise_workspace_bytes).

@@ -630,24 +630,60 @@ __device__ __forceinline__ void given_band(const uint16_t* __restrict__ x, int64
   }
 }
 
-template <bool SR, bool ALIGNED4, int FMT = 0>
-__global__ __launch_bounds__(kColThreads) void quant_cols_given(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-    const float* __restrict__ colmax, float* __restrict__ scale, int8_t* __restrict__ q,
-    int64_t ldq, uint64_t seed, uint64_t offset) {
+template <bool SR, bool ALIGNED4, int FMT>
+__device__ __forceinline__ void cols_given_block(const uint16_t* __restrict__ x, int64_t rows,
+                                                 int64_t cols, int64_t ldx,
+                                                 const float* __restrict__ colmax,
+                                                 float* __restrict__ scale, int8_t* __restrict__ q,
+                                                 int64_t ldq, uint64_t seed, uint64_t offset,
+                                                 int64_t band, int64_t group) {
   const int lane = threadIdx.x & 63;
-  const int64_t tile = (int64_t)blockIdx.y * kColWaves + (threadIdx.x >> 6);
+  const int64_t tile = group * kColWaves + (threadIdx.x >> 6);
   if (tile * kColTile >= cols) return;  // a wave past the last tile
   const int64_t c0 = tile * kColTile + lane * 8;
-  const int64_t r_begin = (int64_t)blockIdx.x * kColBand;
+  const int64_t r_begin = band * kColBand;
   const int64_t nrows = min((int64_t)kColBand, rows - r_begin);  // 0 only when rows == 0
-  const bool store_scales = blockIdx.x == 0;
+  const bool store_scales = band == 0;
   if (nrows == kColBand && (tile + 1) * kColTile <= cols)
     given_band<true, SR, ALIGNED4, FMT>(x, cols, ldx, colmax, scale, q, ldq, seed, offset, r_begin,
                                         nrows, c0, store_scales);
   else
     given_band<false, SR, ALIGNED4, FMT>(x, cols, ldx, colmax, scale, q, ldq, seed, offset, r_begin,
                                          nrows, c0, store_scales);
+}
+
+template <bool SR, bool ALIGNED4, int FMT = 0>
+__global__ __launch_bounds__(kColThreads) void quant_cols_given(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    const float* __restrict__ colmax, float* __restrict__ scale, int8_t* __restrict__ q,
+    int64_t ldq, uint64_t seed, uint64_t offset) {
+  cols_given_block<SR, ALIGNED4, FMT>(x, rows, cols, ldx, colmax, scale, q, ldq, seed, offset,
+                                      blockIdx.x, blockIdx.y);
+}
+
+// Two tensors in one launch (a linear layer's grad-weight GEMM quantizes dY
+// and X column-wise): blockIdx.x in [0, a.bands) takes a's row bands, the rest
+// b's; blockIdx.y walks the column groups of the wider of the two (waves past
+// a tensor's last column tile return).  Results as two separate launches.
+struct ColGivenJob {
+  const uint16_t* x;
+  int64_t rows, cols, ldx;
+  const float* colmax;
+  float* scale;
+  int8_t* q;
+  int64_t ldq;
+  uint64_t offset;
+  int64_t bands;
+};
+
+template <bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(kColThreads) void quant_cols_given2(ColGivenJob a, ColGivenJob b,
+                                                                 uint64_t seed) {
+  const bool second = (int64_t)blockIdx.x >= a.bands;
+  const ColGivenJob j = second ? b : a;
+  const int64_t band = second ? (int64_t)blockIdx.x - a.bands : (int64_t)blockIdx.x;
+  cols_given_block<SR, ALIGNED4, 0>(j.x, j.rows, j.cols, j.ldx, j.colmax, j.scale, j.q, j.ldq, seed,
+                                    j.offset, band, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -662,14 +698,13 @@ __global__ __launch_bounds__(kColThreads) void quant_cols_given(
 // row-wise pass of a tensor also yields what its column-wise pass needs,
 // without a second read of the tensor.
 
-template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false>
-__global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL>
+__device__ __forceinline__ void rows_colmax_band(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset, int64_t rows_per_block,
-    uint16_t* __restrict__ part, int64_t part_ld) {
-  __shared__ uint4 cm[WAVES][NV * 64];
+    uint16_t* __restrict__ part, int64_t part_ld, int64_t band, uint4 (*cm)[NV * 64]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r_begin = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t r_begin = band * rows_per_block;
   const int64_t r_end = min(rows, r_begin + rows_per_block);
 #pragma unroll
   for (int i = 0; i < NV; ++i) cm[wave][i * 64 + lane] = make_uint4(0, 0, 0, 0);
@@ -696,8 +731,45 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
     us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) max_chunk(m, cm[w][j]);
-    *reinterpret_cast<uint4*>(part + (int64_t)blockIdx.x * part_ld + c0) = pack_max(m);
+    *reinterpret_cast<uint4*>(part + band * part_ld + c0) = pack_max(m);
   }
+}
+
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false>
+__global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset, int64_t rows_per_block,
+    uint16_t* __restrict__ part, int64_t part_ld) {
+  __shared__ uint4 cm[WAVES][NV * 64];
+  rows_colmax_band<NV, WAVES, SR, ALIGNED4, FULL>(x, rows, cols, ldx, q, ldq, scale, seed, offset,
+                                                  rows_per_block, part, part_ld, blockIdx.x, cm);
+}
+
+// Two tensors of the same width in one launch (a linear layer's forward
+// quantizes X and W, both along K): blocks [0, a.slabs) take a's bands, the
+// rest b's.  Each tensor keeps its own rows, pitches, outputs, Philox offset
+// and slab maxima, so the results are those of two separate launches.
+struct RowColmaxJob {
+  const uint16_t* x;
+  int64_t rows, ldx;
+  int8_t* q;
+  int64_t ldq;
+  float* scale;
+  uint64_t offset;
+  int64_t rows_per_block, slabs;
+  uint16_t* part;
+};
+
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false>
+__global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax2(RowColmaxJob a, RowColmaxJob b,
+                                                                 int64_t cols, int64_t part_ld,
+                                                                 uint64_t seed) {
+  __shared__ uint4 cm[WAVES][NV * 64];
+  const bool second = (int64_t)blockIdx.x >= a.slabs;
+  const RowColmaxJob j = second ? b : a;
+  const int64_t band = second ? (int64_t)blockIdx.x - a.slabs : (int64_t)blockIdx.x;
+  rows_colmax_band<NV, WAVES, SR, ALIGNED4, FULL>(j.x, j.rows, cols, j.ldx, j.q, j.ldq, j.scale, seed,
+                                                  j.offset, j.rows_per_block, j.part, part_ld, band, cm);
 }
 
 // Row-wise with column maxima for rows longer than 14336 elements (a row no
@@ -809,11 +881,9 @@ __global__ __launch_bounds__(kLongThreads) void rows_long_quant(
 constexpr int kFinThreads = 512;
 constexpr int kFinWaves = kFinThreads / 64;
 
-__global__ __launch_bounds__(kFinThreads) void colmax_finalize(const uint16_t* __restrict__ part,
-                                                               int64_t part_ld, int64_t slabs,
-                                                               int64_t cols,
-                                                               float* __restrict__ colmax) {
-  __shared__ uint4 red[kFinWaves][4];
+__device__ __forceinline__ void finalize_block(const uint16_t* __restrict__ part, int64_t part_ld,
+                                               int64_t slabs, int64_t cols,
+                                               float* __restrict__ colmax, uint4 (*red)[4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunk = lane & 3, sub = lane >> 2;
   const int64_t c0 = (int64_t)blockIdx.x * 32 + chunk * 8;
@@ -851,6 +921,26 @@ __global__ __launch_bounds__(kFinThreads) void colmax_finalize(const uint16_t* _
     for (int j = 0; j < 8; ++j)
       if (c0 + j < cols) colmax[c0 + j] = __uint_as_float(b[j] << 16);
   }
+}
+
+__global__ __launch_bounds__(kFinThreads) void colmax_finalize(const uint16_t* __restrict__ part,
+                                                               int64_t part_ld, int64_t slabs,
+                                                               int64_t cols,
+                                                               float* __restrict__ colmax) {
+  __shared__ uint4 red[kFinWaves][4];
+  finalize_block(part, part_ld, slabs, cols, colmax, red);
+}
+
+// Two tensors of the same width: blockIdx.y picks the tensor.
+__global__ __launch_bounds__(kFinThreads) void colmax_finalize2(
+    const uint16_t* __restrict__ part_a, int64_t slabs_a, float* __restrict__ colmax_a,
+    const uint16_t* __restrict__ part_b, int64_t slabs_b, float* __restrict__ colmax_b,
+    int64_t part_ld, int64_t cols) {
+  __shared__ uint4 red[kFinWaves][4];
+  if (blockIdx.y == 0)
+    finalize_block(part_a, part_ld, slabs_a, cols, colmax_a, red);
+  else
+    finalize_block(part_b, part_ld, slabs_b, cols, colmax_b, red);
 }
 
 // Launch shapes: pass 1 has col_tiles x slabs blocks (about 256, at most
@@ -940,16 +1030,40 @@ RowColmaxPlan rcm_plan(int64_t rows, int64_t cols) {
   return p;
 }
 
+// Waves per block of the row pass with column maxima (LDS: waves x NV KiB of
+// column maxima).  16 waves (at most 128 VGPRs per lane) hold the
+// range-check-free round-to-nearest body of rows of 4096; stochastic rounding
+// (two Philox blocks per chunk) and range-checked rows of 8 chunks per lane
+// need more registers and take 8 waves instead of spilling.
+template <int NV>
+struct RcmWaves {
+  static constexpr int full = NV >= 16 ? 4 : (NV > 8 ? 8 : 16);
+  static constexpr int wide = NV >= 16 ? 4 : (NV >= 8 ? 8 : 16);
+};
+
+template <int NV>
+void launch_rcm2_nv(const RowColmaxJob& a, const RowColmaxJob& b, int64_t cols, int64_t part_ld,
+                    int round, uint64_t seed, hipStream_t stream) {
+  constexpr int WAVES = RcmWaves<NV>::full, WAVES_WIDE = RcmWaves<NV>::wide;
+  const dim3 grid((unsigned)(a.slabs + b.slabs));
+  const bool a4 = (cols % 4) == 0;
+  if (round == 1) {
+    if (a4)
+      quant_rows_colmax2<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+    else
+      quant_rows_colmax2<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+  } else if (cols == NV * 512) {
+    quant_rows_colmax2<NV, WAVES, false, true, true><<<grid, 64 * WAVES, 0, stream>>>(a, b, cols, part_ld, seed);
+  } else {
+    quant_rows_colmax2<NV, WAVES_WIDE, false, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+  }
+}
+
 template <int NV>
 void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int64_t cols,
                    int64_t ldx, int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
                    uint64_t offset, uint16_t* part, hipStream_t stream) {
-  // LDS: WAVES x NV KiB of column maxima.  16 waves (at most 128 VGPRs per
-  // lane) hold the range-check-free round-to-nearest body of rows of 4096;
-  // stochastic rounding (two Philox blocks per chunk) and range-checked rows of
-  // 8 chunks per lane need more registers and take 8 waves instead of spilling.
-  constexpr int WAVES = NV >= 16 ? 4 : (NV > 8 ? 8 : 16);
-  constexpr int WAVES_WIDE = NV >= 16 ? 4 : (NV >= 8 ? 8 : 16);
+  constexpr int WAVES = RcmWaves<NV>::full, WAVES_WIDE = RcmWaves<NV>::wide;
   const dim3 grid((unsigned)p.slabs);
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
@@ -1151,6 +1265,75 @@ hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_
       quant_cols_given<true, false><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, colmax, scale, q, ldq, seed, offset);
   } else {
     quant_cols_given<false, true><<<grid, kColThreads, 0, stream>>>(x, rows, cols, ldx, colmax, scale, q, ldq, seed, offset);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rowwise_colmax_pair(
+    const uint16_t* xa, int64_t rows_a, int64_t ldxa, int8_t* qa, int64_t ldqa, float* scale_a,
+    float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
+    int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
+    void* ws_b, int64_t cols, int round, uint64_t seed, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const RowColmaxPlan pa = rcm_plan(rows_a, cols), pb = rcm_plan(rows_b, cols);
+  if (!pa.fused || rows_a == 0 || rows_b == 0) {
+    const hipError_t e = launch_quantize_rowwise_colmax(xa, rows_a, cols, ldxa, qa, ldqa, scale_a, colmax_a,
+                                                        round, seed, offset_a, ws_a, stream);
+    if (e != hipSuccess) return e;
+    return launch_quantize_rowwise_colmax(xb, rows_b, cols, ldxb, qb, ldqb, scale_b, colmax_b, round, seed,
+                                          offset_b, ws_b, stream);
+  }
+  const RowColmaxJob a{xa, rows_a, ldxa, qa, ldqa, scale_a, offset_a, pa.rows_per_block, pa.slabs,
+                       static_cast<uint16_t*>(ws_a)};
+  const RowColmaxJob b{xb, rows_b, ldxb, qb, ldqb, scale_b, offset_b, pb.rows_per_block, pb.slabs,
+                       static_cast<uint16_t*>(ws_b)};
+  const int64_t per_lane = (cols + 511) / 512;
+  if (per_lane <= 1)
+    launch_rcm2_nv<1>(a, b, cols, pa.part_ld, round, seed, stream);
+  else if (per_lane <= 2)
+    launch_rcm2_nv<2>(a, b, cols, pa.part_ld, round, seed, stream);
+  else if (per_lane <= 4)
+    launch_rcm2_nv<4>(a, b, cols, pa.part_ld, round, seed, stream);
+  else if (per_lane <= 8)
+    launch_rcm2_nv<8>(a, b, cols, pa.part_ld, round, seed, stream);
+  else if (per_lane <= 12)
+    launch_rcm2_nv<12>(a, b, cols, pa.part_ld, round, seed, stream);
+  else if (per_lane <= 16)
+    launch_rcm2_nv<16>(a, b, cols, pa.part_ld, round, seed, stream);
+  else
+    launch_rcm2_nv<28>(a, b, cols, pa.part_ld, round, seed, stream);
+  colmax_finalize2<<<dim3((unsigned)((cols + 31) / 32), 2), kFinThreads, 0, stream>>>(
+      a.part, a.slabs, colmax_a, b.part, b.slabs, colmax_b, pa.part_ld, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise_given_pair(
+    const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, const float* colmax_a,
+    int8_t* qa, int64_t ldqa, float* scale_a, uint64_t offset_a, const uint16_t* xb,
+    int64_t rows_b, int64_t cols_b, int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb,
+    float* scale_b, uint64_t offset_b, int round, uint64_t seed, hipStream_t stream) {
+  if (cols_a == 0 || cols_b == 0) {
+    const hipError_t e = launch_quantize_colwise_given(xa, rows_a, cols_a, ldxa, colmax_a, qa, ldqa, scale_a,
+                                                       round, seed, offset_a, stream);
+    if (e != hipSuccess) return e;
+    return launch_quantize_colwise_given(xb, rows_b, cols_b, ldxb, colmax_b, qb, ldqb, scale_b, round, seed,
+                                         offset_b, stream);
+  }
+  const int64_t span = (int64_t)kColTile * kColWaves;
+  const ColGivenJob a{xa, rows_a, cols_a, ldxa, colmax_a, scale_a, qa, ldqa, offset_a,
+                      max((int64_t)1, (rows_a + kColBand - 1) / kColBand)};
+  const ColGivenJob b{xb, rows_b, cols_b, ldxb, colmax_b, scale_b, qb, ldqb, offset_b,
+                      max((int64_t)1, (rows_b + kColBand - 1) / kColBand)};
+  const int64_t groups = max((cols_a + span - 1) / span, (cols_b + span - 1) / span);
+  if (a.bands + b.bands > 0x7FFFFFFF || groups > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.bands + b.bands), (unsigned)groups);
+  if (round == 1) {
+    if (cols_a % 4 == 0 && cols_b % 4 == 0)
+      quant_cols_given2<true, true><<<grid, kColThreads, 0, stream>>>(a, b, seed);
+    else
+      quant_cols_given2<true, false><<<grid, kColThreads, 0, stream>>>(a, b, seed);
+  } else {
+    quant_cols_given2<false, true><<<grid, kColThreads, 0, stream>>>(a, b, seed);
   }
   return hipGetLastError();
 }

@@ -142,12 +142,12 @@ def _split_planes_bytes(M, N, K):
                                    (256, 512, 512), (64, 32, 48), (1000, 8, 4096)])
 def test_linear_workspace_holds_contraction_split_planes(M, N, K):
     """The forward chain's workspace: int8 codes and scales of X and W, the
-    row passes' slab maxima, and the split GEMM's int32 partial planes, each
-    region 256-byte aligned."""
+    two row passes' slab maxima (one region each: the passes share a launch),
+    and the split GEMM's int32 partial planes, each region 256-byte aligned."""
     up = lambda n: -(-n // 256) * 256  # noqa: E731
     kp = -(-K // 16) * 16
-    part = max(L.i8mp_quantize_rowwise_colmax_workspace_bytes(M, K),
-               L.i8mp_quantize_rowwise_colmax_workspace_bytes(N, K))
+    part = (L.i8mp_quantize_rowwise_colmax_workspace_bytes(M, K)
+            + L.i8mp_quantize_rowwise_colmax_workspace_bytes(N, K))
     want = up(M * kp) + up(N * kp) + up(4 * M) + up(4 * N) + part + up(_split_planes_bytes(M, N, K))
     assert L.i8mp_linear_workspace_bytes(M, N, K, 0) == want
     if (M, N, K) == (2048, 256, 32768):  # 8 tiles: 32 ranges of 1024
