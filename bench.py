@@ -196,7 +196,8 @@ def main():
 
     # The step as the library runs it: i8mp_linear_fwd_colmax then
     # i8mp_linear_bwd_colmax (the forward's two row-wise passes share one
-    # launch, the backward's two column-wise passes too: 9 launches).  Same
+    # launch, the backward's two column-wise passes too, and dY's column
+    # maxima are finalized in the launch of W's column pass: 8 launches).  Same
     # kernels' arithmetic as the 12 primitive launches above, same outputs.
     ws_fwd = torch.empty(L.i8mp_linear_workspace_bytes(M, N, K, 0), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(L.i8mp_linear_workspace_bytes(M, N, K, 1), dtype=torch.uint8, device=dev)

@@ -436,15 +436,25 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
   hipError_t e = hipSuccess;
   if (want_dx) {
     // dX = dY @ W: dY row-wise over N, W column-wise over N, NN
-    e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
-                                                         pass_offset(opts->offset, 2), w.col, s)
-                  : i8mp::launch_quantize_rowwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
-                                                  pass_offset(opts->offset, 2), s);
-    if (e == hipSuccess)
-      e = colmax_w ? i8mp::launch_quantize_colwise_given(W, N, K, K, colmax_w, w.qw, kp, w.sw, r, seed,
-                                                         pass_offset(opts->offset, 3), s)
-                   : i8mp::launch_quantize_colwise(W, N, K, K, w.qw, kp, w.sw, r, seed,
-                                                   pass_offset(opts->offset, 3), w.col, s);
+    if (dy_colmax && colmax_w) {
+      // dY's row pass leaves its slab maxima in w.col; their reduction to dY's
+      // column maxima shares a launch with W's column pass
+      e = i8mp::launch_quantize_rowwise_slabs(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
+                                              pass_offset(opts->offset, 2), w.col, false, s);
+      if (e == hipSuccess)
+        e = i8mp::launch_finalize_and_colwise_given(w.col, M, N, w.cdy, W, N, K, K, colmax_w, w.qw, kp, w.sw,
+                                                    r, seed, pass_offset(opts->offset, 3), s);
+    } else {
+      e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
+                                                           pass_offset(opts->offset, 2), w.col, s)
+                    : i8mp::launch_quantize_rowwise(dY, M, N, N, w.qdy, np, w.sdy, r, seed,
+                                                    pass_offset(opts->offset, 2), s);
+      if (e == hipSuccess)
+        e = colmax_w ? i8mp::launch_quantize_colwise_given(W, N, K, K, colmax_w, w.qw, kp, w.sw, r, seed,
+                                                           pass_offset(opts->offset, 3), s)
+                     : i8mp::launch_quantize_colwise(W, N, K, K, w.qw, kp, w.sw, r, seed,
+                                                     pass_offset(opts->offset, 3), w.col, s);
+    }
     if (e == hipSuccess)
       e = i8mp::launch_gemm_split(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, K, w.split, s);
   }

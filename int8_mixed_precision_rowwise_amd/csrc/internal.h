@@ -29,6 +29,23 @@ hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64
                                           float* colmax, int round, uint64_t seed, uint64_t offset,
                                           void* ws, hipStream_t stream);
 
+// The row pass of launch_quantize_rowwise_colmax alone (finalize = false):
+// codes, scales and the slab maxima in ws, which
+// launch_finalize_and_colwise_given later reduces to colmax.
+hipError_t launch_quantize_rowwise_slabs(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                         int8_t* q, int64_t ldq, float* scale, float* colmax,
+                                         int round, uint64_t seed, uint64_t offset, void* ws,
+                                         bool finalize, hipStream_t stream);
+
+// One launch: fin_colmax[c] from the slab maxima a row pass of a fin_rows x
+// fin_cols tensor left in ws_fin, and the column-wise quantization of x with
+// its maxima given.  Same results as the two separate launches.
+hipError_t launch_finalize_and_colwise_given(const void* ws_fin, int64_t fin_rows, int64_t fin_cols,
+                                             float* fin_colmax, const uint16_t* x, int64_t rows,
+                                             int64_t cols, int64_t ldx, const float* colmax,
+                                             int8_t* q, int64_t ldq, float* scale, int round,
+                                             uint64_t seed, uint64_t offset, hipStream_t stream);
+
 // Column-wise quantization with the column maxima given: one pass.
 hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_t cols,
                                          int64_t ldx, const float* colmax, int8_t* q, int64_t ldq,

@@ -881,12 +881,13 @@ __global__ __launch_bounds__(kLongThreads) void rows_long_quant(
 constexpr int kFinThreads = 512;
 constexpr int kFinWaves = kFinThreads / 64;
 
-__device__ __forceinline__ void finalize_block(const uint16_t* __restrict__ part, int64_t part_ld,
-                                               int64_t slabs, int64_t cols,
-                                               float* __restrict__ colmax, uint4 (*red)[4]) {
+__device__ __forceinline__ void finalize_block_at(const uint16_t* __restrict__ part, int64_t part_ld,
+                                                  int64_t slabs, int64_t cols,
+                                                  float* __restrict__ colmax, uint4 (*red)[4],
+                                                  int64_t group) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunk = lane & 3, sub = lane >> 2;
-  const int64_t c0 = (int64_t)blockIdx.x * 32 + chunk * 8;
+  const int64_t c0 = group * 32 + chunk * 8;
   us2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
   if (c0 < cols) {
     constexpr int64_t step = (int64_t)kFinWaves * 16;
@@ -921,6 +922,12 @@ __device__ __forceinline__ void finalize_block(const uint16_t* __restrict__ part
     for (int j = 0; j < 8; ++j)
       if (c0 + j < cols) colmax[c0 + j] = __uint_as_float(b[j] << 16);
   }
+}
+
+__device__ __forceinline__ void finalize_block(const uint16_t* __restrict__ part, int64_t part_ld,
+                                               int64_t slabs, int64_t cols,
+                                               float* __restrict__ colmax, uint4 (*red)[4]) {
+  finalize_block_at(part, part_ld, slabs, cols, colmax, red, blockIdx.x);
 }
 
 __global__ __launch_bounds__(kFinThreads) void colmax_finalize(const uint16_t* __restrict__ part,
@@ -1207,6 +1214,14 @@ hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64
                                           int64_t ldx, int8_t* q, int64_t ldq, float* scale,
                                           float* colmax, int round, uint64_t seed, uint64_t offset,
                                           void* ws, hipStream_t stream) {
+  return launch_quantize_rowwise_slabs(x, rows, cols, ldx, q, ldq, scale, colmax, round, seed, offset,
+                                       ws, true, stream);
+}
+
+hipError_t launch_quantize_rowwise_slabs(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                         int8_t* q, int64_t ldq, float* scale, float* colmax,
+                                         int round, uint64_t seed, uint64_t offset, void* ws,
+                                         bool finalize, hipStream_t stream) {
   if (cols == 0) return hipSuccess;
   const RowColmaxPlan p = rcm_plan(rows, cols);
   uint16_t* part = static_cast<uint16_t*>(ws);
@@ -1241,8 +1256,9 @@ hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64
         rows_long_quant<false, true><<<grid, kLongThreads, 0, stream>>>(x, rows, cols, ldx, p.rows_per_block, segmax, p.nseg, q, ldq, scale, seed, offset);
     }
   }
-  colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(
-      part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
+  if (finalize)
+    colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(
+        part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
   return hipGetLastError();
 }
 
@@ -1334,6 +1350,64 @@ hipError_t launch_quantize_colwise_given_pair(
       quant_cols_given2<true, false><<<grid, kColThreads, 0, stream>>>(a, b, seed);
   } else {
     quant_cols_given2<false, true><<<grid, kColThreads, 0, stream>>>(a, b, seed);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+// One launch for two independent jobs of the backward chain: reduce dY's slab
+// maxima to its column maxima (blocks [0, fin_blocks), as colmax_finalize) and
+// quantize W column-wise with its maxima given (the rest, as
+// quant_cols_given over bands x groups).  Both use 512-thread blocks.
+template <bool SR, bool ALIGNED4>
+__global__ __launch_bounds__(kColThreads) void finalize_and_cols_given(
+    const uint16_t* __restrict__ part, int64_t part_ld, int64_t slabs, int64_t fin_cols,
+    float* __restrict__ fin_colmax, int64_t fin_blocks, ColGivenJob job, int64_t groups,
+    uint64_t seed) {
+  static_assert(kColThreads == kFinThreads, "one block size for both jobs");
+  __shared__ uint4 red[kFinWaves][4];
+  const int64_t b = blockIdx.x;
+  if (b < fin_blocks) {
+    finalize_block_at(part, part_ld, slabs, fin_cols, fin_colmax, red, b);
+  } else {
+    const int64_t k = b - fin_blocks;
+    cols_given_block<SR, ALIGNED4, 0>(job.x, job.rows, job.cols, job.ldx, job.colmax, job.scale, job.q,
+                                      job.ldq, seed, job.offset, k / groups, k % groups);
+  }
+}
+}  // namespace
+
+hipError_t launch_finalize_and_colwise_given(const void* ws_fin, int64_t fin_rows, int64_t fin_cols,
+                                             float* fin_colmax, const uint16_t* x, int64_t rows,
+                                             int64_t cols, int64_t ldx, const float* colmax,
+                                             int8_t* q, int64_t ldq, float* scale, int round,
+                                             uint64_t seed, uint64_t offset, hipStream_t stream) {
+  const RowColmaxPlan p = rcm_plan(fin_rows, fin_cols);
+  if (fin_cols == 0 || cols == 0) {
+    if (fin_cols > 0)
+      colmax_finalize<<<dim3((unsigned)((fin_cols + 31) / 32)), kFinThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(ws_fin), p.part_ld, fin_rows > 0 ? p.slabs : 0, fin_cols, fin_colmax);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_quantize_colwise_given(x, rows, cols, ldx, colmax, q, ldq, scale, round, seed, offset, stream);
+  }
+  const int64_t span = (int64_t)kColTile * kColWaves;
+  const ColGivenJob job{x, rows, cols, ldx, colmax, scale, q, ldq, offset,
+                        max((int64_t)1, (rows + kColBand - 1) / kColBand)};
+  const int64_t groups = (cols + span - 1) / span;
+  const int64_t fin_blocks = (fin_cols + 31) / 32;
+  const int64_t total = fin_blocks + job.bands * groups;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const uint16_t* part = static_cast<const uint16_t*>(ws_fin);
+  const int64_t slabs = fin_rows > 0 ? p.slabs : 0;
+  const dim3 grid((unsigned)total);
+  if (round == 1) {
+    if (cols % 4 == 0)
+      finalize_and_cols_given<true, true><<<grid, kColThreads, 0, stream>>>(part, p.part_ld, slabs, fin_cols, fin_colmax, fin_blocks, job, groups, seed);
+    else
+      finalize_and_cols_given<true, false><<<grid, kColThreads, 0, stream>>>(part, p.part_ld, slabs, fin_cols, fin_colmax, fin_blocks, job, groups, seed);
+  } else {
+    finalize_and_cols_given<false, true><<<grid, kColThreads, 0, stream>>>(part, p.part_ld, slabs, fin_cols, fin_colmax, fin_blocks, job, groups, seed);
   }
   return hipGetLastError();
 }
