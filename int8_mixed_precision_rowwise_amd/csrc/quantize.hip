@@ -1051,7 +1051,7 @@ struct RcmWaves {
 template <int NV>
 void launch_rcm2_nv(const RowColmaxJob& a, const RowColmaxJob& b, int64_t cols, int64_t part_ld,
                     int round, uint64_t seed, hipStream_t stream) {
-  constexpr int WAVES = RcmWaves<NV>::full, WAVES_WIDE = RcmWaves<NV>::wide;
+  constexpr int WAVES_WIDE = RcmWaves<NV>::wide;
   const dim3 grid((unsigned)(a.slabs + b.slabs));
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
@@ -1060,7 +1060,10 @@ void launch_rcm2_nv(const RowColmaxJob& a, const RowColmaxJob& b, int64_t cols, 
     else
       quant_rows_colmax2<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
   } else if (cols == NV * 512) {
-    quant_rows_colmax2<NV, WAVES, false, true, true><<<grid, 64 * WAVES, 0, stream>>>(a, b, cols, part_ld, seed);
+    // two tensors' bands: with the 16-wave shape's LDS (WAVES x NV KiB) only one
+    // block fits per CU, so a pair would run as two rounds; 8 waves (two rows
+    // each) keep both tensors' blocks resident at once
+    quant_rows_colmax2<NV, WAVES_WIDE, false, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
   } else {
     quant_rows_colmax2<NV, WAVES_WIDE, false, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
   }
