@@ -182,6 +182,11 @@ i8mp_status i8mp_philox4x32_10(uint64_t seed, uint64_t offset, int64_t n_blocks,
  * Y: bf16 [M x N], all dense (leading dim = columns).  X and W are quantized
  * row-wise over K, then the NT scaled matmul runs.  K <= I8MP_MAX_CONTRACTION.
  * ws: at least i8mp_linear_workspace_bytes(M, N, K, 0) bytes, 256-aligned.
+ * The workspace holds the int8 codes, scales and slab maxima of the chain and,
+ * for an output of fewer than 128 tiles of 256 x 256 with a contraction of at
+ * least 2048, the int32 partial sums of a contraction split (reduced exactly
+ * before the fp32 epilogue: results equal i8mp_int8_scaled_mm's).  Its
+ * contents on entry do not matter and are not kept.
  */
 size_t i8mp_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t backward);
 i8mp_status i8mp_linear_fwd(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
