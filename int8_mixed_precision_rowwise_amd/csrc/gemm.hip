@@ -1048,7 +1048,8 @@ hipError_t pick(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, c
 //
 // A problem with fewer 256 x 256 tiles than half the CUs and a long
 // contraction (the grad-weight GEMM of a narrow layer contracts over all
-// tokens) splits the contraction over `splits` copies of the tile grid.  Each
+// tokens) splits the contraction over `splits` copies of the tile grid, when
+// that launches at least as many workgroups as its 128 x 128 tiling would.  Each
 // copy writes exact int32 partial sums into its own plane; splitk_reduce adds
 // the planes (integer addition: exact and order-free, and every partial sum is
 // a sum over a subset of the contraction, bounded like the full one) and
@@ -1072,7 +1073,10 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) 
   int64_t kc = (K + s - 1) / s;
   kc = (kc + BK - 1) / BK * BK;
   s = (K + kc - 1) / kc;  // every copy gets a non-empty range; K % 16 == 0 carries to the last
-  if (s < 2) return p;
+  // Worth it only with at least as many workgroups as the 128 x 128 tiling
+  // would launch (4 t), or a full chip: at 2048^3 (64 tiles, 2 copies) the
+  // split chain takes 44 + 116 us against 33 + 88 us on 128 x 128 tiles.
+  if (s < 2 || s * t < std::min<int64_t>(256, 4 * t)) return p;
   p.splits = (int)s;
   p.kchunk = kc;
   p.ldp = (N + 3) / 4 * 4;

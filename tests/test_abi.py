@@ -121,9 +121,10 @@ def test_linear_validation_and_workspace():
 
 def _split_planes_bytes(M, N, K):
     """Bytes of int32 partial planes the forward chain's NT GEMM (both operands
-    K-contiguous, rows padded to 16 bytes) takes: the output has fewer than 128
-    tiles of 256 x 256 and the contraction is a multiple of 16, so it splits
-    into min(256 // tiles, K // 1024) ranges of whole 64-deep slabs."""
+    K-contiguous, rows padded to 16 bytes) takes: when the output has fewer than
+    128 tiles of 256 x 256 and the contraction is a multiple of 16, it splits
+    into min(256 // tiles, K // 1024) ranges of whole 64-deep slabs, provided
+    that makes at least min(256, 4 * tiles) workgroups."""
     tiles = -(-M // 256) * -(-N // 256)
     if tiles >= 128 or K % 16 or K == 0:
         return 0
@@ -133,13 +134,14 @@ def _split_planes_bytes(M, N, K):
     kc = -(-K // s)
     kc = -(-kc // 64) * 64
     s = -(-K // kc)
-    if s < 2:
+    if s < 2 or s * tiles < min(256, 4 * tiles):  # no more workgroups than 128 x 128 tiles
         return 0
     return s * M * (-(-N // 4) * 4) * 4
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 256, 32768), (300, 264, 2048), (4096, 4096, 4096),
-                                   (256, 512, 512), (64, 32, 48), (1000, 8, 4096)])
+@pytest.mark.parametrize("M,N,K", [(2048, 256, 32768), (300, 264, 4096), (4096, 4096, 4096),
+                                   (2048, 2048, 2048), (1024, 1024, 8192), (256, 512, 512),
+                                   (64, 32, 48), (1000, 8, 4096)])
 def test_linear_workspace_holds_contraction_split_planes(M, N, K):
     """The forward chain's workspace: int8 codes and scales of X and W, the
     two row passes' slab maxima (one region each: the passes share a launch),
@@ -152,8 +154,10 @@ def test_linear_workspace_holds_contraction_split_planes(M, N, K):
     assert L.i8mp_linear_workspace_bytes(M, N, K, 0) == want
     if (M, N, K) == (2048, 256, 32768):  # 8 tiles: 32 ranges of 1024
         assert _split_planes_bytes(M, N, K) == 32 * 2048 * 256 * 4
-    if (M, N, K) == (4096, 4096, 4096):  # 256 tiles: no split
+    if (M, N, K) in ((4096, 4096, 4096), (2048, 2048, 2048)):  # 256 tiles; 2 copies of 64
         assert _split_planes_bytes(M, N, K) == 0
+    if (M, N, K) == (1024, 1024, 8192):  # 16 tiles: 8 ranges of 1024
+        assert _split_planes_bytes(M, N, K) == 8 * 1024 * 1024 * 4
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):

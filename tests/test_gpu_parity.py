@@ -245,11 +245,11 @@ def test_linear_single_layer_full(rounding, rc):
     assert torch.equal(dX2, dX) and torch.equal(dW2, dW)
 
 
-# (300, 264, 2048): the forward GEMM splits its contraction in two;
-# (300, 2048, 264): the grad-input GEMM does; (3088, 200, 296): the
-# grad-weight GEMM splits its 3088 tokens in three (1088 + 1088 + 912).
+# (300, 264, 4096): the forward GEMM splits its contraction in four;
+# (300, 4096, 264): the grad-input GEMM does; (4112, 200, 296): the
+# grad-weight GEMM splits its 4112 tokens in four (3 x 1088 + 848).
 @pytest.mark.parametrize("M,N,K", [(1, 8, 8), (17, 24, 40), (130, 264, 72), (1000, 8, 520),
-                                   (300, 264, 2048), (300, 2048, 264), (3088, 200, 296)])
+                                   (300, 264, 4096), (300, 4096, 264), (4112, 200, 296)])
 def test_linear_ragged(M, N, K):
     from workloads import LinearShape, bf16_bits, linear_inputs
     t = linear_inputs(LinearShape("ragged", M, N, K), seed=M + N + K)
@@ -264,7 +264,8 @@ def test_linear_ragged(M, N, K):
     assert_bf16_equal(tensor_bits(dW), dWo, "dW")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 264, 2048), (3088, 200, 296), (2048, 256, 32768)])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 4096), (4112, 200, 296), (2048, 256, 32768),
+                                   (1024, 8192, 1024)])
 def test_contraction_split_equals_unsplit_gemm(M, N, K):
     """The linear chains split the contraction of few-tile GEMMs into int32
     partial planes; their outputs equal the public unsplit GEMM's on the same

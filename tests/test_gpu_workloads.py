@@ -170,10 +170,13 @@ def test_square_4096_step_with_column_maxima(rounding):
 
 
 @pytest.mark.parametrize("rounding", ["rne", "sr"])
-def test_square_2048_step_contraction_split(rounding):
-    """M = N = K = 2048 has 64 big output tiles, so each GEMM of the chains
-    splits its contraction in two int32 partial planes."""
-    run_layer(square(2048), rounding, seed=7, offset=3, colmax=True)
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 8192), (1024, 8192, 1024), (2048, 2048, 2048)])
+def test_step_contraction_split(rounding, M, N, K):
+    """Chains whose forward (1024 x 1024 outputs, contraction 8192) or
+    grad-input GEMM (contraction 8192) splits its contraction eight ways into
+    int32 partial planes, and 2048^3, which runs unsplit on 128 x 128 tiles."""
+    from workloads import LinearShape
+    run_layer(LinearShape(f"split_{M}x{N}x{K}", M, N, K), rounding, seed=7, offset=3, colmax=True)
 
 
 @pytest.mark.parametrize("layer", ["llama1b_down_proj", "llama1b_gate_proj"])
