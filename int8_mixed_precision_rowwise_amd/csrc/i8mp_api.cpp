@@ -628,13 +628,18 @@ i8mp_status i8mp_linear_bwd_fp8(const uint16_t* dY, const uint16_t* X, const uin
   uint8_t* qw = reinterpret_cast<uint8_t*>(w.qw);
   uint8_t* qx = reinterpret_cast<uint8_t*>(w.qx);
   hipError_t e = hipSuccess;
+  // with both gradients, dY's column maxima come from its row-wise pass, so its
+  // column-wise pass reads it once (as in the INT8 chain)
+  const bool dy_colmax = want_dx && want_dw && i8mp::rowwise_colmax_fp8_fused(M, N);
   if (want_dx) {
-    e = i8mp::launch_quantize_rowwise_fp8(dY, M, N, N, qdy, np, w.sdy, s);
+    e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax_fp8(dY, M, N, N, qdy, np, w.sdy, w.cdy, w.col, s)
+                  : i8mp::launch_quantize_rowwise_fp8(dY, M, N, N, qdy, np, w.sdy, s);
     if (e == hipSuccess) e = i8mp::launch_quantize_colwise_fp8(W, N, K, K, qw, kp, w.sw, w.col, s);
     if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_NN, M, K, N, qdy, np, w.sdy, qw, kp, w.sw, dX, nullptr, K, s);
   }
   if (want_dw && e == hipSuccess) {
-    e = i8mp::launch_quantize_colwise_fp8(dY, M, N, N, qdy, np, w.sdy, w.col, s);
+    e = dy_colmax ? i8mp::launch_quantize_colwise_given_fp8(dY, M, N, N, w.cdy, qdy, np, w.sdy, s)
+                  : i8mp::launch_quantize_colwise_fp8(dY, M, N, N, qdy, np, w.sdy, w.col, s);
     if (e == hipSuccess) e = i8mp::launch_quantize_colwise_fp8(X, M, K, K, qx, kp, w.sx, w.col, s);
     if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_TN, N, K, M, qdy, np, w.sdy, qx, kp, w.sx, dW, nullptr, K, s);
   }

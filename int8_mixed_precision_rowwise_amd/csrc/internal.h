@@ -78,6 +78,18 @@ hipError_t launch_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t 
                                        uint8_t* q8, int64_t ldq, float* scale, void* ws,
                                        hipStream_t stream);
 
+// FP8 (E4M3) row-wise quantization that also writes colmax (as
+// launch_quantize_rowwise_colmax; rows of at most 14336 elements, where
+// rowwise_colmax_fp8_fused holds), and the FP8 column-wise pass with the
+// column maxima given.
+bool rowwise_colmax_fp8_fused(int64_t rows, int64_t cols);
+hipError_t launch_quantize_rowwise_colmax_fp8(const uint16_t* x, int64_t rows, int64_t cols,
+                                              int64_t ldx, uint8_t* q8, int64_t ldq, float* scale,
+                                              float* colmax, void* ws, hipStream_t stream);
+hipError_t launch_quantize_colwise_given_fp8(const uint16_t* x, int64_t rows, int64_t cols,
+                                            int64_t ldx, const float* colmax, uint8_t* q8,
+                                            int64_t ldq, float* scale, hipStream_t stream);
+
 // FP8 (E4M3) scaled GEMM with fp32 accumulation, same layouts; needs
 // K % 16 == 0.  Exactly one of C (bf16, with both scales) or C_f32 (the raw
 // fp32 sums) is non-null.

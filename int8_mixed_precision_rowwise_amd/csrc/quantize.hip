@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kColThreads) void quant_cols_given2(ColGivenJob a, 
 // row-wise pass of a tensor also yields what its column-wise pass needs,
 // without a second read of the tensor.
 
-template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL>
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL, int FMT = 0>
 __device__ __forceinline__ void rows_colmax_band(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset, int64_t rows_per_block,
@@ -727,7 +727,7 @@ __device__ __forceinline__ void rows_colmax_band(
       max_chunk(m, v[i]);
       cm[wave][i * 64 + lane] = pack_max(m);
     }
-    quantize_row<NV, SR, ALIGNED4, 0, FULL, true>(v, r, cols, q, ldq, scale, seed, offset, lane);
+    quantize_row<NV, SR, ALIGNED4, FMT, FULL, true>(v, r, cols, q, ldq, scale, seed, offset, lane);
     const int64_t rn = r + WAVES;
     if (rn < r_end) load_row<NV, FULL>(v, x + rn * ldx, cols, lane);
   }
@@ -742,14 +742,14 @@ __device__ __forceinline__ void rows_colmax_band(
   }
 }
 
-template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false>
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false, int FMT = 0>
 __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint64_t seed, uint64_t offset, int64_t rows_per_block,
     uint16_t* __restrict__ part, int64_t part_ld) {
   __shared__ uint4 cm[WAVES][NV * 64];
-  rows_colmax_band<NV, WAVES, SR, ALIGNED4, FULL>(x, rows, cols, ldx, q, ldq, scale, seed, offset,
-                                                  rows_per_block, part, part_ld, blockIdx.x, cm);
+  rows_colmax_band<NV, WAVES, SR, ALIGNED4, FULL, FMT>(x, rows, cols, ldx, q, ldq, scale, seed, offset,
+                                                       rows_per_block, part, part_ld, blockIdx.x, cm);
 }
 
 // Two tensors of the same width in one launch (a linear layer's forward
@@ -1164,6 +1164,64 @@ hipError_t launch_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t 
     launch_rows_f8_nv<28>(x, rows, cols, ldx, q, ldq, scale, stream);
   else
     quant_rows_block<false, true, 1><<<dim3((unsigned)rows), kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0);
+  return hipGetLastError();
+}
+
+namespace {
+template <int NV>
+void launch_rcm_f8_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int64_t cols,
+                      int64_t ldx, int8_t* q, int64_t ldq, float* scale, uint16_t* part,
+                      hipStream_t stream) {
+  constexpr int WAVES = RcmWaves<NV>::full, WAVES_WIDE = RcmWaves<NV>::wide;
+  const dim3 grid((unsigned)p.slabs);
+  if (cols == NV * 512)
+    quant_rows_colmax<NV, WAVES, false, true, true, 1><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0, p.rows_per_block, part, p.part_ld);
+  else
+    quant_rows_colmax<NV, WAVES_WIDE, false, true, false, 1><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, 0, 0, p.rows_per_block, part, p.part_ld);
+}
+}  // namespace
+
+bool rowwise_colmax_fp8_fused(int64_t rows, int64_t cols) { return rcm_plan(rows, cols).fused; }
+
+hipError_t launch_quantize_rowwise_colmax_fp8(const uint16_t* x, int64_t rows, int64_t cols,
+                                              int64_t ldx, uint8_t* q8, int64_t ldq, float* scale,
+                                              float* colmax, void* ws, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const RowColmaxPlan p = rcm_plan(rows, cols);
+  if (!p.fused) return hipErrorInvalidValue;  // rows over 14336 elements: not offered
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  int8_t* q = reinterpret_cast<int8_t*>(q8);
+  if (rows > 0) {
+    const int64_t per_lane = (cols + 511) / 512;
+    if (per_lane <= 1)
+      launch_rcm_f8_nv<1>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else if (per_lane <= 2)
+      launch_rcm_f8_nv<2>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else if (per_lane <= 4)
+      launch_rcm_f8_nv<4>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else if (per_lane <= 8)
+      launch_rcm_f8_nv<8>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else if (per_lane <= 12)
+      launch_rcm_f8_nv<12>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else if (per_lane <= 16)
+      launch_rcm_f8_nv<16>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else
+      launch_rcm_f8_nv<28>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+  }
+  colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(
+      part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise_given_fp8(const uint16_t* x, int64_t rows, int64_t cols,
+                                            int64_t ldx, const float* colmax, uint8_t* q8,
+                                            int64_t ldq, float* scale, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const int64_t bands = max((int64_t)1, (rows + kColBand - 1) / kColBand);
+  const int64_t groups = (cols + (int64_t)kColTile * kColWaves - 1) / ((int64_t)kColTile * kColWaves);
+  if (bands > 0x7FFFFFFF || groups > 65535) return hipErrorInvalidValue;
+  quant_cols_given<false, true, 1><<<dim3((unsigned)bands, (unsigned)groups), kColThreads, 0, stream>>>(
+      x, rows, cols, ldx, colmax, scale, reinterpret_cast<int8_t*>(q8), ldq, 0, 0);
   return hipGetLastError();
 }
 
