@@ -363,6 +363,7 @@ def main():
     sweep = None if args.no_context else context_square_sweep(i8, dev, stream)
     qctx = None if args.no_context else context_quantize_large(i8, dev, stream)
     llama = None if args.no_context else context_llama1b_layers(i8, dev, stream)
+    llama8b = None if args.no_context else context_llama3_8b_layers(i8, dev, stream)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -405,6 +406,7 @@ def main():
         "context_square_sweep_vs_torch_bf16": sweep,
         "context_quantize_llama1b_sizes": qctx,
         "context_llama1b_7_linears_fwd_bwd": llama,
+        "context_llama3_8b_linears_and_lm_head_fwd_bwd": llama8b,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
@@ -506,16 +508,28 @@ def context_quantize_large(i8, dev, stream):
 
 
 def context_llama1b_layers(i8, dev, stream):
-    """The seven Llama-1B decoder linears at 16 x 2048 = 32768 tokens, one
-    training step each through the chains (forward with column maxima, then
-    both gradients: 6 quantize passes + 3 INT8 GEMMs), against the three bf16
-    torch matmuls of the same step (no quantization)."""
+    """The seven Llama-1B decoder linears at 16 x 2048 = 32768 tokens."""
+    from workloads import llama_1b_layers
+    return context_layers(i8, dev, stream, llama_1b_layers(), "llama1b_", 10)
+
+
+def context_llama3_8b_layers(i8, dev, stream):
+    """The seven Llama-3-8B decoder linears and the LM head [4096 -> 128256]
+    at 8192 tokens."""
+    from workloads import llama3_8b_layers
+    return context_layers(i8, dev, stream, llama3_8b_layers(), "llama3_8b_", 5)
+
+
+def context_layers(i8, dev, stream, shapes, prefix, iters):
+    """Each linear's training step through the chains (forward with column
+    maxima, then both gradients: 6 quantize passes + 3 INT8 GEMMs), against
+    the three bf16 torch matmuls of the same step (no quantization)."""
     import torch
-    from workloads import linear_inputs, llama_1b_layers
+    from workloads import linear_inputs
     tot8 = tot16 = 0.0
     ops = 0.0
     per = {}
-    for shape in llama_1b_layers():
+    for shape in shapes:
         M, N, K = shape.M, shape.N, shape.K
         t = linear_inputs(shape, seed=0, device=dev)
         X, W, dY = t["X"], t["W"], t["dY"]
@@ -534,9 +548,9 @@ def context_llama1b_layers(i8, dev, stream):
             torch.matmul(dY, W, out=dX)
             torch.matmul(dY.t(), X, out=dW)
 
-        t8 = _time_us(step8, stream, 10)
-        t16 = _time_us(step16, stream, 10)
-        per[shape.name.replace("llama1b_", "")] = {"int8_us": round(t8, 1), "bf16_us": round(t16, 1)}
+        t8 = _time_us(step8, stream, iters)
+        t16 = _time_us(step16, stream, iters)
+        per[shape.name.replace(prefix, "")] = {"int8_us": round(t8, 1), "bf16_us": round(t16, 1)}
         tot8 += t8
         tot16 += t16
         ops += 3 * 2.0 * M * N * K
@@ -545,7 +559,7 @@ def context_llama1b_layers(i8, dev, stream):
     return {"int8_us": round(tot8, 1), "bf16_gemms_us": round(tot16, 1),
             "speedup_vs_bf16": round(tot16 / tot8, 3), "int8_tops": round(ops / tot8 / 1e6, 1),
             "per_linear": per,
-            "note": "tokens 32768; int8 includes all quantize passes, bf16 is the GEMMs alone"}
+            "note": f"tokens {shapes[0].M}; int8 includes all quantize passes, bf16 is the GEMMs alone"}
 
 
 def cpu_baseline(tokens: int, N: int, K: int, rounding: str):
