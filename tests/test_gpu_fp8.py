@@ -215,7 +215,7 @@ def test_fp8_scaled_mm_4096_sampled(layout):
                  np.einsum("ij,ij->i", Am[ms], Bm[ns]))
 
 
-@pytest.mark.parametrize("M,N,K", [(32, 48, 64), (256, 512, 512), (1008, 272, 608)])
+@pytest.mark.parametrize("M,N,K", [(32, 48, 64), (256, 512, 512), (1008, 272, 608), (512, 4096, 256)])
 def test_linear_chains_fp8(M, N, K):
     t = linear_inputs(LinearShape("fp8_chain", M, N, K), seed=2, device="cuda")
     X, W, dY = t["X"], t["W"], t["dY"]
@@ -237,6 +237,19 @@ def test_linear_chains_fp8(M, N, K):
     y, _, ad = oracle.fp8_scaled_mm(oracle.TN, qdyc, sdyc, qxc, sxc, want_acc=True)
     Am, Bm = block_term("TN", qdyc, qxc)
     within_bound(dW, y, ad, np.abs(sdyc[:, None] * sxc[None, :]).astype(np.float64), M, "dW", Am @ Bm.T)
+    # With both gradients the chain takes dY's column maxima from its row-wise
+    # pass; its gradients equal, byte for byte, the FP8 GEMMs of the public
+    # quantize passes' codes (same codes, same deterministic GEMM).
+    gx, gw = i8.linear_bwd_fp8(dY, X, W)
+    qa, sa = i8.quantize_rowwise_fp8(dY)
+    qb, sb = i8.quantize_colwise_fp8(W)
+    want_dx = i8.fp8_scaled_mm("NN", qa, sa, qb, sb)
+    qa, sa = i8.quantize_colwise_fp8(dY)
+    qb, sb = i8.quantize_colwise_fp8(X)
+    want_dw = i8.fp8_scaled_mm("TN", qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(gx.view(torch.int16), want_dx.view(torch.int16)), "dX differs from the primitives"
+    assert torch.equal(gw.view(torch.int16), want_dw.view(torch.int16)), "dW differs from the primitives"
 
 
 @pytest.mark.parametrize("K", [64, 1024])
