@@ -160,6 +160,54 @@ def test_linear_workspace_holds_contraction_split_planes(M, N, K):
         assert _split_planes_bytes(M, N, K) == 8 * 1024 * 1024 * 4
 
 
+def _split_bytes(M, N, K, a_kmajor, b_kmajor, lda, ldb):
+    """Partial-plane bytes of a chain GEMM with output M x N and contraction K
+    (the rule of _split_planes_bytes, with the pipelined kernel's conditions:
+    K % 16 == 0, operand tiles under 2^31 bytes, and an output extent that is a
+    multiple of 4 along each operand read down its rows)."""
+    tiles = -(-M // 256) * -(-N // 256)
+    lim = (1 << 31) - 1024
+    a_ext = 256 * lda if a_kmajor else K * lda
+    b_ext = 256 * ldb if b_kmajor else K * ldb
+    mn_ok = (a_kmajor or M % 4 == 0) and (b_kmajor or N % 4 == 0)
+    if tiles >= 128 or K == 0 or K % 16 or a_ext >= lim or b_ext >= lim or not mn_ok:
+        return 0
+    s = min(256 // tiles, K // 1024)
+    if s < 2:
+        return 0
+    kc = -(-K // s)
+    kc = -(-kc // 64) * 64
+    s = -(-K // kc)
+    if s < 2 or s * tiles < min(256, 4 * tiles):
+        return 0
+    return s * M * (-(-N // 4) * 4) * 4
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 256, 32768), (32768, 256, 2048), (300, 4096, 264),
+                                   (4112, 200, 296), (4096, 4096, 4096), (1024, 8192, 1024),
+                                   (64, 32, 48), (32768, 5632, 2048)])
+def test_linear_backward_workspace_layout(M, N, K):
+    """The backward chain's workspace: dY's codes (one buffer for its row- and
+    column-wise passes), W's and X's codes, the scales, dY's column maxima, the
+    largest slab scratch of its quantize passes, and the larger of the
+    grad-input (NN) and grad-weight (TN) GEMMs' split planes; 256-byte regions."""
+    up = lambda n: -(-n // 256) * 256  # noqa: E731
+    kp, np_ = -(-K // 16) * 16, -(-N // 16) * 16
+    col = max(L.i8mp_quantize_colwise_workspace_bytes(N, K), L.i8mp_quantize_colwise_workspace_bytes(M, N),
+              L.i8mp_quantize_colwise_workspace_bytes(M, K),
+              L.i8mp_quantize_rowwise_colmax_workspace_bytes(M, N))
+    split = max(_split_bytes(M, K, N, True, False, np_, kp), _split_bytes(N, K, M, False, False, np_, kp))
+    want = (up(M * np_) + up(N * kp) + up(M * kp) + up(4 * max(M, N)) + up(4 * K) + up(4 * K)
+            + up(4 * N) + col + up(split))
+    assert L.i8mp_linear_workspace_bytes(M, N, K, 1) == want
+    if (M, N, K) == (32768, 256, 2048):  # grad-weight 256 x 2048 (8 tiles) over 32768 tokens
+        assert _split_bytes(N, K, M, False, False, np_, kp) == 32 * 256 * 2048 * 4
+    if (M, N, K) == (2048, 256, 32768):  # grad-weight 256 x 32768 has 128 tiles: no split
+        assert _split_bytes(N, K, M, False, False, np_, kp) == 0
+    if (M, N, K) == (1024, 8192, 1024):  # grad-input: 16 tiles, contraction 8192 in 8 ranges
+        assert _split_bytes(M, K, N, True, False, np_, kp) == 8 * 1024 * 1024 * 4
+
+
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
     """The package refuses to import without its library instead of falling back."""
     import importlib
