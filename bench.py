@@ -90,8 +90,8 @@ def read_traffic(kernel: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding "
-              "of this path is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sharding this path "
+              "over several GPUs is described in the design notes, not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
