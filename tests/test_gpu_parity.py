@@ -264,6 +264,29 @@ def test_linear_ragged(M, N, K):
     assert_bf16_equal(tensor_bits(dW), dWo, "dW")
 
 
+# Ragged chains with the column maxima handed from forward to backward (the
+# paired and fused quantize launches), against the oracle in full: forward
+# splits (few tiles, contraction 4496 / 8816), grad-input splits (dY 5968 /
+# 8352 wide), grad-weight splits (5744 / 2384 tokens), both roundings.
+@pytest.mark.parametrize("M,N,K,rounding", [(144, 64, 4496, "rne"), (208, 32, 8816, "sr"),
+                                            (205, 5968, 152, "sr"), (114, 8352, 256, "rne"),
+                                            (5744, 64, 16, "rne"), (2384, 120, 208, "sr")])
+def test_linear_chains_with_maxima_ragged_splits(M, N, K, rounding):
+    from workloads import LinearShape, bf16_bits, linear_inputs
+    rc = oracle.SR if rounding == "sr" else oracle.RNE
+    t = linear_inputs(LinearShape("ragged_split", M, N, K), seed=M + N + K, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    off = 7 << 44
+    Y, cx, cw = i8.linear_fwd_colmax(X, W, rounding, 11, off)
+    dX, dW = i8.linear_bwd(dY, X, W, rounding, 11, off, colmax_x=cx, colmax_w=cw)
+    torch.cuda.synchronize()
+    Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
+    assert_bf16_equal(tensor_bits(Y), oracle.linear_fwd(Xb, Wb, rc, 11, off), "Y")
+    dXo, dWo = oracle.linear_bwd(dYb, Xb, Wb, rc, 11, off)
+    assert_bf16_equal(tensor_bits(dX), dXo, "dX")
+    assert_bf16_equal(tensor_bits(dW), dWo, "dW")
+
+
 @pytest.mark.parametrize("M,N,K", [(300, 264, 4096), (4112, 200, 296), (2048, 256, 32768),
                                    (1024, 8192, 1024)])
 def test_contraction_split_equals_unsplit_gemm(M, N, K):
