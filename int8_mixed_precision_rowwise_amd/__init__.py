@@ -128,12 +128,66 @@ def _empty_2d(rows: int, cols: int, dtype, device) -> torch.Tensor:
     return torch.empty((rows, ld), dtype=dtype, device=device)[:, :cols]
 
 
-def _bits(t: torch.Tensor, dtype=torch.bfloat16) -> torch.Tensor:
+# Argument checks.  The C ABI receives bare pointers and sizes, so every
+# tensor's dtype, shape, layout and device is checked here, before the call:
+# a mismatch raises (TypeError for a wrong type or dtype, ValueError for a
+# wrong shape, layout or device) and nothing is launched.  Type and shape
+# checks come first and the device check last, so they hold on any device.
+
+
+def _tensor(t, name: str, dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: torch.Tensor expected, got {type(t).__name__}")
     if t.dtype != dtype:
-        raise TypeError(f"{dtype} tensor expected, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError("device tensor expected")
+        raise TypeError(f"{name}: {dtype} tensor expected, got {t.dtype}")
     return t
+
+
+def _mat(t, name: str, dtype, shape=None, dense: bool = False) -> torch.Tensor:
+    """2-D matrix of `dtype`, rows with contiguous columns (a leading
+    dimension), of `shape` if given; `dense`: fully contiguous (the linear
+    chains take leading dimension = columns)."""
+    _tensor(t, name, dtype)
+    if t.dim() != 2:
+        raise ValueError(f"{name}: 2-D tensor expected, got {t.dim()}-D")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(shape)} expected, got {tuple(t.shape)}")
+    if t.numel() > 0:
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name}: columns must be contiguous (stride 1)")
+        if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+            raise ValueError(f"{name}: row stride {t.stride(0)} is shorter than a row ({t.shape[1]})")
+        if dense and not t.is_contiguous():
+            raise ValueError(f"{name}: contiguous tensor expected")
+    return t
+
+
+def _vec(t, name: str, n: int, dtype=torch.float32) -> torch.Tensor:
+    """Contiguous 1-D vector of n elements."""
+    _tensor(t, name, dtype)
+    if t.dim() != 1 or t.numel() != n:
+        raise ValueError(f"{name}: 1-D tensor of {n} elements expected, got shape {tuple(t.shape)}")
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name}: contiguous tensor expected")
+    return t
+
+
+def _workspace(t, name: str = "workspace") -> torch.Tensor:
+    _tensor(t, name, torch.uint8)
+    if t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name}: contiguous 1-D uint8 tensor expected")
+    return t
+
+
+def _device(*ts) -> torch.device:
+    """The one GPU that every given tensor lives on."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors on one device expected, got {sorted(str(d) for d in devs)}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"device tensors expected, got tensors on {dev}")
+    return dev
 
 
 # --------------------------------------------------------------------------- primitives
@@ -142,13 +196,18 @@ def _bits(t: torch.Tensor, dtype=torch.bfloat16) -> torch.Tensor:
 def quantize_rowwise(x: torch.Tensor, rounding="rne", seed: int = 0, offset: int = 0,
                      q: torch.Tensor | None = None, scale: torch.Tensor | None = None):
     """Row-wise dynamic INT8 quantization of bf16 ``x`` [R, C] -> (int8 q [R, C], fp32 scale [R])."""
-    _bits(x)
+    _mat(x, "x", torch.bfloat16)
     R, C = x.shape
-    q = _empty_2d(R, C, torch.int8, x.device) if q is None else q
-    scale = torch.empty(R, dtype=torch.float32, device=x.device) if scale is None else scale
-    with torch.cuda.device(x.device):
+    if q is not None:
+        _mat(q, "q", torch.int8, (R, C))
+    if scale is not None:
+        _vec(scale, "scale", R)
+    dev = _device(x, q, scale)
+    q = _empty_2d(R, C, torch.int8, dev) if q is None else q
+    scale = torch.empty(R, dtype=torch.float32, device=dev) if scale is None else scale
+    with torch.cuda.device(dev):
         st = lib.i8mp_quantize_rowwise(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
-                                       _ROUNDING[rounding], seed, offset, _stream(x.device))
+                                       _ROUNDING[rounding], seed, offset, _stream(dev))
     _check(st, "i8mp_quantize_rowwise")
     return q, scale
 
@@ -163,18 +222,27 @@ def quantize_rowwise_colmax(x: torch.Tensor, rounding="rne", seed: int = 0, offs
                             workspace: torch.Tensor | None = None):
     """Row-wise quantization that also returns the column maxima of |x|:
     (int8 q [R, C], fp32 scale [R], fp32 colmax [C])."""
-    _bits(x)
+    _mat(x, "x", torch.bfloat16)
     R, C = x.shape
-    q = _empty_2d(R, C, torch.int8, x.device) if q is None else q
-    scale = torch.empty(R, dtype=torch.float32, device=x.device) if scale is None else scale
-    colmax = torch.empty(C, dtype=torch.float32, device=x.device) if colmax is None else colmax
+    if q is not None:
+        _mat(q, "q", torch.int8, (R, C))
+    if scale is not None:
+        _vec(scale, "scale", R)
+    if colmax is not None:
+        _vec(colmax, "colmax", C)
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _device(x, q, scale, colmax, workspace)
+    q = _empty_2d(R, C, torch.int8, dev) if q is None else q
+    scale = torch.empty(R, dtype=torch.float32, device=dev) if scale is None else scale
+    colmax = torch.empty(C, dtype=torch.float32, device=dev) if colmax is None else colmax
     need = rowwise_colmax_workspace_bytes(R, C)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         st = lib.i8mp_quantize_rowwise_colmax(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
                                               _ptr(colmax), _ROUNDING[rounding], seed, offset,
-                                              _ptr(workspace), workspace.numel(), _stream(x.device))
+                                              _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "i8mp_quantize_rowwise_colmax")
     return q, scale, colmax
 
@@ -184,15 +252,20 @@ def quantize_colwise_given_colmax(x: torch.Tensor, colmax: torch.Tensor, roundin
                                   scale: torch.Tensor | None = None):
     """Column-wise quantization with known column maxima (one pass):
     (int8 q [R, C] in x's layout, fp32 scale [C])."""
-    _bits(x)
-    _bits(colmax, torch.float32)
+    _mat(x, "x", torch.bfloat16)
     R, C = x.shape
-    q = _empty_2d(R, C, torch.int8, x.device) if q is None else q
-    scale = torch.empty(C, dtype=torch.float32, device=x.device) if scale is None else scale
-    with torch.cuda.device(x.device):
+    _vec(colmax, "colmax", C)
+    if q is not None:
+        _mat(q, "q", torch.int8, (R, C))
+    if scale is not None:
+        _vec(scale, "scale", C)
+    dev = _device(x, colmax, q, scale)
+    q = _empty_2d(R, C, torch.int8, dev) if q is None else q
+    scale = torch.empty(C, dtype=torch.float32, device=dev) if scale is None else scale
+    with torch.cuda.device(dev):
         st = lib.i8mp_quantize_colwise_given_colmax(_ptr(x), R, C, _ld(x), _ptr(colmax), _ptr(q),
                                                     _ld(q), _ptr(scale), _ROUNDING[rounding], seed,
-                                                    offset, _stream(x.device))
+                                                    offset, _stream(dev))
     _check(st, "i8mp_quantize_colwise_given_colmax")
     return q, scale
 
@@ -205,17 +278,24 @@ def quantize_colwise(x: torch.Tensor, rounding="rne", seed: int = 0, offset: int
                      q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
                      workspace: torch.Tensor | None = None):
     """Column-wise dynamic INT8 quantization -> (int8 q [R, C] in x's layout, fp32 scale [C])."""
-    _bits(x)
+    _mat(x, "x", torch.bfloat16)
     R, C = x.shape
-    q = _empty_2d(R, C, torch.int8, x.device) if q is None else q
-    scale = torch.empty(C, dtype=torch.float32, device=x.device) if scale is None else scale
+    if q is not None:
+        _mat(q, "q", torch.int8, (R, C))
+    if scale is not None:
+        _vec(scale, "scale", C)
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _device(x, q, scale, workspace)
+    q = _empty_2d(R, C, torch.int8, dev) if q is None else q
+    scale = torch.empty(C, dtype=torch.float32, device=dev) if scale is None else scale
     need = colwise_workspace_bytes(R, C)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         st = lib.i8mp_quantize_colwise(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
                                        _ROUNDING[rounding], seed, offset, _ptr(workspace),
-                                       workspace.numel(), _stream(x.device))
+                                       workspace.numel(), _stream(dev))
     _check(st, "i8mp_quantize_colwise")
     return q, scale
 
@@ -238,18 +318,33 @@ def _mnk(layout: int, A: torch.Tensor, B: torch.Tensor):
     return M, N, K
 
 
+def _mm_args(layout, A, B, code_dtype, scale_a=None, scale_b=None, out=None, out_dtype=None):
+    """Checks of a GEMM's operands (codes of `code_dtype` in `layout`), its
+    scales and its output; returns (layout, M, N, K, device)."""
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be 'NT', 'NN' or 'TN', got {layout!r}")
+    layout = _LAYOUTS[layout]
+    _mat(A, "A", code_dtype)
+    _mat(B, "B", code_dtype)
+    M, N, K = _mnk(layout, A, B)
+    if out_dtype is torch.bfloat16:
+        _vec(scale_a, "scale_a", M)
+        _vec(scale_b, "scale_b", N)
+    if out is not None:
+        _mat(out, "out", out_dtype, (M, N))
+    return layout, M, N, K, _device(A, B, scale_a, scale_b, out)
+
+
 def int8_scaled_mm(layout, A: torch.Tensor, scale_a: torch.Tensor, B: torch.Tensor,
                    scale_b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 C[M,N] = bf16(((float)(A(m,:) . B(:,n)) * scale_a[m]) * scale_b[n]).
 
     layout: "NT" (A [M,K], B [N,K]), "NN" (A [M,K], B [K,N]) or "TN" (A [K,M], B [K,N])."""
-    layout = _LAYOUTS[layout]
-    _bits(A, torch.int8), _bits(B, torch.int8)
-    M, N, K = _mnk(layout, A, B)
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if out is None else out
-    with torch.cuda.device(A.device):
+    layout, M, N, K, dev = _mm_args(layout, A, B, torch.int8, scale_a, scale_b, out, torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    with torch.cuda.device(dev):
         st = lib.i8mp_int8_scaled_mm(layout, M, N, K, _ptr(A), _ld(A), _ptr(scale_a), _ptr(B),
-                                     _ld(B), _ptr(scale_b), _ptr(out), _ld(out), _stream(A.device))
+                                     _ld(B), _ptr(scale_b), _ptr(out), _ld(out), _stream(dev))
     _check(st, "i8mp_int8_scaled_mm")
     return out
 
@@ -257,22 +352,23 @@ def int8_scaled_mm(layout, A: torch.Tensor, scale_a: torch.Tensor, B: torch.Tens
 def int8_mm_i32(layout, A: torch.Tensor, B: torch.Tensor,
                 out: torch.Tensor | None = None) -> torch.Tensor:
     """int32 C[M,N] = A(m,:) . B(:,n) (same layouts as int8_scaled_mm)."""
-    layout = _LAYOUTS[layout]
-    _bits(A, torch.int8), _bits(B, torch.int8)
-    M, N, K = _mnk(layout, A, B)
-    out = torch.empty((M, N), dtype=torch.int32, device=A.device) if out is None else out
-    with torch.cuda.device(A.device):
+    layout, M, N, K, dev = _mm_args(layout, A, B, torch.int8, out=out, out_dtype=torch.int32)
+    out = torch.empty((M, N), dtype=torch.int32, device=dev) if out is None else out
+    with torch.cuda.device(dev):
         st = lib.i8mp_int8_mm_i32(layout, M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(out),
-                                  _ld(out), _stream(A.device))
+                                  _ld(out), _stream(dev))
     _check(st, "i8mp_int8_mm_i32")
     return out
 
 
 def philox4x32_10(seed: int, offset: int, n_blocks: int, device="cuda") -> torch.Tensor:
     """uint32 words (returned as int32) [4 * n_blocks] of Philox4x32-10 blocks offset.."""
+    if n_blocks < 0:
+        raise ValueError(f"n_blocks must be >= 0, got {n_blocks}")
     out = torch.empty(4 * n_blocks, dtype=torch.int32, device=device)
-    with torch.cuda.device(out.device):
-        st = lib.i8mp_philox4x32_10(seed, offset, n_blocks, _ptr(out), _stream(out.device))
+    dev = _device(out)
+    with torch.cuda.device(dev):
+        st = lib.i8mp_philox4x32_10(seed, offset, n_blocks, _ptr(out), _stream(dev))
     _check(st, "i8mp_philox4x32_10")
     return out
 
@@ -288,20 +384,58 @@ def _opts(rounding, seed, offset):
     return _Opts(_ROUNDING[rounding], seed & (2**64 - 1), offset & (2**64 - 1))
 
 
+def _fwd_args(X, W, out, workspace):
+    """Checks of a forward chain's dense bf16 operands: X [M, K], W [N, K],
+    out [M, N]; returns (M, N, K, device)."""
+    _mat(X, "X", torch.bfloat16, dense=True)
+    M, K = X.shape
+    _mat(W, "W", torch.bfloat16, dense=True)
+    if W.shape[1] != K:
+        raise ValueError(f"W: {K} columns expected (X is {tuple(X.shape)}), got {tuple(W.shape)}")
+    N = W.shape[0]
+    if out is not None:
+        _mat(out, "out", torch.bfloat16, (M, N), dense=True)
+    if workspace is not None:
+        _workspace(workspace)
+    return M, N, K, _device(X, W, out, workspace)
+
+
+def _bwd_args(dY, X, W, dX, dW, workspace, colmax_x=None, colmax_w=None):
+    """Checks of a backward chain's dense bf16 tensors: dY [M, N], X [M, K],
+    W [N, K], dX [M, K], dW [N, K], colmax_x / colmax_w fp32 [K]; returns
+    (M, N, K, device)."""
+    _mat(dY, "dY", torch.bfloat16, dense=True)
+    M, N = dY.shape
+    _mat(W, "W", torch.bfloat16, dense=True)
+    if W.shape[0] != N:
+        raise ValueError(f"W: {N} rows expected (dY is {tuple(dY.shape)}), got {tuple(W.shape)}")
+    K = W.shape[1]
+    _mat(X, "X", torch.bfloat16, (M, K), dense=True)
+    if dX is not None:
+        _mat(dX, "dX", torch.bfloat16, (M, K), dense=True)
+    if dW is not None:
+        _mat(dW, "dW", torch.bfloat16, (N, K), dense=True)
+    if colmax_x is not None:
+        _vec(colmax_x, "colmax_x", K)
+    if colmax_w is not None:
+        _vec(colmax_w, "colmax_w", K)
+    if workspace is not None:
+        _workspace(workspace)
+    return M, N, K, _device(dY, X, W, dX, dW, workspace, colmax_x, colmax_w)
+
+
 def linear_fwd(X: torch.Tensor, W: torch.Tensor, rounding="rne", seed: int = 0, offset: int = 0,
                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Y = X @ W.T with both operands quantized row-wise over K (dense bf16 tensors)."""
-    _bits(X), _bits(W)
-    M, K = X.shape
-    N = W.shape[0]
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device) if out is None else out
+    M, N, K, dev = _fwd_args(X, W, out, workspace)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
     need = linear_workspace_bytes(M, N, K, False)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     o = _opts(rounding, seed, offset)
-    with torch.cuda.device(X.device):
+    with torch.cuda.device(dev):
         st = lib.i8mp_linear_fwd(_ptr(X), _ptr(W), _ptr(Y), M, N, K, ctypes.byref(o),
-                                 _ptr(workspace), workspace.numel(), _stream(X.device))
+                                 _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "i8mp_linear_fwd")
     return Y
 
@@ -311,20 +445,18 @@ def linear_fwd_colmax(X: torch.Tensor, W: torch.Tensor, rounding="rne", seed: in
                       workspace: torch.Tensor | None = None):
     """linear_fwd that also returns the column maxima of X and W (fp32 [K]
     each) for linear_bwd: (Y, colmax_x, colmax_w)."""
-    _bits(X), _bits(W)
-    M, K = X.shape
-    N = W.shape[0]
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device) if out is None else out
-    cx = torch.empty(K, dtype=torch.float32, device=X.device)
-    cw = torch.empty(K, dtype=torch.float32, device=X.device)
+    M, N, K, dev = _fwd_args(X, W, out, workspace)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    cx = torch.empty(K, dtype=torch.float32, device=dev)
+    cw = torch.empty(K, dtype=torch.float32, device=dev)
     need = linear_workspace_bytes(M, N, K, False)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     o = _opts(rounding, seed, offset)
-    with torch.cuda.device(X.device):
+    with torch.cuda.device(dev):
         st = lib.i8mp_linear_fwd_colmax(_ptr(X), _ptr(W), _ptr(Y), M, N, K, ctypes.byref(o),
                                         _ptr(cx), _ptr(cw), _ptr(workspace), workspace.numel(),
-                                        _stream(X.device))
+                                        _stream(dev))
     _check(st, "i8mp_linear_fwd_colmax")
     return Y, cx, cw
 
@@ -337,25 +469,20 @@ def linear_bwd(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, rounding="rne
     """(dX = dY @ W, dW = dY.T @ X), each quantized along its own contraction.
     colmax_x / colmax_w: the column maxima from linear_fwd_colmax (optional;
     the results are the same, the column-wise passes then read X / W once)."""
-    _bits(dY), _bits(X), _bits(W)
-    for c in (colmax_x, colmax_w):
-        if c is not None:
-            _bits(c, torch.float32)
-    M, N = dY.shape
-    K = W.shape[1]
+    M, N, K, dev = _bwd_args(dY, X, W, dX, dW, workspace, colmax_x, colmax_w)
     if want_dx and dX is None:
-        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device)
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     if want_dw and dW is None:
-        dW = torch.empty((N, K), dtype=torch.bfloat16, device=dY.device)
+        dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     need = linear_workspace_bytes(M, N, K, True)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dY.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     o = _opts(rounding, seed, offset)
-    with torch.cuda.device(dY.device):
+    with torch.cuda.device(dev):
         st = lib.i8mp_linear_bwd_colmax(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX if want_dx else None),
                                         _ptr(dW if want_dw else None), M, N, K, ctypes.byref(o),
                                         _ptr(colmax_x), _ptr(colmax_w), _ptr(workspace),
-                                        workspace.numel(), _stream(dY.device))
+                                        workspace.numel(), _stream(dev))
     _check(st, "i8mp_linear_bwd_colmax")
     return (dX if want_dx else None), (dW if want_dw else None)
 
@@ -367,13 +494,18 @@ def quantize_rowwise_fp8(x: torch.Tensor, q: torch.Tensor | None = None,
                          scale: torch.Tensor | None = None):
     """Row-wise FP8 quantization of bf16 ``x`` [R, C] -> (E4M3 codes as uint8 [R, C],
     fp32 scale [R]); ``codes.view(torch.float8_e4m3fn)`` gives torch's view of them."""
-    _bits(x)
+    _mat(x, "x", torch.bfloat16)
     R, C = x.shape
-    q = _empty_2d(R, C, torch.uint8, x.device) if q is None else q
-    scale = torch.empty(R, dtype=torch.float32, device=x.device) if scale is None else scale
-    with torch.cuda.device(x.device):
+    if q is not None:
+        _mat(q, "q", torch.uint8, (R, C))
+    if scale is not None:
+        _vec(scale, "scale", R)
+    dev = _device(x, q, scale)
+    q = _empty_2d(R, C, torch.uint8, dev) if q is None else q
+    scale = torch.empty(R, dtype=torch.float32, device=dev) if scale is None else scale
+    with torch.cuda.device(dev):
         st = lib.i8mp_quantize_rowwise_fp8(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
-                                           _stream(x.device))
+                                           _stream(dev))
     _check(st, "i8mp_quantize_rowwise_fp8")
     return q, scale
 
@@ -381,16 +513,23 @@ def quantize_rowwise_fp8(x: torch.Tensor, q: torch.Tensor | None = None,
 def quantize_colwise_fp8(x: torch.Tensor, q: torch.Tensor | None = None,
                          scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Column-wise FP8 quantization -> (E4M3 codes uint8 [R, C] in x's layout, fp32 scale [C])."""
-    _bits(x)
+    _mat(x, "x", torch.bfloat16)
     R, C = x.shape
-    q = _empty_2d(R, C, torch.uint8, x.device) if q is None else q
-    scale = torch.empty(C, dtype=torch.float32, device=x.device) if scale is None else scale
+    if q is not None:
+        _mat(q, "q", torch.uint8, (R, C))
+    if scale is not None:
+        _vec(scale, "scale", C)
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _device(x, q, scale, workspace)
+    q = _empty_2d(R, C, torch.uint8, dev) if q is None else q
+    scale = torch.empty(C, dtype=torch.float32, device=dev) if scale is None else scale
     need = colwise_workspace_bytes(R, C)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    with torch.cuda.device(x.device):
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         st = lib.i8mp_quantize_colwise_fp8(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
-                                           _ptr(workspace), workspace.numel(), _stream(x.device))
+                                           _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "i8mp_quantize_colwise_fp8")
     return q, scale
 
@@ -399,13 +538,11 @@ def fp8_scaled_mm(layout, A: torch.Tensor, scale_a: torch.Tensor, B: torch.Tenso
                   scale_b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 C[M,N] from E4M3 codes (uint8): fp32 sums of the exact products, then
     bf16((sum * scale_a[m]) * scale_b[n]).  Layouts as for int8_scaled_mm; K % 16 == 0."""
-    layout = _LAYOUTS[layout]
-    _bits(A, torch.uint8), _bits(B, torch.uint8)
-    M, N, K = _mnk(layout, A, B)
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if out is None else out
-    with torch.cuda.device(A.device):
+    layout, M, N, K, dev = _mm_args(layout, A, B, torch.uint8, scale_a, scale_b, out, torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    with torch.cuda.device(dev):
         st = lib.i8mp_fp8_scaled_mm(layout, M, N, K, _ptr(A), _ld(A), _ptr(scale_a), _ptr(B),
-                                    _ld(B), _ptr(scale_b), _ptr(out), _ld(out), _stream(A.device))
+                                    _ld(B), _ptr(scale_b), _ptr(out), _ld(out), _stream(dev))
     _check(st, "i8mp_fp8_scaled_mm")
     return out
 
@@ -414,13 +551,11 @@ def fp8_mm_f32(layout, A: torch.Tensor, B: torch.Tensor,
                out: torch.Tensor | None = None) -> torch.Tensor:
     """float32 C[M,N]: the matrix core's fp32 sums of E4M3 products (same layouts
     as fp8_scaled_mm, no scales)."""
-    layout = _LAYOUTS[layout]
-    _bits(A, torch.uint8), _bits(B, torch.uint8)
-    M, N, K = _mnk(layout, A, B)
-    out = torch.empty((M, N), dtype=torch.float32, device=A.device) if out is None else out
-    with torch.cuda.device(A.device):
+    layout, M, N, K, dev = _mm_args(layout, A, B, torch.uint8, out=out, out_dtype=torch.float32)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else out
+    with torch.cuda.device(dev):
         st = lib.i8mp_fp8_mm_f32(layout, M, N, K, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(out),
-                                 _ld(out), _stream(A.device))
+                                 _ld(out), _stream(dev))
     _check(st, "i8mp_fp8_mm_f32")
     return out
 
@@ -428,16 +563,14 @@ def fp8_mm_f32(layout, A: torch.Tensor, B: torch.Tensor,
 def linear_fwd_fp8(X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None):
     """Y = X @ W.T with both operands quantized row-wise to FP8 (E4M3) over K."""
-    _bits(X), _bits(W)
-    M, K = X.shape
-    N = W.shape[0]
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device) if out is None else out
+    M, N, K, dev = _fwd_args(X, W, out, workspace)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
     need = linear_workspace_bytes(M, N, K, False)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
-    with torch.cuda.device(X.device):
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         st = lib.i8mp_linear_fwd_fp8(_ptr(X), _ptr(W), _ptr(Y), M, N, K, _ptr(workspace),
-                                     workspace.numel(), _stream(X.device))
+                                     workspace.numel(), _stream(dev))
     _check(st, "i8mp_linear_fwd_fp8")
     return Y
 
@@ -446,16 +579,14 @@ def linear_bwd_fp8(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, want_dx: 
                    want_dw: bool = True, workspace: torch.Tensor | None = None):
     """(dX = dY @ W, dW = dY.T @ X) with FP8 (E4M3) operands, each quantized along
     its own contraction."""
-    _bits(dY), _bits(X), _bits(W)
-    M, N = dY.shape
-    K = W.shape[1]
-    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device) if want_dx else None
-    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dY.device) if want_dw else None
+    M, N, K, dev = _bwd_args(dY, X, W, None, None, workspace)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if want_dx else None
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if want_dw else None
     need = linear_workspace_bytes(M, N, K, True)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dY.device)
-    with torch.cuda.device(dY.device):
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
         st = lib.i8mp_linear_bwd_fp8(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX), _ptr(dW), M, N, K,
-                                     _ptr(workspace), workspace.numel(), _stream(dY.device))
+                                     _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "i8mp_linear_bwd_fp8")
     return dX, dW

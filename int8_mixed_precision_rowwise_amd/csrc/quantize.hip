@@ -1290,7 +1290,8 @@ hipError_t launch_quantize_rowwise_slabs(const uint16_t* x, int64_t rows, int64_
                                          int8_t* q, int64_t ldq, float* scale, float* colmax,
                                          int round, uint64_t seed, uint64_t offset, void* ws,
                                          bool finalize, hipStream_t stream) {
-  if (cols == 0) return hipSuccess;
+  // no columns: no maxima, but every row's scale is still written (0)
+  if (cols == 0) return launch_quantize_rowwise(x, rows, 0, ldx, q, ldq, scale, round, seed, offset, stream);
   const RowColmaxPlan p = rcm_plan(rows, cols);
   uint16_t* part = static_cast<uint16_t*>(ws);
   if (rows > 0) {
@@ -1358,7 +1359,11 @@ hipError_t launch_quantize_rowwise_colmax_pair(
     float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
     int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
     void* ws_b, int64_t cols, int round, uint64_t seed, hipStream_t stream) {
-  if (cols == 0) return hipSuccess;
+  if (cols == 0) {  // no maxima; the row scales are still written (0)
+    const hipError_t e = launch_quantize_rowwise(xa, rows_a, 0, ldxa, qa, ldqa, scale_a, round, seed, offset_a, stream);
+    if (e != hipSuccess) return e;
+    return launch_quantize_rowwise(xb, rows_b, 0, ldxb, qb, ldqb, scale_b, round, seed, offset_b, stream);
+  }
   const RowColmaxPlan pa = rcm_plan(rows_a, cols), pb = rcm_plan(rows_b, cols);
   if (!pa.fused || rows_a == 0 || rows_b == 0) {
     const hipError_t e = launch_quantize_rowwise_colmax(xa, rows_a, cols, ldxa, qa, ldqa, scale_a, colmax_a,

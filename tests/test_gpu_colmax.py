@@ -91,3 +91,67 @@ def test_linear_chains_with_column_maxima(rounding, rc, M, N, K):
             assert np.array_equal(tensor_bits(dX), dXo), f"dX ({want_dx}, {want_dw})"
         if want_dw:
             assert np.array_equal(tensor_bits(dW), dWo), f"dW ({want_dx}, {want_dw})"
+
+
+# Rows of exactly 512 * NV elements take the row passes without range checks
+# (the FULL kernels the 4096^3 step and the Llama-1B K = 2048 layers run, in
+# the paired launch of X's and W's rows); K in {1024, 2048, 4096, 8192}.  A
+# 4096-wide dY also takes them in the backward (dY's row pass, and W's and
+# dY's column passes over whole 512-column tiles).  Every output against the
+# oracle, both roundings.
+@pytest.mark.parametrize("rounding,rc", ROUNDINGS)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 1024), (300, 264, 2048), (300, 264, 4096),
+                                   (300, 264, 8192), (136, 4096, 1024)])
+def test_linear_chains_with_maxima_full_width_rows(rounding, rc, M, N, K):
+    t = linear_inputs(LinearShape("full_rows", M, N, K), seed=K + N, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
+    seed, off = 77, 3 << 44
+    Y, cx, cw = i8.linear_fwd_colmax(X, W, rounding, seed, off)
+    dX, dW = i8.linear_bwd(dY, X, W, rounding, seed, off, colmax_x=cx, colmax_w=cw)
+    torch.cuda.synchronize()
+    assert np.array_equal(tensor_bits(Y), oracle.linear_fwd(Xb, Wb, rc, seed, off)), "Y"
+    same_f32(cx, oracle.col_absmax(Xb), "colmax X")
+    same_f32(cw, oracle.col_absmax(Wb), "colmax W")
+    dXo, dWo = oracle.linear_bwd(dYb, Xb, Wb, rc, seed, off)
+    assert np.array_equal(tensor_bits(dX), dXo), "dX"
+    assert np.array_equal(tensor_bits(dW), dWo), "dW"
+
+
+def test_chains_with_maxima_and_an_empty_contraction():
+    """K = 0 (forward) and N = 0 (grad-input) with column-maxima pointers given
+    through the C ABI: the row scales of the empty rows are 0 and the outputs
+    +0, whatever the workspace held (filled with NaN bytes first)."""
+    import ctypes
+    L = i8.lib
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    M, N = 40, 24
+    o = i8._Opts(0, 0, 0)
+    cx = torch.full((4,), 7.0, device="cuda")
+    cw = torch.full((4,), 7.0, device="cuda")
+    ws = torch.full((i8.linear_workspace_bytes(M, N, 0, False) + 256,), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    for a, b in ((cx, cw), (cx, None), (None, cw)):  # the paired row pass and the single ones
+        ws.fill_(0xFF)
+        Y = torch.full((M, N), 3.0, dtype=torch.bfloat16, device="cuda")
+        st = L.i8mp_linear_fwd_colmax(None, None, P(Y), M, N, 0, ctypes.byref(o),
+                                      P(a) if a is not None else None, P(b) if b is not None else None,
+                                      P(ws), ws.numel(), sp)
+        torch.cuda.synchronize()
+        assert st == 0
+        assert (tensor_bits(Y) == 0).all(), "Y must be +0"
+    # grad-input with an empty contraction (N = 0): dX = dY @ W = 0
+    K = 48
+    X = torch.ones((M, K), dtype=torch.bfloat16, device="cuda")
+    W = torch.ones((0, K), dtype=torch.bfloat16, device="cuda")
+    dX = torch.full((M, K), 3.0, dtype=torch.bfloat16, device="cuda")
+    cx = torch.ones(K, device="cuda")
+    cw = torch.zeros(K, device="cuda")
+    wsb = torch.full((i8.linear_workspace_bytes(M, 0, K, True) + 256,), 0xFF, dtype=torch.uint8,
+                     device="cuda")
+    st = L.i8mp_linear_bwd_colmax(None, P(X), None, P(dX), None, M, 0, K, ctypes.byref(o), P(cx),
+                                  P(cw), P(wsb), wsb.numel(), sp)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert (tensor_bits(dX) == 0).all(), "dX must be +0"

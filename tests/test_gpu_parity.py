@@ -324,3 +324,48 @@ def test_repeat_runs_are_byte_identical():
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_two_streams_and_reordered_launches_give_the_same_bytes():
+    """Two layers' training steps (stochastic rounding; the first splits its
+    forward contraction, the second takes the paired full-width row passes)
+    run once on the current stream in order A then B, then again concurrently
+    on two other streams of the default priority, B's launches first: every
+    output is byte-identical (no kernel depends on timing, launch order or
+    what a previous call left in a workspace)."""
+    from workloads import LinearShape, linear_inputs
+    shapes = [LinearShape("det_a", 256, 512, 8192), LinearShape("det_b", 1024, 768, 4096)]
+    jobs = []
+    for k, s in enumerate(shapes):
+        t = linear_inputs(s, seed=100 + k, device="cuda")
+        ws_f = torch.empty(i8.linear_workspace_bytes(s.M, s.N, s.K, False), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(i8.linear_workspace_bytes(s.M, s.N, s.K, True), dtype=torch.uint8, device="cuda")
+        outs = [torch.empty((s.M, s.N), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((s.M, s.K), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((s.N, s.K), dtype=torch.bfloat16, device="cuda")]
+        jobs.append((t["X"], t["W"], t["dY"], ws_f, ws_b, outs))
+
+    def step(job, seed):
+        X, W, dY, ws_f, ws_b, (Y, dX, dW) = job
+        _, cx, cw = i8.linear_fwd_colmax(X, W, "sr", seed, 5 << 44, out=Y, workspace=ws_f)
+        i8.linear_bwd(dY, X, W, "sr", seed, 5 << 44, dX=dX, dW=dW, workspace=ws_b, colmax_x=cx, colmax_w=cw)
+
+    step(jobs[0], 1)
+    step(jobs[1], 2)
+    torch.cuda.synchronize()
+    ref = [[o.clone() for o in job[5]] for job in jobs]
+    for job in jobs:
+        for o in job[5]:
+            o.fill_(0)
+        job[3].fill_(0xA5)
+        job[4].fill_(0x5A)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        step(jobs[1], 2)
+    with torch.cuda.stream(s1):
+        step(jobs[0], 1)
+    torch.cuda.synchronize()
+    for k, job in enumerate(jobs):
+        for got, want, what in zip(job[5], ref[k], ("Y", "dX", "dW")):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"layer {k} {what}"
