@@ -195,10 +195,13 @@ def test_fp8_scaled_mm(layout, M, N, K):
 
 def test_fp8_shape_rules():
     z = lambda r, c: torch.zeros((r, c), dtype=torch.uint8, device="cuda")  # noqa: E731
-    s = torch.ones(64, device="cuda")
-    for layout, A, B in (("NT", z(4, 24), z(4, 24)), ("NN", z(4, 16), z(16, 3)), ("TN", z(16, 3), z(16, 4))):
-        with pytest.raises(i8.I8mpError):
-            i8.fp8_scaled_mm(layout, A, s, B, s)
+    s = lambda n: torch.ones(n, device="cuda")  # noqa: E731
+    # K = 24 (not a multiple of 16); N = 3 read down B's rows; M = 3 read down A's rows
+    for layout, A, B, M, N in (("NT", z(4, 24), z(4, 24), 4, 4), ("NN", z(4, 16), z(16, 3), 4, 3),
+                               ("TN", z(16, 3), z(16, 4), 3, 4)):
+        with pytest.raises(i8.I8mpError) as e:
+            i8.fp8_scaled_mm(layout, A, s(M), B, s(N))
+        assert e.value.status == 1
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
