@@ -13,7 +13,9 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates, frees or retains memory.  Scratch space comes in
- *     through the `ws` argument of the calls that need it.
+ *     through the `ws` argument of the calls that need it (the one
+ *     exception, i8mp_quantize_colwise_noalloc, uses a static device buffer
+ *     of the library's own).
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL is the null stream).  Buffers must stay valid until the stream
  *     work completes.
@@ -28,8 +30,9 @@
  *     (never outside that aligned 16-byte chunk); outputs are written only
  *     inside their rows.
  *   - Outputs must not overlap inputs.
- *   - The library is stateless and reentrant.  The device check (gfx950) is
- *     cached per device.
+ *   - The library is stateless and reentrant, except that calls of
+ *     i8mp_quantize_colwise_noalloc on one GPU share that GPU's static
+ *     scratch.  The device check (gfx950) is cached per device.
  */
 #ifndef I8MP_H
 #define I8MP_H
@@ -48,6 +51,7 @@ typedef enum {
   I8MP_EDEVICE = 3,    /* no current HIP device, or it is not gfx950 */
   I8MP_EHIP = 4,       /* a HIP launch reported an error */
   I8MP_EWORKSPACE = 5, /* workspace NULL or smaller than the query function returns */
+  I8MP_ESCRATCH = 6,   /* the problem needs more scratch than I8MP_STATIC_SCRATCH_BYTES */
 } i8mp_status;
 
 /* Rounding of the quantization step.  RNE: round half to even.  SR:
@@ -114,6 +118,25 @@ i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols,
                                   int8_t* q, int64_t ldq, float* scale, int32_t round,
                                   uint64_t seed, uint64_t offset, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/*
+ * i8mp_quantize_colwise for callers that cannot allocate memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments and results, with no workspace argument.
+ * The column-maxima scratch is a static device buffer of
+ * I8MP_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; nothing is allocated or freed by this call.
+ * Problems whose scratch, i8mp_quantize_colwise_workspace_bytes(rows, cols),
+ * exceeds that size return I8MP_ESCRATCH (about 2 bytes per column: up to
+ * some 2 million columns).  Every call on one GPU shares its buffer, so calls
+ * that overlap on one GPU (several streams or threads at once) race:
+ * serialize them, for instance on one stream.
+ */
+#define I8MP_STATIC_SCRATCH_BYTES (4u << 20)
+i8mp_status i8mp_quantize_colwise_noalloc(const uint16_t* x, int64_t rows, int64_t cols,
+                                          int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                          int32_t round, uint64_t seed, uint64_t offset,
+                                          void* stream);
 
 /*
  * Row-wise quantization that also returns each column's maximum magnitude,

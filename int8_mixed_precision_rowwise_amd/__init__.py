@@ -25,7 +25,7 @@ __all__ = [
     "colwise_workspace_bytes", "quantize_rowwise_colmax", "quantize_colwise_given_colmax",
     "rowwise_colmax_workspace_bytes", "linear_fwd_colmax", "quantize_rowwise_fp8",
     "quantize_colwise_fp8", "fp8_scaled_mm", "fp8_mm_f32", "linear_fwd_fp8", "linear_bwd_fp8",
-    "EXPORTED_SYMBOLS",
+    "quantize_colwise_noalloc", "STATIC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
 ]
 
 RNE, SR = 0, 1
@@ -33,6 +33,7 @@ NT, NN, TN = 0, 1, 2
 _LAYOUTS = {"NT": NT, "NN": NN, "TN": TN, NT: NT, NN: NN, TN: TN}
 _ROUNDING = {"rne": RNE, "sr": SR, RNE: RNE, SR: SR}
 MAX_CONTRACTION = 133144
+STATIC_SCRATCH_BYTES = 4 << 20  # the library's per-GPU scratch of i8mp_quantize_colwise_noalloc
 
 EXPORTED_SYMBOLS = (
     "i8mp_status_str", "i8mp_abi_version", "i8mp_quantize_rowwise",
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "i8mp_quantize_rowwise_colmax", "i8mp_quantize_colwise_given_colmax", "i8mp_linear_fwd_colmax",
     "i8mp_linear_bwd_colmax", "i8mp_quantize_rowwise_fp8", "i8mp_quantize_colwise_fp8",
     "i8mp_fp8_scaled_mm", "i8mp_fp8_mm_f32", "i8mp_linear_fwd_fp8", "i8mp_linear_bwd_fp8",
+    "i8mp_quantize_colwise_noalloc",
 )
 
 
@@ -87,6 +89,7 @@ def _load() -> ctypes.CDLL:
         "i8mp_fp8_mm_f32": ([i32, i64, i64, i64, p, i64, p, i64, p, i64, p], i32),
         "i8mp_linear_fwd_fp8": ([p, p, p, i64, i64, i64, p, sz, p], i32),
         "i8mp_linear_bwd_fp8": ([p, p, p, p, p, i64, i64, i64, p, sz, p], i32),
+        "i8mp_quantize_colwise_noalloc": ([p, i64, i64, i64, p, i64, p, i32, u64, u64, p], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -297,6 +300,24 @@ def quantize_colwise(x: torch.Tensor, rounding="rne", seed: int = 0, offset: int
                                        _ROUNDING[rounding], seed, offset, _ptr(workspace),
                                        workspace.numel(), _stream(dev))
     _check(st, "i8mp_quantize_colwise")
+    return q, scale
+
+
+def quantize_colwise_noalloc(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
+                             rounding="rne", seed: int = 0, offset: int = 0):
+    """quantize_colwise into caller-given q (int8 [R, C]) and scale (fp32 [C])
+    with no allocation at all: the library's static per-GPU scratch holds the
+    column maxima (STATIC_SCRATCH_BYTES; larger problems raise).  Calls that
+    overlap on one GPU share that scratch and race."""
+    _mat(x, "x", torch.bfloat16)
+    R, C = x.shape
+    _mat(q, "q", torch.int8, (R, C))
+    _vec(scale, "scale", C)
+    dev = _device(x, q, scale)
+    with torch.cuda.device(dev):
+        st = lib.i8mp_quantize_colwise_noalloc(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(scale),
+                                               _ROUNDING[rounding], seed, offset, _stream(dev))
+    _check(st, "i8mp_quantize_colwise_noalloc")
     return q, scale
 
 

@@ -211,11 +211,12 @@ const char* i8mp_status_str(i8mp_status s) {
     case I8MP_EDEVICE: return "no current HIP device, or the device is not gfx950";
     case I8MP_EHIP: return "HIP reported an error at launch";
     case I8MP_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case I8MP_ESCRATCH: return "problem needs more scratch than the library's static device buffer holds";
   }
   return "unknown status";
 }
 
-int32_t i8mp_abi_version(void) { return 1; }
+int32_t i8mp_abi_version(void) { return 2; }
 
 i8mp_status i8mp_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                   int8_t* q, int64_t ldq, float* scale, int32_t round,
@@ -249,6 +250,20 @@ i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols,
   if ((st = device_check()) != I8MP_OK) return st;
   return hip_status(i8mp::launch_quantize_colwise(x, rows, cols, ldx, q, ldq, scale, round, seed,
                                                   offset, ws, as_stream(stream)));
+}
+
+i8mp_status i8mp_quantize_colwise_noalloc(const uint16_t* x, int64_t rows, int64_t cols,
+                                          int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                          int32_t round, uint64_t seed, uint64_t offset,
+                                          void* stream) {
+  static_assert(I8MP_STATIC_SCRATCH_BYTES == i8mp::kStaticScratchBytes, "one scratch size");
+  i8mp_status st = validate_quant(x, rows, cols, ldx, q, ldq, scale, cols, round);
+  if (st != I8MP_OK) return st;
+  if (cols == 0) return I8MP_OK;
+  if (i8mp_quantize_colwise_workspace_bytes(rows, cols) > I8MP_STATIC_SCRATCH_BYTES) return I8MP_ESCRATCH;
+  if ((st = device_check()) != I8MP_OK) return st;
+  return hip_status(i8mp::launch_quantize_colwise_static(x, rows, cols, ldx, q, ldq, scale, round, seed,
+                                                         offset, as_stream(stream)));
 }
 
 size_t i8mp_quantize_rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols) {

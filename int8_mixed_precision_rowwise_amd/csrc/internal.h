@@ -21,6 +21,15 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
                                    int8_t* q, int64_t ldq, float* scale, int round, uint64_t seed,
                                    uint64_t offset, void* ws, hipStream_t stream);
 
+// The column-wise quantization with its slab maxima in the library's static
+// device scratch (kStaticScratchBytes per GPU, shared by every call on that
+// GPU) instead of a caller workspace; needs colwise_workspace_bytes(rows,
+// cols) <= kStaticScratchBytes (hipErrorInvalidValue otherwise).
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+hipError_t launch_quantize_colwise_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                          int8_t* q, int64_t ldq, float* scale, int round,
+                                          uint64_t seed, uint64_t offset, hipStream_t stream);
+
 // Row-wise quantization that also writes colmax[c] = max_r |x[r,c]| (fp32),
 // via slab maxima in ws.
 size_t rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols);

@@ -25,6 +25,9 @@
 #include "internal.h"
 #include "philox.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace i8mp {
 namespace {
 
@@ -1271,6 +1274,57 @@ hipError_t launch_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols
   return hipGetLastError();
 }
 
+
+// ---- column-wise quantization without a workspace argument ---------------
+//
+// The slab column maxima of the two-pass column quantize live in this static
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  Every call on one GPU shares
+// it, so calls that overlap on one GPU (on different streams, or from
+// different threads) race.  Nothing in it has to start at zero: the first
+// pass writes every slab entry the second pass reads.
+//
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current: its copy
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_quantize_colwise_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                          int8_t* q, int64_t ldq, float* scale, int round,
+                                          uint64_t seed, uint64_t offset, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  if (colwise_workspace_bytes(rows, cols) > kStaticScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_quantize_colwise(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, ws, stream);
+}
 
 size_t rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols) {
   const RowColmaxPlan p = rcm_plan(rows, cols);

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "i8mp.h")
 i8 = pytest.importorskip("int8_mixed_precision_rowwise_amd")
 L = i8.lib
 
-EINVAL, ERANGE, EDEVICE, EWORKSPACE = 1, 2, 3, 5
+EINVAL, ERANGE, EDEVICE, EWORKSPACE, ESCRATCH = 1, 2, 3, 5, 6
 A16 = 0x10000  # fake, 16-byte aligned device addresses: validation never dereferences them
 
 
@@ -36,8 +36,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert L.i8mp_abi_version() == 1
-    for s in range(6):
+    assert L.i8mp_abi_version() == 2
+    for s in range(7):
         assert L.i8mp_status_str(s)
     assert b"133144" in L.i8mp_status_str(ERANGE)
 
@@ -229,3 +229,22 @@ def test_product_package_never_imports_the_oracle():
             if fn.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower(), fn
+
+
+def test_colwise_noalloc_validation():
+    """The scratch-free column-wise pass validates like i8mp_quantize_colwise
+    and rejects problems whose scratch exceeds the static buffer."""
+    f = L.i8mp_quantize_colwise_noalloc
+    x, q, s = fake(1), fake(3), fake(5)
+    assert f(x, 4, 8, 8, q, 16, s, 7, 0, 0, None) == EINVAL
+    assert f(x, 4, 8, 4, q, 16, s, 0, 0, 0, None) == EINVAL
+    assert f(None, 4, 0, 8, None, 16, None, 0, 0, 0, None) == 0  # no columns: nothing to do
+    cap = i8.STATIC_SCRATCH_BYTES
+    big = 1
+    while L.i8mp_quantize_colwise_workspace_bytes(4, big) <= cap:
+        big *= 2
+    assert L.i8mp_quantize_colwise_workspace_bytes(4, big // 2) <= cap
+    # rows of `big` columns: x at 2*big bytes per row, q at big
+    xb, qb, sb = ctypes.c_void_p(A16 * 1), ctypes.c_void_p(A16 * 1 + 16 * big), ctypes.c_void_p(A16 * 1 + 32 * big)
+    assert f(xb, 4, big, big, qb, big, sb, 0, 0, 0, None) == ESCRATCH
+    assert b"static" in L.i8mp_status_str(ESCRATCH)
