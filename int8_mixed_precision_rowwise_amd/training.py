@@ -23,11 +23,21 @@ layer's step counter advances the counter offset by ``STEP_STRIDE`` per forward
 call, so every quantize pass of every step draws fresh numbers and a run is
 reproducible from the seed.  The backward of a step reuses its forward's
 (seed, offset): the six quantize passes of one step use offsets
-``offset + j * 2**40``, j = 0..5.
+``offset + j * 2**40``, j = 0..5.  The 64-bit offset holds ``STEPS_PER_KEY``
+steps; past that the key moves on (``step_key_offset``), so draws never repeat.
+
+The seed and the step counter are part of the module's state dict (its extra
+state), so a run resumed from a checkpoint continues the same stream.  Under
+activation checkpointing (``torch.utils.checkpoint.checkpoint`` with
+``use_reentrant=False`` and ``context_fn=sr_checkpoint_contexts``) the
+recomputed forward replays the (key, offset) of the original forward instead
+of drawing new numbers, so its activations and the gradients equal those of a
+run without checkpointing.
 """
 from __future__ import annotations
 
 import dataclasses
+import threading
 from typing import Callable, Optional
 
 import torch
@@ -35,9 +45,11 @@ import torch
 from . import linear_bwd, linear_bwd_fp8, linear_fwd, linear_fwd_colmax, linear_fwd_fp8
 
 __all__ = ["Int8MixedPrecisionConfig", "Int8MixedPrecisionLinearFunction",
-           "Int8MixedPrecisionLinear", "swap_linear_modules", "STEP_STRIDE", "module_seed"]
+           "Int8MixedPrecisionLinear", "swap_linear_modules", "STEP_STRIDE", "STEPS_PER_KEY",
+           "module_seed", "step_key_offset", "sr_checkpoint_contexts"]
 
 STEP_STRIDE = 8 << 40  # Philox blocks reserved per linear step (6 passes of 2**40 each, rounded up)
+STEPS_PER_KEY = (1 << 64) // STEP_STRIDE  # steps whose offsets fit the 64-bit block counter
 
 
 @dataclasses.dataclass(frozen=True)
@@ -74,6 +86,56 @@ def module_seed(base_seed: int, index: int) -> int:
     z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & 0xFFFFFFFFFFFFFFFF
     z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & 0xFFFFFFFFFFFFFFFF
     return z ^ (z >> 31)
+
+
+def step_key_offset(seed: int, step: int) -> tuple[int, int]:
+    """(Philox key, counter offset) of a module's step-th training forward.
+    Steps 0 .. STEPS_PER_KEY-1 use the module's seed with offset
+    step * STEP_STRIDE; each later run of STEPS_PER_KEY steps uses the key
+    module_seed(seed, step // STEPS_PER_KEY) (a SplitMix64 step away from the
+    seed) with the offsets starting again at 0, so no (key, offset) pair of a
+    module repeats."""
+    if step < 0:
+        raise ValueError(f"step must be >= 0, got {step}")
+    epoch, within = divmod(step, STEPS_PER_KEY)
+    key = seed if epoch == 0 else module_seed(seed, epoch)
+    return key, within * STEP_STRIDE
+
+
+class _CheckpointState(threading.local):
+    mode: Optional[str] = None  # None, "record" (original forward) or "replay" (recompute)
+    log: Optional[list] = None
+
+
+_ckpt = _CheckpointState()
+
+
+class _SrContext:
+    """Enters one of the two modes of a checkpointed region (see
+    sr_checkpoint_contexts); the previous mode comes back on exit."""
+
+    def __init__(self, mode: str, log: list):
+        self.mode, self.log = mode, log
+
+    def __enter__(self):
+        self.saved = (_ckpt.mode, _ckpt.log)
+        _ckpt.mode, _ckpt.log = self.mode, self.log
+        return self
+
+    def __exit__(self, *exc):
+        _ckpt.mode, _ckpt.log = self.saved
+        return False
+
+
+def sr_checkpoint_contexts():
+    """Context managers for ``torch.utils.checkpoint.checkpoint(fn, *args,
+    use_reentrant=False, context_fn=sr_checkpoint_contexts)``: during the
+    original forward every INT8 mixed-precision linear of the region records
+    the (key, offset) it drew with; during the recompute it replays them in
+    the same order instead of advancing its step.  One checkpointed region at
+    a time (no nesting)."""
+    log: list = []
+    return _SrContext("record", log), _SrContext("replay", log)
 
 
 def _as_rows(t: torch.Tensor, cols: int) -> torch.Tensor:
@@ -139,7 +201,10 @@ class Int8MixedPrecisionLinear(torch.nn.Linear):
     """Bias-free linear layer whose GEMMs run per ``config``.
 
     ``seed`` keys this module's stochastic-rounding stream; ``step`` counts its
-    forward calls (the Philox offset of a call is step * STEP_STRIDE)."""
+    training forward calls (step_key_offset gives the Philox key and offset of
+    a call).  Both are saved in the state dict as the module's extra state and
+    restored by load_state_dict, so a resumed run draws what an uninterrupted
+    one would."""
 
     def __init__(self, in_features: int, out_features: int,
                  config: Optional[Int8MixedPrecisionConfig] = None, seed: int = 0,
@@ -164,11 +229,35 @@ class Int8MixedPrecisionLinear(torch.nn.Linear):
         new.config, new.seed, new.step = config, seed, 0
         return new
 
-    def forward(self, x: torch.Tensor) -> torch.Tensor:
-        offset = self.step * STEP_STRIDE
+    def get_extra_state(self):
+        return {"seed": int(self.seed), "step": int(self.step)}
+
+    def set_extra_state(self, state):
+        if not isinstance(state, dict) or set(state) != {"seed", "step"}:
+            raise ValueError(f"expected {{'seed', 'step'}} extra state, got {state!r}")
+        seed, step = int(state["seed"]), int(state["step"])
+        if not (0 <= seed < 2**64 and step >= 0):
+            raise ValueError(f"seed must be in [0, 2**64) and step >= 0, got {seed}, {step}")
+        self.seed, self.step = seed, step
+
+    def _key_offset(self) -> tuple[int, int]:
+        """(key, offset) of this call; a training call outside a replay
+        advances the step."""
+        if _ckpt.mode == "replay" and self.training:
+            if not _ckpt.log or _ckpt.log[0][0] is not self:
+                raise RuntimeError("checkpoint recompute reached an INT8 mixed-precision linear "
+                                   "that the original forward did not (or in another order)")
+            return _ckpt.log.pop(0)[1]
+        ko = step_key_offset(self.seed, self.step)
         if self.training:
             self.step += 1
-        return Int8MixedPrecisionLinearFunction.apply(x, self.weight, self.config, self.seed, offset)
+            if _ckpt.mode == "record":
+                _ckpt.log.append((self, ko))
+        return ko
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        key, offset = self._key_offset()
+        return Int8MixedPrecisionLinearFunction.apply(x, self.weight, self.config, key, offset)
 
     def extra_repr(self) -> str:
         c = self.config

@@ -141,3 +141,68 @@ def test_fp8_mlp_matches_fp8_chains():
     for got, want, what in ((y.view(-1, N), Y2, "y"), (x.grad.view(-1, K1), dX, "dX"),
                             (model[0].weight.grad, dW1, "dW1"), (model[2].weight.grad, dW2, "dW2")):
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), what
+
+
+def _sr_mlp(seed_cfg=17):
+    K1, H, N = 256, 512, 192
+    W1 = gaussian_bf16(H, K1, seed=41, std=0.02).cuda()
+    W2 = gaussian_bf16(N, H, seed=42, std=0.02).cuda()
+    m = torch.nn.Sequential(torch.nn.Linear(K1, H, bias=False), torch.nn.ReLU(),
+                            torch.nn.Linear(H, N, bias=False)).to(torch.bfloat16).cuda()
+    with torch.no_grad():
+        m[0].weight.copy_(W1)
+        m[2].weight.copy_(W2)
+    return T.swap_linear_modules(m, T.Int8MixedPrecisionConfig(stochastic_rounding=True, seed=seed_cfg))
+
+
+def _sr_step(m, ckpt=None):
+    """One forward + backward; ckpt: None (no checkpointing), "bare"
+    (checkpointing without the contexts) or "replay" (with them)."""
+    from torch.utils.checkpoint import checkpoint
+    x = gaussian_bf16(128, 256, seed=43).cuda().requires_grad_()
+    G = gaussian_bf16(128, 192, seed=44, std=1e-3).cuda()
+    for p in m.parameters():
+        p.grad = None
+    if ckpt is None:
+        y = m(x)
+    elif ckpt == "bare":
+        y = checkpoint(m, x, use_reentrant=False)
+    else:
+        y = checkpoint(m, x, use_reentrant=False, context_fn=T.sr_checkpoint_contexts)
+    y.backward(G)
+    return [t.detach().clone() for t in (y, x.grad, m[0].weight.grad, m[2].weight.grad)]
+
+
+def _same_all(a, b):
+    return all(torch.equal(u.view(torch.int16), v.view(torch.int16)) for u, v in zip(a, b))
+
+
+def test_resumed_sr_run_equals_uninterrupted_run():
+    """Stochastic rounding: a model whose state dict (seed and step of every
+    swapped linear) is saved after two steps and loaded into a fresh model
+    (built with another seed) draws in its third step exactly what the
+    uninterrupted model draws: output and all gradients byte-identical."""
+    import io
+    a = _sr_mlp()
+    steps = [_sr_step(a) for _ in range(3)]
+    assert not _same_all(steps[0], steps[2])  # the step's draws matter
+    b = _sr_mlp()
+    _sr_step(b), _sr_step(b)
+    buf = io.BytesIO()
+    torch.save(b.state_dict(), buf)
+    buf.seek(0)
+    c = _sr_mlp(seed_cfg=12345)
+    c.load_state_dict(torch.load(buf, weights_only=True))
+    assert _same_all(_sr_step(c), steps[2])
+
+
+def test_checkpointed_sr_step_equals_plain_step():
+    """Activation checkpointing with sr_checkpoint_contexts: the recomputed
+    forward replays the original draws, so output and gradients equal the
+    run without checkpointing, step after step (and a recompute that drew
+    anew, without the contexts, would not)."""
+    a, b, c = _sr_mlp(), _sr_mlp(), _sr_mlp()
+    for _ in range(2):
+        plain = _sr_step(a)
+        assert _same_all(_sr_step(b, "replay"), plain)
+    assert not _same_all(_sr_step(c, "bare"), _sr_step(_sr_mlp()))

@@ -82,3 +82,69 @@ def test_fp8_config():
     with pytest.raises(ValueError):
         T.Int8MixedPrecisionConfig(fp8=True, stochastic_rounding=True)
     assert "codes=fp8_e4m3" in repr(T.Int8MixedPrecisionLinear(4, 4, c))
+
+
+def test_key_rotates_when_the_offsets_run_out():
+    assert T.STEPS_PER_KEY * T.STEP_STRIDE == 2**64
+    last = T.STEPS_PER_KEY - 1
+    assert T.step_key_offset(9, last) == (9, last * T.STEP_STRIDE)
+    assert T.step_key_offset(9, T.STEPS_PER_KEY) == (T.module_seed(9, 1), 0)
+    assert T.step_key_offset(9, 2 * T.STEPS_PER_KEY + 3) == (T.module_seed(9, 2), 3 * T.STEP_STRIDE)
+    with pytest.raises(ValueError):
+        T.step_key_offset(9, -1)
+
+
+def _recording(monkeypatch):
+    calls = []
+
+    def fake_apply(x, w, cfg, seed, offset):
+        calls.append((seed, offset))
+        return x @ w.t()
+
+    monkeypatch.setattr(T.Int8MixedPrecisionLinearFunction, "apply", staticmethod(fake_apply))
+    return calls
+
+
+def test_sr_state_is_in_the_state_dict(monkeypatch, tmp_path):
+    """seed and step travel with the state dict (also through torch.save and
+    a weights-only load), so a resumed module continues the stream."""
+    calls = _recording(monkeypatch)
+    cfg = T.Int8MixedPrecisionConfig(stochastic_rounding=True, seed=3)
+    m = T.swap_linear_modules(torch.nn.Sequential(torch.nn.Linear(4, 4, bias=False)).to(torch.bfloat16), cfg)
+    x = torch.zeros(2, 4, dtype=torch.bfloat16)
+    for _ in range(3):
+        m(x)
+    sd = m.state_dict()
+    assert sd["0._extra_state"] == {"seed": T.module_seed(3, 0), "step": 3}
+    path = tmp_path / "ckpt.pt"
+    torch.save(sd, path)
+    fresh = T.swap_linear_modules(torch.nn.Sequential(torch.nn.Linear(4, 4, bias=False)).to(torch.bfloat16),
+                                  T.Int8MixedPrecisionConfig(stochastic_rounding=True, seed=99))
+    fresh.load_state_dict(torch.load(path, weights_only=True))
+    assert (fresh[0].seed, fresh[0].step) == (m[0].seed, 3)
+    calls.clear()
+    m(x), fresh(x)
+    assert calls[0] == calls[1] == (T.module_seed(3, 0), 3 * T.STEP_STRIDE)
+    with pytest.raises(ValueError):
+        fresh[0].set_extra_state({"seed": -1, "step": 0})
+
+
+def test_checkpoint_recompute_replays_the_forward_draws(monkeypatch):
+    """Under torch.utils.checkpoint with sr_checkpoint_contexts, the
+    recomputed forward uses the original (key, offset) of every layer and the
+    step advances once per training forward, as without checkpointing."""
+    from torch.utils.checkpoint import checkpoint
+    calls = _recording(monkeypatch)
+    cfg = T.Int8MixedPrecisionConfig(stochastic_rounding=True, seed=5)
+    m = T.swap_linear_modules(torch.nn.Sequential(torch.nn.Linear(4, 8, bias=False), torch.nn.ReLU(),
+                                                  torch.nn.Linear(8, 4, bias=False)).to(torch.bfloat16), cfg)
+    x = torch.randn(3, 4, dtype=torch.bfloat16, requires_grad=True)
+    for step in range(2):
+        calls.clear()
+        y = checkpoint(m, x, use_reentrant=False, context_fn=T.sr_checkpoint_contexts)
+        y.float().sum().backward()
+        k0, k2 = T.module_seed(5, 0), T.module_seed(5, 1)
+        first = [(k0, step * T.STEP_STRIDE), (k2, step * T.STEP_STRIDE)]
+        assert calls == first + first  # forward, then the recompute with the same draws
+        assert m[0].step == m[2].step == step + 1
+    assert T._ckpt.mode is None and T._ckpt.log is None
