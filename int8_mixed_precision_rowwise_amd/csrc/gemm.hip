@@ -73,6 +73,12 @@ __device__ __forceinline__ constexpr int mnmajor_swz(int W, int k) {
 template <int W>
 __device__ __forceinline__ int mnmajor_off(int k, int c) { return k * W + ((c ^ mnmajor_swz(W, k)) << 4); }
 
+// Elementwise maximum of two pairs of packed 16-bit unsigned values.
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
 // Keep the first n (0..16) bytes of a 16-byte chunk.
 __device__ __forceinline__ uint4 keep_bytes(uint4 v, int n) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -563,6 +569,92 @@ struct Dma {
   }
 };
 
+// ---- column maxima reduced in a GEMM's prologue ----------------------------
+//
+// A linear chain's row-wise passes leave slab maxima of |x| (bf16 bit
+// patterns, [slabs][part_ld], see ColmaxJob) that still have to be reduced to
+// fp32 column maxima before the backward needs them.  Instead of a launch of
+// its own, workgroup g of the following GEMM reduces group g: 32 columns of
+// one tensor over all its slabs (at most kSideSlabs).  Its slab rows come
+// into a spare LDS region by the same LDS-DMA loads as the operand slabs,
+// issued just before them, so the reduction overlaps the wait for the first
+// operand slab.  Maximum is exact and order-free: the result is colmax
+// finalize's.
+constexpr int kSideSlabs = 256;
+constexpr int kSideBytes = kSideSlabs * 64;  // 32 columns x 2 bytes per slab row
+
+template <int NW>
+struct SideJob {
+  static constexpr int kInst = kSideBytes / 1024 / NW;  // 1 KiB loads per wave
+  v4u rsrc;
+  bool on;          // this workgroup has a group (workgroup-uniform)
+  int t;            // tensor of the group
+  int64_t c_first;  // first column of the group
+
+  __device__ __forceinline__ void init(const ColmaxJob& j, int64_t g) {
+    const int64_t gpt = (j.cols + 31) / 32;
+    on = j.n > 0 && g < j.n * gpt;
+    if (!on) return;
+    t = (int)(g / gpt);
+    c_first = (g % gpt) * 32;
+    const int64_t slabs = j.slabs[t];
+    // exactly the bytes of this group's columns, so nothing past the slab
+    // maxima is read: rows of part_ld elements, the last one from c_first on
+    const int64_t bytes = slabs > 0 ? ((slabs - 1) * j.part_ld + (j.part_ld - c_first)) * 2 : 0;
+    rsrc = Dma<64, true, NW>::make_rsrc(reinterpret_cast<const int8_t*>(j.part[t] + c_first), bytes);
+  }
+
+  // Instruction i of this wave: chunk k = (wave + NW i) * 64 + lane is slab row
+  // k / 4, 16-byte column chunk k % 4; it lands at side + 16 k.
+  __device__ __forceinline__ void issue(int8_t* side, int64_t part_ld, int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+      const int k = (wave + NW * i) * 64 + lane;
+      const uint32_t o = (uint32_t)((int64_t)(k >> 2) * part_ld * 2 + (k & 3) * 16);
+      const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(side + (wave + NW * i) * 1024)));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(l), "v"(o), "s"(rsrc)
+                   : "memory", "m0");
+    }
+  }
+
+  // After every wave's loads have landed (the caller's wait and barrier):
+  // thread tid takes column chunk tid % 4 of slab rows tid / 4, tid / 4 + NT / 4,
+  // ...; the 16 lanes of a chunk fold by shuffles, the waves through `red`.
+  __device__ __forceinline__ void reduce(const ColmaxJob& j, const int8_t* side, uint4 (*red)[4],
+                                         int tid, int wave, int lane) const {
+    constexpr int NT = 64 * NW;
+    const int chunk = tid & 3;
+    uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kSideSlabs * 4 / NT; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(side + ((tid >> 2) + i * (NT / 4)) * 64 + chunk * 16);
+      m[0] = max_u16x2(m[0], v.x), m[1] = max_u16x2(m[1], v.y);
+      m[2] = max_u16x2(m[2], v.z), m[3] = max_u16x2(m[3], v.w);
+    }
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = max_u16x2(m[e], (uint32_t)__shfl_xor((int)m[e], off));
+    if (lane < 4) red[wave][lane] = make_uint4(m[0], m[1], m[2], m[3]);
+    __syncthreads();
+    if (wave == 0 && lane < 4) {
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const uint4 o = red[w][lane];
+        m[0] = max_u16x2(m[0], o.x), m[1] = max_u16x2(m[1], o.y);
+        m[2] = max_u16x2(m[2], o.z), m[3] = max_u16x2(m[3], o.w);
+      }
+      const int64_t c0 = c_first + lane * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e < j.cols) j.colmax[t][c0 + e] = __uint_as_float(((m[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+    }
+  }
+};
+
 // MFMA 16x16x64 i8 operand/result layout: lane l supplies row l % 16 of its
 // first operand block and column l % 16 of its second, each with 16
 // contraction values (here k = 16 (l / 16) + 0..15 of the 64-deep slab; the
@@ -812,14 +904,16 @@ struct Mma<1> {
   }
 };
 
-template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC, int FMT = 0>
+template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC, int FMT = 0,
+          bool SIDE = false>
 __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
                                                               const int8_t* __restrict__ A, int64_t lda,
                                                               const float* __restrict__ sa,
                                                               const int8_t* __restrict__ B, int64_t ldb,
                                                               const float* __restrict__ sb,
                                                               void* __restrict__ Cv, int64_t ldc,
-                                                              int64_t kchunk, int64_t split_stride) {
+                                                              int64_t kchunk, int64_t split_stride,
+                                                              ColmaxJob side) {
   constexpr int NW = 2 * WGN, NT = 64 * NW;  // 2 x WGN waves
   constexpr int WM = BM / 2, WN = BN / WGN;
   typedef Mma<FMT> T;
@@ -834,8 +928,15 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * SLAB];
 
   __shared__ __attribute__((aligned(16))) float s_lds[BM + BN];  // scales of the tile
+  __shared__ __attribute__((aligned(1024))) int8_t side_lds[SIDE ? kSideBytes : 16];
+  __shared__ uint4 side_red[SIDE ? NW : 1][4];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  SideJob<NW> sj;
+  if constexpr (SIDE) {  // the column-maxima loads go out first (see SideJob)
+    sj.init(side, blockIdx.x);
+    if (sj.on) sj.issue(side_lds, side.part_ld, wave, lane);
+  }
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   int wg = blockIdx.x, nwg = gridDim.x;
   if constexpr (OUT_I32) {
@@ -896,6 +997,13 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   for (int s = 0; s < STAGES; ++s) {
     da.issue(lds + s * SLAB, s, K, wave);
     db.issue(lds + s * SLAB + A_BYTES, s, K, wave);
+  }
+  if constexpr (SIDE) {
+    if (sj.on) {  // workgroup-uniform
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(STAGES * PER));  // this wave's column-maxima loads have landed
+      lds_barrier();                                        // ... and every other wave's
+      sj.reduce(side, side_lds, side_red, t, wave, lane);
+    }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 1) * PER));  // slab 0 has landed
   lds_barrier();
@@ -981,14 +1089,29 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
 template <int BM, int BN, bool AK, bool BKM, bool OUT_I32, bool VEC>
 void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
             const float* sa, const int8_t* B, int64_t ldb, const float* sb, void* C, int64_t ldc,
-            hipStream_t stream) {
+            const ColmaxJob* side, hipStream_t stream) {
   // 256 x 256 tiles: 8 waves (2 per SIMD, 128 x 64 each) so one wave's MFMAs
   // run while the other waits on its slab-load issue; 128 x 128: 4 waves.
+  // side (pipelined kernel only) is a column-maxima reduction the caller has
+  // checked fits (side_fits).
   constexpr int WGN = BM >= 256 ? 4 : 2;
-  if (fast)
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0);
+  if (fast && side)
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC, 0, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0, *side);
+  else if (fast)
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0, ColmaxJob{});
   else
     gemm_i8_general<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
+}
+
+// Whether a column-maxima reduction can ride in the prologue of a pipelined
+// launch of `wgs` workgroups: one group of 32 columns per workgroup at most,
+// at most kSideSlabs slabs per tensor.
+bool side_fits(const ColmaxJob& j, int64_t wgs) {
+  if (j.n <= 0 || j.n > 2) return false;
+  const int64_t groups = j.n * ((j.cols + 31) / 32);
+  for (int t = 0; t < j.n; ++t)
+    if (j.slabs[t] > kSideSlabs) return false;
+  return groups <= wgs && j.part_ld * 2 * (int64_t)kSideSlabs < (int64_t(1) << 31);
 }
 
 // Whether the pipelined kernel can take a BM x BN tiling of this problem.
@@ -1009,19 +1132,24 @@ bool pipelined_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
 template <int BM, int BN, bool AK, bool BKM>
 hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const float* sa,
                const int8_t* B, int64_t ldb, const float* sb, uint16_t* Cb, int32_t* Ci,
-               int64_t ldc, hipStream_t stream) {
+               int64_t ldc, const ColmaxJob* side, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool fast = pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
+  if (side && (Ci || !(fast && side_fits(*side, tiles)))) {  // as a launch of its own
+    const hipError_t e = launch_colmax_finalize(*side, stream);
+    if (e != hipSuccess) return e;
+    side = nullptr;
+  }
   // packed stores of adjacent outputs need 16-byte aligned rows
   const uintptr_t c = Ci ? reinterpret_cast<uintptr_t>(Ci) : reinterpret_cast<uintptr_t>(Cb);
   const bool vec = Ci ? (ldc % 4 == 0 && c % 16 == 0) : (ldc % 8 == 0 && c % 16 == 0);
-  if (Ci) {
-    if (vec) launch<BM, BN, AK, BKM, true, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, stream);
-    else launch<BM, BN, AK, BKM, true, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, stream);
+  if (Ci) {  // the int32 hook: no column maxima ride along
+    if (vec) launch<BM, BN, AK, BKM, true, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, nullptr, stream);
+    else launch<BM, BN, AK, BKM, true, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, nullptr, stream);
   } else {
-    if (vec) launch<BM, BN, AK, BKM, false, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, stream);
-    else launch<BM, BN, AK, BKM, false, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, stream);
+    if (vec) launch<BM, BN, AK, BKM, false, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, side, stream);
+    else launch<BM, BN, AK, BKM, false, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, side, stream);
   }
   return hipGetLastError();
 }
@@ -1038,10 +1166,10 @@ int64_t big_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) 
 template <bool AK, bool BKM>
 hipError_t pick(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const float* sa,
                 const int8_t* B, int64_t ldb, const float* sb, uint16_t* Cb, int32_t* Ci,
-                int64_t ldc, hipStream_t stream) {
+                int64_t ldc, const ColmaxJob* side, hipStream_t stream) {
   if (big_tiles(M, N) >= kBigTileMin)
-    return run<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, stream);
-  return run<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, stream);
+    return run<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, side, stream);
+  return run<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, Cb, Ci, ldc, side, stream);
 }
 
 // ---- contraction split (the linear chains) -------------------------------
@@ -1125,15 +1253,25 @@ __global__ __launch_bounds__(256) void splitk_reduce(const int32_t* __restrict__
 template <bool AK, bool BKM>
 hipError_t run_split(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const int8_t* A,
                      int64_t lda, const float* sa, const int8_t* B, int64_t ldb, const float* sb,
-                     uint16_t* C, int64_t ldc, int32_t* P, hipStream_t stream) {
+                     uint16_t* C, int64_t ldc, int32_t* P, const ColmaxJob* side, hipStream_t stream) {
   const int64_t tiles = big_tiles(M, N);
   const int64_t plane = M * p.ldp;
-  gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true><<<dim3((unsigned)(tiles * p.splits)), 512, 0, stream>>>(
-      M, N, K, A, lda, nullptr, B, ldb, nullptr, P, p.ldp, p.kchunk, plane);
+  const dim3 grid((unsigned)(tiles * p.splits));
+  if (side && !side_fits(*side, tiles * p.splits)) {  // as a launch of its own
+    const hipError_t e = launch_colmax_finalize(*side, stream);
+    if (e != hipSuccess) return e;
+    side = nullptr;
+  }
+  if (side)
+    gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true, 0, true><<<grid, 512, 0, stream>>>(
+        M, N, K, A, lda, nullptr, B, ldb, nullptr, P, p.ldp, p.kchunk, plane, *side);
+  else
+    gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true><<<grid, 512, 0, stream>>>(
+        M, N, K, A, lda, nullptr, B, ldb, nullptr, P, p.ldp, p.kchunk, plane, ColmaxJob{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((N + 1023) / 1024), (unsigned)std::min<int64_t>(M, 65535));
-  splitk_reduce<<<grid, 256, 0, stream>>>(P, p.ldp, plane, p.splits, M, N, sa, sb,
+  const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)std::min<int64_t>(M, 65535));
+  splitk_reduce<<<rgrid, 256, 0, stream>>>(P, p.ldp, plane, p.splits, M, N, sa, sb,
                                           reinterpret_cast<__bf16*>(C), ldc);
   return hipGetLastError();
 }
@@ -1149,11 +1287,11 @@ hipError_t run_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t ld
   const int8_t* a = reinterpret_cast<const int8_t*>(A);
   const int8_t* b = reinterpret_cast<const int8_t*>(B);
   if (Cf)
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, true, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc, K, 0);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, true, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc, K, 0, ColmaxJob{});
   else if (vec)
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, ColmaxJob{});
   else
-    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0);
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, ColmaxJob{});
   return hipGetLastError();
 }
 
@@ -1203,16 +1341,22 @@ size_t gemm_split_workspace_bytes(int layout, int64_t M, int64_t N, int64_t K, i
 hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
                              int64_t lda, const float* sa, const int8_t* B, int64_t ldb,
                              const float* sb, uint16_t* C, int64_t ldc, void* ws,
-                             hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
+                             const ColmaxJob* side, hipStream_t stream) {
+  if (side && side->n <= 0) side = nullptr;
+  if (M == 0 || N == 0) return side ? launch_colmax_finalize(*side, stream) : hipSuccess;
   const SplitPlan p = K > 0 ? plan_for(layout, M, N, K, lda, ldb) : SplitPlan{1, K, 0};
-  if (p.splits < 2 || !ws)
-    return launch_gemm(layout, M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, stream);
+  if (p.splits < 2 || !ws) {
+    switch (layout) {
+      case 0: return pick<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, side, stream);
+      case 1: return pick<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, side, stream);
+      default: return pick<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, side, stream);
+    }
+  }
   int32_t* P = static_cast<int32_t*>(ws);
   switch (layout) {
-    case 0: return run_split<true, true>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, stream);
-    case 1: return run_split<true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, stream);
-    default: return run_split<false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, stream);
+    case 0: return run_split<true, true>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
+    case 1: return run_split<true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
+    default: return run_split<false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
   }
 }
 
@@ -1222,11 +1366,11 @@ hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t
   if (M == 0 || N == 0) return hipSuccess;
   switch (layout) {
     case 0:
-      return pick<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C_bf16, C_i32, ldc, stream);
+      return pick<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C_bf16, C_i32, ldc, nullptr, stream);
     case 1:
-      return pick<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C_bf16, C_i32, ldc, stream);
+      return pick<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C_bf16, C_i32, ldc, nullptr, stream);
     default:
-      return pick<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C_bf16, C_i32, ldc, stream);
+      return pick<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C_bf16, C_i32, ldc, nullptr, stream);
   }
 }
 

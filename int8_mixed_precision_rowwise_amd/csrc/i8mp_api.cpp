@@ -383,10 +383,22 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
   const int64_t kp = pad16(K);
   const int r = opts->round;
   hipError_t e = hipSuccess;
+  i8mp::ColmaxJob side{};  // X's and W's slab maxima, reduced in the GEMM's prologue
   if (colmax_x && colmax_w) {  // both row-wise passes (same width K) in one launch
     e = i8mp::launch_quantize_rowwise_colmax_pair(X, M, K, w.qx, kp, w.sx, colmax_x, pass_offset(opts->offset, 0),
                                                   w.part_x, W, N, K, w.qw, kp, w.sw, colmax_w,
-                                                  pass_offset(opts->offset, 1), w.part_w, K, r, opts->seed, s);
+                                                  pass_offset(opts->offset, 1), w.part_w, K, r, opts->seed,
+                                                  K == 0, s);
+    if (K > 0) {
+      side.n = 2;
+      side.cols = K;
+      side.part[0] = static_cast<const uint16_t*>(w.part_x);
+      side.part[1] = static_cast<const uint16_t*>(w.part_w);
+      side.colmax[0] = colmax_x;
+      side.colmax[1] = colmax_w;
+      i8mp::rowwise_colmax_geometry(M, K, &side.slabs[0], &side.part_ld);
+      i8mp::rowwise_colmax_geometry(N, K, &side.slabs[1], &side.part_ld);
+    }
   } else {
     e = colmax_x ? i8mp::launch_quantize_rowwise_colmax(X, M, K, K, w.qx, kp, w.sx, colmax_x, r, opts->seed,
                                                         pass_offset(opts->offset, 0), w.part_x, s)
@@ -399,7 +411,8 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
                                                    pass_offset(opts->offset, 1), s);
   }
   if (e == hipSuccess)
-    e = i8mp::launch_gemm_split(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, N, w.split, s);
+    e = i8mp::launch_gemm_split(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, N, w.split,
+                                side.n ? &side : nullptr, s);
   return hip_status(e);
 }
 
@@ -449,16 +462,22 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
   // dY's column maxima come from its row-wise pass when both GEMMs run
   const bool dy_colmax = want_dx && want_dw;
   hipError_t e = hipSuccess;
+  i8mp::ColmaxJob side{};  // dY's slab maxima, reduced in the grad-input GEMM's prologue
   if (want_dx) {
     // dX = dY @ W: dY row-wise over N, W column-wise over N, NN
     if (dy_colmax && colmax_w) {
-      // dY's row pass leaves its slab maxima in w.col; their reduction to dY's
-      // column maxima shares a launch with W's column pass
+      // dY's row pass leaves its slab maxima in w.col; the grad-input GEMM
+      // reduces them to dY's column maxima (needed by dY's column pass, after it)
       e = i8mp::launch_quantize_rowwise_slabs(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
                                               pass_offset(opts->offset, 2), w.col, false, s);
       if (e == hipSuccess)
-        e = i8mp::launch_finalize_and_colwise_given(w.col, M, N, w.cdy, W, N, K, K, colmax_w, w.qw, kp, w.sw,
-                                                    r, seed, pass_offset(opts->offset, 3), s);
+        e = i8mp::launch_quantize_colwise_given(W, N, K, K, colmax_w, w.qw, kp, w.sw, r, seed,
+                                                pass_offset(opts->offset, 3), s);
+      side.n = 1;
+      side.cols = N;
+      side.part[0] = static_cast<const uint16_t*>(w.col);
+      side.colmax[0] = w.cdy;
+      i8mp::rowwise_colmax_geometry(M, N, &side.slabs[0], &side.part_ld);
     } else {
       e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
                                                            pass_offset(opts->offset, 2), w.col, s)
@@ -471,7 +490,8 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
                                                      pass_offset(opts->offset, 3), w.col, s);
     }
     if (e == hipSuccess)
-      e = i8mp::launch_gemm_split(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, K, w.split, s);
+      e = i8mp::launch_gemm_split(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, K, w.split,
+                                  side.n ? &side : nullptr, s);
   }
   if (want_dw && e == hipSuccess) {
     // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
@@ -491,7 +511,7 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
                                                      pass_offset(opts->offset, 5), w.col, s);
     }
     if (e == hipSuccess)
-      e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, s);
+      e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, nullptr, s);
   }
   return hip_status(e);
 }

@@ -39,21 +39,12 @@ hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64
                                           void* ws, hipStream_t stream);
 
 // The row pass of launch_quantize_rowwise_colmax alone (finalize = false):
-// codes, scales and the slab maxima in ws, which
-// launch_finalize_and_colwise_given later reduces to colmax.
+// codes, scales and the slab maxima in ws, which a later ColmaxJob reduces
+// to colmax.
 hipError_t launch_quantize_rowwise_slabs(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                          int8_t* q, int64_t ldq, float* scale, float* colmax,
                                          int round, uint64_t seed, uint64_t offset, void* ws,
                                          bool finalize, hipStream_t stream);
-
-// One launch: fin_colmax[c] from the slab maxima a row pass of a fin_rows x
-// fin_cols tensor left in ws_fin, and the column-wise quantization of x with
-// its maxima given.  Same results as the two separate launches.
-hipError_t launch_finalize_and_colwise_given(const void* ws_fin, int64_t fin_rows, int64_t fin_cols,
-                                             float* fin_colmax, const uint16_t* x, int64_t rows,
-                                             int64_t cols, int64_t ldx, const float* colmax,
-                                             int8_t* q, int64_t ldq, float* scale, int round,
-                                             uint64_t seed, uint64_t offset, hipStream_t stream);
 
 // Column-wise quantization with the column maxima given: one pass.
 hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_t cols,
@@ -62,13 +53,15 @@ hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_
                                          hipStream_t stream);
 
 // Two tensors of the same width quantized row-wise with column maxima in one
-// launch (and one finalize); each has its own workspace of
-// rowwise_colmax_workspace_bytes(rows, cols).  Same results as two calls.
+// launch (and, with finalize, one reduction launch; without it the slab
+// maxima stay in ws_a / ws_b for a later ColmaxJob); each has its own
+// workspace of rowwise_colmax_workspace_bytes(rows, cols).  Same results as
+// two calls.
 hipError_t launch_quantize_rowwise_colmax_pair(
     const uint16_t* xa, int64_t rows_a, int64_t ldxa, int8_t* qa, int64_t ldqa, float* scale_a,
     float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
     int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
-    void* ws_b, int64_t cols, int round, uint64_t seed, hipStream_t stream);
+    void* ws_b, int64_t cols, int round, uint64_t seed, bool finalize, hipStream_t stream);
 
 // Two tensors quantized column-wise with their column maxima given, in one
 // launch.  Same results as two calls.
@@ -107,6 +100,23 @@ hipError_t launch_gemm_fp8(int layout, int64_t M, int64_t N, int64_t K, const ui
                            const float* sb, uint16_t* C, float* C_f32, int64_t ldc,
                            hipStream_t stream);
 
+// Column maxima still to be reduced from the slab maxima (bf16 bit patterns,
+// [slabs][part_ld]) that row-wise passes left in a workspace: up to two
+// tensors of the same width.  colmax[t][c] = max over slabs of part[t][s][c]
+// as fp32 (what colmax_finalize computes).
+struct ColmaxJob {
+  const uint16_t* part[2];
+  float* colmax[2];
+  int64_t slabs[2];
+  int64_t part_ld, cols;
+  int n;  // tensors (0: nothing to reduce)
+};
+// The slab-maxima geometry of a row pass with column maxima over rows x cols.
+void rowwise_colmax_geometry(int64_t rows, int64_t cols, int64_t* slabs, int64_t* part_ld);
+// The reduction as its own launch (colmax_finalize, or colmax_finalize2 for
+// two tensors).
+hipError_t launch_colmax_finalize(const ColmaxJob& job, hipStream_t stream);
+
 // int8 GEMM in layout 0 = NT, 1 = NN, 2 = TN.  Exactly one of (C_bf16 with
 // both scales) or C_i32 is non-null.
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
@@ -120,10 +130,14 @@ hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t
 // launch_gemm.  lda/ldb as in launch_gemm.
 size_t gemm_split_workspace_bytes(int layout, int64_t M, int64_t N, int64_t K, int64_t lda,
                                   int64_t ldb);
+// side: column maxima to reduce as well (or null).  The GEMM's workgroups
+// do it in their prologue, while their first operand slabs load, when the
+// problem allows (pipelined kernel, at most one group of 32 columns per
+// workgroup, at most 256 slabs); otherwise it runs as its own launch first.
 hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
                              int64_t lda, const float* sa, const int8_t* B, int64_t ldb,
                              const float* sb, uint16_t* C, int64_t ldc, void* ws,
-                             hipStream_t stream);
+                             const ColmaxJob* side, hipStream_t stream);
 
 hipError_t launch_philox(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
                          hipStream_t stream);

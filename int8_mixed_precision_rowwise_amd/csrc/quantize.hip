@@ -1113,6 +1113,8 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols
     launch_rows_nv<4>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
   else if (per_lane <= 8)
     launch_rows_nv<8>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane == 11)
+    launch_rows_nv<11>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
   else if (per_lane <= 12)
     launch_rows_nv<12>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
   else if (per_lane <= 16)
@@ -1159,6 +1161,8 @@ hipError_t launch_quantize_rowwise_fp8(const uint16_t* x, int64_t rows, int64_t 
     launch_rows_f8_nv<4>(x, rows, cols, ldx, q, ldq, scale, stream);
   else if (per_lane <= 8)
     launch_rows_f8_nv<8>(x, rows, cols, ldx, q, ldq, scale, stream);
+  else if (per_lane == 11)
+    launch_rows_f8_nv<11>(x, rows, cols, ldx, q, ldq, scale, stream);
   else if (per_lane <= 12)
     launch_rows_f8_nv<12>(x, rows, cols, ldx, q, ldq, scale, stream);
   else if (per_lane <= 16)
@@ -1204,6 +1208,8 @@ hipError_t launch_quantize_rowwise_colmax_fp8(const uint16_t* x, int64_t rows, i
       launch_rcm_f8_nv<4>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
     else if (per_lane <= 8)
       launch_rcm_f8_nv<8>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
+    else if (per_lane == 11)
+      launch_rcm_f8_nv<11>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
     else if (per_lane <= 12)
       launch_rcm_f8_nv<12>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
     else if (per_lane <= 16)
@@ -1359,6 +1365,8 @@ hipError_t launch_quantize_rowwise_slabs(const uint16_t* x, int64_t rows, int64_
         launch_rcm_nv<4>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
       else if (per_lane <= 8)
         launch_rcm_nv<8>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
+      else if (per_lane == 11)
+        launch_rcm_nv<11>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
       else if (per_lane <= 12)
         launch_rcm_nv<12>(p, x, rows, cols, ldx, q, ldq, scale, round, seed, offset, part, stream);
       else if (per_lane <= 16)
@@ -1412,7 +1420,7 @@ hipError_t launch_quantize_rowwise_colmax_pair(
     const uint16_t* xa, int64_t rows_a, int64_t ldxa, int8_t* qa, int64_t ldqa, float* scale_a,
     float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
     int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
-    void* ws_b, int64_t cols, int round, uint64_t seed, hipStream_t stream) {
+    void* ws_b, int64_t cols, int round, uint64_t seed, bool finalize, hipStream_t stream) {
   if (cols == 0) {  // no maxima; the row scales are still written (0)
     const hipError_t e = launch_quantize_rowwise(xa, rows_a, 0, ldxa, qa, ldqa, scale_a, round, seed, offset_a, stream);
     if (e != hipSuccess) return e;
@@ -1420,11 +1428,11 @@ hipError_t launch_quantize_rowwise_colmax_pair(
   }
   const RowColmaxPlan pa = rcm_plan(rows_a, cols), pb = rcm_plan(rows_b, cols);
   if (!pa.fused || rows_a == 0 || rows_b == 0) {
-    const hipError_t e = launch_quantize_rowwise_colmax(xa, rows_a, cols, ldxa, qa, ldqa, scale_a, colmax_a,
-                                                        round, seed, offset_a, ws_a, stream);
+    const hipError_t e = launch_quantize_rowwise_slabs(xa, rows_a, cols, ldxa, qa, ldqa, scale_a, colmax_a,
+                                                       round, seed, offset_a, ws_a, finalize, stream);
     if (e != hipSuccess) return e;
-    return launch_quantize_rowwise_colmax(xb, rows_b, cols, ldxb, qb, ldqb, scale_b, colmax_b, round, seed,
-                                          offset_b, ws_b, stream);
+    return launch_quantize_rowwise_slabs(xb, rows_b, cols, ldxb, qb, ldqb, scale_b, colmax_b, round, seed,
+                                         offset_b, ws_b, finalize, stream);
   }
   const RowColmaxJob a{xa, rows_a, ldxa, qa, ldqa, scale_a, offset_a, pa.rows_per_block, pa.slabs,
                        static_cast<uint16_t*>(ws_a)};
@@ -1439,14 +1447,34 @@ hipError_t launch_quantize_rowwise_colmax_pair(
     launch_rcm2_nv<4>(a, b, cols, pa.part_ld, round, seed, stream);
   else if (per_lane <= 8)
     launch_rcm2_nv<8>(a, b, cols, pa.part_ld, round, seed, stream);
+  else if (per_lane == 11)
+    launch_rcm2_nv<11>(a, b, cols, pa.part_ld, round, seed, stream);
   else if (per_lane <= 12)
     launch_rcm2_nv<12>(a, b, cols, pa.part_ld, round, seed, stream);
   else if (per_lane <= 16)
     launch_rcm2_nv<16>(a, b, cols, pa.part_ld, round, seed, stream);
   else
     launch_rcm2_nv<28>(a, b, cols, pa.part_ld, round, seed, stream);
-  colmax_finalize2<<<dim3((unsigned)((cols + 31) / 32), 2), kFinThreads, 0, stream>>>(
-      a.part, a.slabs, colmax_a, b.part, b.slabs, colmax_b, pa.part_ld, cols);
+  if (finalize)
+    colmax_finalize2<<<dim3((unsigned)((cols + 31) / 32), 2), kFinThreads, 0, stream>>>(
+        a.part, a.slabs, colmax_a, b.part, b.slabs, colmax_b, pa.part_ld, cols);
+  return hipGetLastError();
+}
+
+void rowwise_colmax_geometry(int64_t rows, int64_t cols, int64_t* slabs, int64_t* part_ld) {
+  const RowColmaxPlan p = rcm_plan(rows, cols);
+  *slabs = rows > 0 ? p.slabs : 0;
+  *part_ld = p.part_ld;
+}
+
+hipError_t launch_colmax_finalize(const ColmaxJob& j, hipStream_t stream) {
+  if (j.n <= 0 || j.cols == 0) return hipSuccess;
+  const dim3 blocks((unsigned)((j.cols + 31) / 32), (unsigned)j.n);
+  if (j.n == 1)
+    colmax_finalize<<<blocks, kFinThreads, 0, stream>>>(j.part[0], j.part_ld, j.slabs[0], j.cols, j.colmax[0]);
+  else
+    colmax_finalize2<<<blocks, kFinThreads, 0, stream>>>(j.part[0], j.slabs[0], j.colmax[0], j.part[1], j.slabs[1],
+                                                         j.colmax[1], j.part_ld, j.cols);
   return hipGetLastError();
 }
 
@@ -1479,66 +1507,6 @@ hipError_t launch_quantize_colwise_given_pair(
       quant_cols_given2<true, false><<<grid, kColThreads, 0, stream>>>(a, b, seed);
   } else {
     quant_cols_given2<false, true><<<grid, kColThreads, 0, stream>>>(a, b, seed);
-  }
-  return hipGetLastError();
-}
-
-namespace {
-// One launch for two independent jobs of the backward chain: reduce dY's slab
-// maxima to its column maxima (blocks [0, fin_blocks), as colmax_finalize) and
-// quantize W column-wise with its maxima given (the rest: one row band by one
-// column group per block, as quant_cols_given; two bands per block measured
-// slower here, 15.0 against 13.8 us at 4096 x 4096).  Both use 512-thread
-// blocks.
-template <bool SR, bool ALIGNED4>
-__global__ __launch_bounds__(kColThreads) void finalize_and_cols_given(
-    const uint16_t* __restrict__ part, int64_t part_ld, int64_t slabs, int64_t fin_cols,
-    float* __restrict__ fin_colmax, int64_t fin_blocks, ColGivenJob job, int64_t groups,
-    uint64_t seed) {
-  static_assert(kColThreads == kFinThreads, "one block size for both jobs");
-  __shared__ uint4 red[kFinWaves][4];
-  const int64_t b = blockIdx.x;
-  if (b < fin_blocks) {
-    finalize_block_at(part, part_ld, slabs, fin_cols, fin_colmax, red, b);
-  } else {
-    const int64_t k = b - fin_blocks;
-    cols_given_block<SR, ALIGNED4, 0>(job.x, job.rows, job.cols, job.ldx, job.colmax, job.scale, job.q,
-                                      job.ldq, seed, job.offset, k / groups, k % groups);
-  }
-}
-}  // namespace
-
-hipError_t launch_finalize_and_colwise_given(const void* ws_fin, int64_t fin_rows, int64_t fin_cols,
-                                             float* fin_colmax, const uint16_t* x, int64_t rows,
-                                             int64_t cols, int64_t ldx, const float* colmax,
-                                             int8_t* q, int64_t ldq, float* scale, int round,
-                                             uint64_t seed, uint64_t offset, hipStream_t stream) {
-  const RowColmaxPlan p = rcm_plan(fin_rows, fin_cols);
-  if (fin_cols == 0 || cols == 0) {
-    if (fin_cols > 0)
-      colmax_finalize<<<dim3((unsigned)((fin_cols + 31) / 32)), kFinThreads, 0, stream>>>(
-          static_cast<const uint16_t*>(ws_fin), p.part_ld, fin_rows > 0 ? p.slabs : 0, fin_cols, fin_colmax);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_quantize_colwise_given(x, rows, cols, ldx, colmax, q, ldq, scale, round, seed, offset, stream);
-  }
-  const int64_t span = (int64_t)kColTile * kColWaves;
-  const int64_t bands = max((int64_t)1, (rows + kColBand - 1) / kColBand);
-  const ColGivenJob job{x, rows, cols, ldx, colmax, scale, q, ldq, offset, bands, bands};
-  const int64_t groups = (cols + span - 1) / span;
-  const int64_t fin_blocks = (fin_cols + 31) / 32;
-  const int64_t total = fin_blocks + job.bands * groups;
-  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const uint16_t* part = static_cast<const uint16_t*>(ws_fin);
-  const int64_t slabs = fin_rows > 0 ? p.slabs : 0;
-  const dim3 grid((unsigned)total);
-  if (round == 1) {
-    if (cols % 4 == 0)
-      finalize_and_cols_given<true, true><<<grid, kColThreads, 0, stream>>>(part, p.part_ld, slabs, fin_cols, fin_colmax, fin_blocks, job, groups, seed);
-    else
-      finalize_and_cols_given<true, false><<<grid, kColThreads, 0, stream>>>(part, p.part_ld, slabs, fin_cols, fin_colmax, fin_blocks, job, groups, seed);
-  } else {
-    finalize_and_cols_given<false, true><<<grid, kColThreads, 0, stream>>>(part, p.part_ld, slabs, fin_cols, fin_colmax, fin_blocks, job, groups, seed);
   }
   return hipGetLastError();
 }
