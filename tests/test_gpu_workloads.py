@@ -4,7 +4,11 @@
   in full, bit for bit.
 * GEMM outputs of the library's linear forward / backward are compared on
   sampled positions plus whole bands of rows, bit for bit, against the
-  oracle's scaled matmul of the oracle's own quantized operands.
+  oracle's scaled matmul of the oracle's own quantized operands, and in full,
+  byte for byte, against the public scaled GEMM applied to the public
+  quantize passes' codes (which are oracle-checked in full): the chains'
+  own kernels (paired and split launches, the column maxima reduced in a
+  GEMM's prologue) reproduce every output of the primitives.
 * Stochastic rounding is additionally checked for unbiasedness over 256
   seeds on a [64, 64] slice, on the GPU's own draws.
 * The quotient x / s the kernels evaluate is checked exhaustively: every
@@ -110,8 +114,19 @@ def check_gemm(layout, Y, qa, sa, qb, sb, rng, what):
         raise AssertionError(f"{what}: {bad} of {len(ms)} sampled bf16 outputs differ")
 
 
+def same_in_full(chain_out, prim_out, what):
+    """The chain's bf16 output against the public GEMM's on the public codes,
+    every element, on the GPU."""
+    eq = chain_out.view(torch.int16) == prim_out.view(torch.int16)
+    if not bool(eq.all()):
+        bad = torch.nonzero(~eq)
+        raise AssertionError(f"{what}: {bad.shape[0]} of {eq.numel()} outputs differ from the public "
+                             f"GEMM on the public codes, first at {bad[0].tolist()}")
+
+
 def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad"), colmax=False):
-    """All quantized operands in full and the GEMM outputs on samples.  With
+    """All quantized operands in full, the GEMM outputs against the oracle on
+    samples and against the public GEMM on the public codes in full.  With
     colmax, the forward also returns X's and W's column maxima (checked in
     full) and the backward takes them."""
     t = linear_inputs(shape, seed=0, device="cuda")
@@ -123,8 +138,9 @@ def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")
     if "fwd" in gemms:
         ox = oracle_rowwise(Xb, rounding, seed, po(0))
         ow = oracle_rowwise(Wb, rounding, seed, po(1))
-        check_quant(i8.quantize_rowwise(X, rounding, seed, po(0)), ox, name + " X row")
-        check_quant(i8.quantize_rowwise(W, rounding, seed, po(1)), ow, name + " W row")
+        px, pw = i8.quantize_rowwise(X, rounding, seed, po(0)), i8.quantize_rowwise(W, rounding, seed, po(1))
+        check_quant(px, ox, name + " X row")
+        check_quant(pw, ow, name + " W row")
         cx = cw = None
         if colmax:
             Y, cx, cw = i8.linear_fwd_colmax(X, W, rounding, seed, offset)
@@ -134,7 +150,8 @@ def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")
         else:
             Y = i8.linear_fwd(X, W, rounding, seed, offset)
         check_gemm("NT", Y, ox[0], ox[1], ow[0], ow[1], rng, name + " Y")
-        del Y, ox, ow
+        same_in_full(Y, i8.int8_scaled_mm("NT", px[0], px[1], pw[0], pw[1]), name + " Y")
+        del Y, ox, ow, px, pw
     else:
         cx = cw = None
     dX, dW = i8.linear_bwd(dY, X, W, rounding, seed, offset,
@@ -143,16 +160,20 @@ def run_layer(shape, rounding, seed=0, offset=0, gemms=("fwd", "dgrad", "wgrad")
     if "dgrad" in gemms:
         ody = oracle_rowwise(dYb, rounding, seed, po(2))
         owc = oracle_colwise(Wb, rounding, seed, po(3))
-        check_quant(i8.quantize_rowwise(dY, rounding, seed, po(2)), ody, name + " dY row")
-        check_quant(i8.quantize_colwise(W, rounding, seed, po(3)), owc, name + " W col")
+        pdy, pwc = i8.quantize_rowwise(dY, rounding, seed, po(2)), i8.quantize_colwise(W, rounding, seed, po(3))
+        check_quant(pdy, ody, name + " dY row")
+        check_quant(pwc, owc, name + " W col")
         check_gemm("NN", dX, ody[0], ody[1], owc[0], owc[1], rng, name + " dX")
-        del ody, owc
+        same_in_full(dX, i8.int8_scaled_mm("NN", pdy[0], pdy[1], pwc[0], pwc[1]), name + " dX")
+        del ody, owc, pdy, pwc
     if "wgrad" in gemms:
         odc = oracle_colwise(dYb, rounding, seed, po(4))
         oxc = oracle_colwise(Xb, rounding, seed, po(5))
-        check_quant(i8.quantize_colwise(dY, rounding, seed, po(4)), odc, name + " dY col")
-        check_quant(i8.quantize_colwise(X, rounding, seed, po(5)), oxc, name + " X col")
+        pdc, pxc = i8.quantize_colwise(dY, rounding, seed, po(4)), i8.quantize_colwise(X, rounding, seed, po(5))
+        check_quant(pdc, odc, name + " dY col")
+        check_quant(pxc, oxc, name + " X col")
         check_gemm("TN", dW, odc[0], odc[1], oxc[0], oxc[1], rng, name + " dW")
+        same_in_full(dW, i8.int8_scaled_mm("TN", pdc[0], pdc[1], pxc[0], pxc[1]), name + " dW")
     torch.cuda.empty_cache()
 
 
@@ -179,7 +200,7 @@ def test_step_contraction_split(rounding, M, N, K):
     run_layer(LinearShape(f"split_{M}x{N}x{K}", M, N, K), rounding, seed=7, offset=3, colmax=True)
 
 
-@pytest.mark.parametrize("layer", ["llama1b_down_proj", "llama1b_gate_proj"])
+@pytest.mark.parametrize("layer", ["llama1b_down_proj", "llama1b_gate_proj", "llama1b_k_proj"])
 def test_llama1b_layer_with_column_maxima(layer):
     """Llama-1B linears at 32768 tokens (5632-wide rows of X, resp. dY) through
     the column-maxima chains."""
@@ -194,7 +215,7 @@ def test_llama1b_layer_rne(layer):
     run_layer(shape, "rne")
 
 
-@pytest.mark.parametrize("layer", ["llama1b_k_proj", "llama1b_down_proj"])
+@pytest.mark.parametrize("layer", [s.name for s in llama_1b_layers()])
 def test_llama1b_layer_sr(layer):
     """The same layers with stochastic rounding in every quantize pass."""
     shape = next(s for s in llama_1b_layers() if s.name == layer)
@@ -227,12 +248,20 @@ def test_sr_unbiased_over_256_seeds_on_gpu():
         assert abs(z) < 5
 
 
-@pytest.mark.parametrize("layer", ["llama3_8b_k_proj", "llama3_8b_down_proj", "llama3_8b_lm_head"])
+@pytest.mark.parametrize("layer", [s.name for s in llama3_8b_layers()])
 def test_llama3_8b_layer_rne(layer):
     """Llama-3-8B-shaped linears at 8192 tokens, including the 128256-wide LM
     head (grad-input contraction 128256, inside the int32 bound)."""
     shape = next(s for s in llama3_8b_layers() if s.name == layer)
     run_layer(shape, "rne")
+
+
+def test_llama3_8b_lm_head_with_column_maxima():
+    """The LM head [4096 -> 128256] at 8192 tokens through the column-maxima
+    chains: dY's 128256-wide rows take the banded two-pass row kernel, and its
+    column maxima are reduced in the grad-input GEMM's prologue or launch."""
+    shape = next(s for s in llama3_8b_layers() if s.name == "llama3_8b_lm_head")
+    run_layer(shape, "rne", seed=5, colmax=True)
 
 
 @pytest.mark.parametrize("rounding", ["rne", "sr"])
