@@ -261,6 +261,7 @@ def main():
         ctx["context_other_rounding_step"] = other_rounding(chain_step, r, step_ms, args, stream, gemm_ops)
         ctx["context_sr_quantize_passes"] = sr_passes(A, sets, n, args.kernel_iters, stream)
         ctx["context_gemm_cold_vs_warm"] = gemm_cold_warm(A, n, args.kernel_iters, stream, records)
+        ctx["context_mfma_power_ceiling"] = mfma_ceiling(A, prim["qX"], breakdown, stream)
     if not args.no_context and not args.only_step:
         ctx["context_torch_bf16_matmul_tflops"] = torch_bf16(sets[0], stream, gemm_ops)
         ctx["context_autograd_layer_step_ms"] = autograd_step(i8, sets[0], args.rounding, seed, stream)
@@ -502,6 +503,33 @@ def gemm_cold_warm(A, n, iters, stream, records):
     del ops
     torch.cuda.empty_cache()
     return res
+
+
+def mfma_ceiling(A, codes, breakdown, stream):
+    """The matrix cores' sustained rate on the GEMM's own work with the data
+    path taken away (i8mp_mfma_rate_probe: the GEMM's launch shape and wave
+    tile, operands in registers, 32 rounds = 2 * 4096^3 operations, the op
+    count of one 4096^3 GEMM), on the step's quantized Gaussian codes and on
+    uniform random bytes (the chip's power draw depends on the bits).  The
+    GEMMs' share of this ceiling says how much of the gap to the 5.0 POP/s
+    figure the kernel itself leaves."""
+    import torch
+    i8 = A.i8
+    flat = codes.reshape(-1)
+    rnd = torch.randint(-128, 128, (flat.numel(),), dtype=torch.int8, device=flat.device,
+                        generator=torch.Generator(device=flat.device).manual_seed(3))
+    sink = torch.empty(i8.MFMA_PROBE_SINK_INTS, dtype=torch.int32, device=flat.device)
+    rounds = 32
+    ops = rounds * 2.0**32
+    out = {}
+    for tag, c in (("quantized_gaussian_codes", flat), ("uniform_random_bytes", rnd)):
+        us = time_us(lambda: i8.mfma_rate_probe(c, rounds, sink), stream, 20, warm=5)
+        tops = ops / us / 1e6
+        out[tag] = {"us": round(us, 2), "tops": round(tops, 1), "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
+    ceil = out["quantized_gaussian_codes"]["tops"]
+    out["gemm_share_of_ceiling"] = {k: round(breakdown[k]["tops"] / ceil, 4)
+                                    for k in ("gemm_NT_fwd", "gemm_NN_dgrad", "gemm_TN_wgrad")}
+    return out
 
 
 def torch_bf16(inputs, stream, gemm_ops):

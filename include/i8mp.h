@@ -25,7 +25,8 @@
  *     that fails validation launches nothing and writes nothing.
  *   - Alignment: base pointers of bf16/int8/int32 matrices are 16-byte
  *     aligned and ld * element size is a multiple of 16 bytes; scale vectors
- *     are 4-byte aligned.  Any sizes >= 0 are accepted.  Reads of an input
+ *     are 4-byte aligned.  The INT8 entry points accept any sizes >= 0; the
+ *     FP8 GEMM entry points state their own shape rules.  Reads of an input
  *     may touch bytes between the end of a row and the next 16-byte boundary
  *     (never outside that aligned 16-byte chunk); outputs are written only
  *     inside their rows.
@@ -81,9 +82,15 @@ typedef struct {
   uint64_t offset;
 } i8mp_linear_opts;
 
+/* A fixed, human-readable description of a status code (never NULL; the
+ * string lives as long as the library).  The codes are this library's own
+ * error reporting; the pages report errors as Python exceptions
+ * ("Integrate INT8 mixed-precision from torchao 0.7", the device guard and
+ * the checks the recipe runs before training). */
 const char* i8mp_status_str(i8mp_status s);
 
-/* Version of this ABI (incremented on any signature change). */
+/* Version of this ABI (incremented on any signature change).  Bindings
+ * compare it with the version they were written for. */
 int32_t i8mp_abi_version(void);
 
 /*
@@ -113,6 +120,8 @@ i8mp_status i8mp_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols,
  *   ws: scratch of at least i8mp_quantize_colwise_workspace_bytes(rows, cols)
  *       bytes, 256-byte aligned; its contents on entry do not matter.
  */
+/* Bytes of scratch i8mp_quantize_colwise needs for rows x cols (the slab
+ * column maxima of its first pass); 0 for cols = 0 or invalid sizes. */
 size_t i8mp_quantize_colwise_workspace_bytes(int64_t rows, int64_t cols);
 i8mp_status i8mp_quantize_colwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                   int8_t* q, int64_t ldq, float* scale, int32_t round,
@@ -151,6 +160,9 @@ i8mp_status i8mp_quantize_colwise_noalloc(const uint16_t* x, int64_t rows, int64
  *   ws: scratch of at least i8mp_quantize_rowwise_colmax_workspace_bytes(rows,
  *       cols) bytes, 256-byte aligned; its contents on entry do not matter.
  */
+/* Bytes of scratch i8mp_quantize_rowwise_colmax needs for rows x cols (slab
+ * column maxima, and for rows over 14336 elements the row-segment maxima);
+ * 0 for cols = 0 or invalid sizes. */
 size_t i8mp_quantize_rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols);
 i8mp_status i8mp_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
                                          int64_t ldx, int8_t* q, int64_t ldq, float* scale,
@@ -188,7 +200,10 @@ i8mp_status i8mp_int8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K,
                                 int64_t ldc, void* stream);
 
 /* The integer accumulators alone, C = int32 [M x N] (same layouts, same
- * kernels without the scale epilogue).  For checking the int32 sums. */
+ * kernels without the scale epilogue): the "INT8 matmul" of "Quantized model
+ * training", section "Speed benchmarks > Matmul" (int8 x int8 -> int32 in the
+ * three layouts), before any scaling.  For checking the int32 sums, which must
+ * equal the exact integer dot products (K <= I8MP_MAX_CONTRACTION). */
 i8mp_status i8mp_int8_mm_i32(int32_t layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
                              int64_t lda, const int8_t* B, int64_t ldb, int32_t* C, int64_t ldc,
                              void* stream);
@@ -198,6 +213,26 @@ i8mp_status i8mp_int8_mm_i32(int32_t layout, int64_t M, int64_t N, int64_t K, co
  * seed.  out: uint32 [4 * n_blocks], 16-byte aligned.  For checking draws. */
 i8mp_status i8mp_philox4x32_10(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
                                void* stream);
+
+/*
+ * Measurement hook: how fast the INT8 matrix cores run the scaled GEMM's
+ * multiply-accumulate work alone under the chip's power limit.  The GEMM's
+ * launch shape (256 workgroups of 8 waves) and per-wave tile (8 x 4
+ * v_mfma_i32_16x16x64_i8 blocks) with operands held in registers: each wave
+ * loads 24 KiB of `codes` (two sets of fragments, at its own 1 KiB-aligned
+ * origin inside the buffer) once, then issues rounds x 2 x 32 MFMAs,
+ * alternating the two sets, i.e. rounds x 2^32 integer operations in total.
+ * The codes' bit patterns matter: the chip's power draw, and so its clock,
+ * depends on them.  sink receives one int32 per thread (a checksum of the
+ * accumulators) so no work is elided.
+ *   codes: int8 [codes_bytes], 16-byte aligned, codes_bytes >= I8MP_MFMA_PROBE_MIN_BYTES
+ *   rounds: 0 .. 2^24
+ *   sink: int32 [I8MP_MFMA_PROBE_SINK_INTS], not overlapping codes
+ */
+#define I8MP_MFMA_PROBE_MIN_BYTES (24 * 1024)
+#define I8MP_MFMA_PROBE_SINK_INTS (256 * 512)
+i8mp_status i8mp_mfma_rate_probe(const int8_t* codes, int64_t codes_bytes, int64_t rounds,
+                                 int32_t* sink, void* stream);
 
 /*
  * One linear layer, Y = X @ W.T ("Quantized model training", section "INT8
@@ -211,6 +246,9 @@ i8mp_status i8mp_philox4x32_10(uint64_t seed, uint64_t offset, int64_t n_blocks,
  * before the fp32 epilogue: results equal i8mp_int8_scaled_mm's).  Its
  * contents on entry do not matter and are not kept.
  */
+/* Bytes of workspace the forward (backward = 0) or backward (backward = 1)
+ * chain needs for an M x N x K layer (the same for its _colmax and FP8
+ * forms); 0 for invalid sizes. */
 size_t i8mp_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t backward);
 i8mp_status i8mp_linear_fwd(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
                             int64_t N, int64_t K, const i8mp_linear_opts* opts, void* ws,

@@ -25,7 +25,7 @@ __all__ = [
     "colwise_workspace_bytes", "quantize_rowwise_colmax", "quantize_colwise_given_colmax",
     "rowwise_colmax_workspace_bytes", "linear_fwd_colmax", "quantize_rowwise_fp8",
     "quantize_colwise_fp8", "fp8_scaled_mm", "fp8_mm_f32", "linear_fwd_fp8", "linear_bwd_fp8",
-    "quantize_colwise_noalloc", "STATIC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
+    "quantize_colwise_noalloc", "STATIC_SCRATCH_BYTES", "mfma_rate_probe", "EXPORTED_SYMBOLS",
 ]
 
 RNE, SR = 0, 1
@@ -43,7 +43,7 @@ EXPORTED_SYMBOLS = (
     "i8mp_quantize_rowwise_colmax", "i8mp_quantize_colwise_given_colmax", "i8mp_linear_fwd_colmax",
     "i8mp_linear_bwd_colmax", "i8mp_quantize_rowwise_fp8", "i8mp_quantize_colwise_fp8",
     "i8mp_fp8_scaled_mm", "i8mp_fp8_mm_f32", "i8mp_linear_fwd_fp8", "i8mp_linear_bwd_fp8",
-    "i8mp_quantize_colwise_noalloc",
+    "i8mp_quantize_colwise_noalloc", "i8mp_mfma_rate_probe",
 )
 
 
@@ -90,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "i8mp_linear_fwd_fp8": ([p, p, p, i64, i64, i64, p, sz, p], i32),
         "i8mp_linear_bwd_fp8": ([p, p, p, p, p, i64, i64, i64, p, sz, p], i32),
         "i8mp_quantize_colwise_noalloc": ([p, i64, i64, i64, p, i64, p, i32, u64, u64, p], i32),
+        "i8mp_mfma_rate_probe": ([p, i64, i64, p, p], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -392,6 +393,26 @@ def philox4x32_10(seed: int, offset: int, n_blocks: int, device="cuda") -> torch
         st = lib.i8mp_philox4x32_10(seed, offset, n_blocks, _ptr(out), _stream(dev))
     _check(st, "i8mp_philox4x32_10")
     return out
+
+
+MFMA_PROBE_SINK_INTS = 256 * 512
+
+
+def mfma_rate_probe(codes: torch.Tensor, rounds: int, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Launch the matrix-core throughput probe (rounds x 2^32 integer operations
+    on fragments taken from ``codes``, int8, at least 24 KiB, contiguous) on the
+    current stream; returns the int32 sink.  Time it with events around the call."""
+    _tensor(codes, "codes", torch.int8)
+    if not codes.is_contiguous() or codes.numel() < 24 * 1024:
+        raise ValueError("codes: contiguous int8 tensor of at least 24 KiB expected")
+    if sink is None:
+        sink = torch.empty(MFMA_PROBE_SINK_INTS, dtype=torch.int32, device=codes.device)
+    _vec(sink, "sink", MFMA_PROBE_SINK_INTS, torch.int32)
+    dev = _device(codes, sink)
+    with torch.cuda.device(dev):
+        st = lib.i8mp_mfma_rate_probe(_ptr(codes), codes.numel(), rounds, _ptr(sink), _stream(dev))
+    _check(st, "i8mp_mfma_rate_probe")
+    return sink
 
 
 # --------------------------------------------------------------------------- linear layer

@@ -1086,6 +1086,55 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
 }
 
 
+// ---- matrix-core throughput probe ------------------------------------------
+//
+// The INT8 GEMM's matrix-core work with everything else taken away: the
+// GEMM's launch shape (256 workgroups of 8 waves, two waves per SIMD) and its
+// per-wave tile (8 x 4 blocks of 16 x 16, 128 accumulator registers), with the
+// operands in registers.  Each wave loads two slabs' worth of fragments (real
+// codes, so the operand bits toggle as in the GEMM) once, then issues
+// `rounds` x 2 x 32 v_mfma_i32_16x16x64_i8, alternating the two fragment sets.
+// Measures how fast the chip runs this work under its power limit.
+__global__ __launch_bounds__(512) void mfma_rate_probe(const int8_t* __restrict__ codes, int64_t span,
+                                                       int64_t rounds, int32_t* __restrict__ sink) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 8 + (t >> 6);
+  // this wave's 24 fragments of 1 KiB, consecutive in the codes (wrapping)
+  const int8_t* base = codes + (wave * 24 * 1024) % span;
+  v4i a0[8], b0[4], a1[8], b1[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a0[i] = *reinterpret_cast<const v4i*>(base + i * 1024 + lane * 16);
+    a1[i] = *reinterpret_cast<const v4i*>(base + (12 + i) * 1024 + lane * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    b0[j] = *reinterpret_cast<const v4i*>(base + (8 + j) * 1024 + lane * 16);
+    b1[j] = *reinterpret_cast<const v4i*>(base + (20 + j) * 1024 + lane * 16);
+  }
+  v4i acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+  for (int64_t r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0[j], a0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1[j], a1[i], acc[i][j], 0, 0, 0);
+  }
+  int32_t h = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h ^= acc[i][j].x ^ acc[i][j].y ^ acc[i][j].z ^ acc[i][j].w;
+  sink[(int64_t)blockIdx.x * 512 + t] = h;
+}
+
 template <int BM, int BN, bool AK, bool BKM, bool OUT_I32, bool VEC>
 void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
             const float* sa, const int8_t* B, int64_t ldb, const float* sb, void* C, int64_t ldc,
@@ -1358,6 +1407,13 @@ hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const 
     case 1: return run_split<true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
     default: return run_split<false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
   }
+}
+
+hipError_t launch_mfma_rate_probe(const int8_t* codes, int64_t bytes, int64_t rounds, int32_t* sink,
+                                  hipStream_t stream) {
+  const int64_t span = (bytes - 24 * 1024) / 1024 * 1024 + 1024;  // fragment origins a wave may take
+  mfma_rate_probe<<<dim3(kMfmaProbeWorkgroups), 512, 0, stream>>>(codes, span, rounds, sink);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,

@@ -216,7 +216,7 @@ const char* i8mp_status_str(i8mp_status s) {
   return "unknown status";
 }
 
-int32_t i8mp_abi_version(void) { return 2; }
+int32_t i8mp_abi_version(void) { return 3; }
 
 i8mp_status i8mp_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                   int8_t* q, int64_t ldq, float* scale, int32_t round,
@@ -344,6 +344,19 @@ i8mp_status i8mp_philox4x32_10(uint64_t seed, uint64_t offset, int64_t n_blocks,
   i8mp_status st = device_check();
   if (st != I8MP_OK) return st;
   return hip_status(i8mp::launch_philox(seed, offset, n_blocks, out, as_stream(stream)));
+}
+
+i8mp_status i8mp_mfma_rate_probe(const int8_t* codes, int64_t codes_bytes, int64_t rounds,
+                                 int32_t* sink, void* stream) {
+  if (!codes || !aligned(codes, 16) || codes_bytes < I8MP_MFMA_PROBE_MIN_BYTES || codes_bytes >= kMaxDim)
+    return I8MP_EINVAL;
+  if (rounds < 0 || rounds > (int64_t(1) << 24)) return I8MP_EINVAL;
+  if (!sink || !aligned(sink, 4)) return I8MP_EINVAL;
+  if (overlap(vec_range(codes, codes_bytes, 1), vec_range(sink, I8MP_MFMA_PROBE_SINK_INTS, 4))) return I8MP_EINVAL;
+  static_assert(I8MP_MFMA_PROBE_SINK_INTS == i8mp::kMfmaProbeWorkgroups * 512, "one int32 per probe thread");
+  i8mp_status st = device_check();
+  if (st != I8MP_OK) return st;
+  return hip_status(i8mp::launch_mfma_rate_probe(codes, codes_bytes, rounds, sink, as_stream(stream)));
 }
 
 size_t i8mp_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t backward) {

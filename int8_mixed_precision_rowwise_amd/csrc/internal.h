@@ -142,4 +142,12 @@ hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const 
 hipError_t launch_philox(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
                          hipStream_t stream);
 
+// The matrix-core throughput probe: kMfmaProbeWorkgroups workgroups of 512
+// threads; each wave reads 24 KiB of codes at its own origin (a multiple of
+// 1 KiB, wrapping within `bytes`, which must be at least 24 KiB) and writes
+// one int32 per thread to sink.
+constexpr int kMfmaProbeWorkgroups = 256;
+hipError_t launch_mfma_rate_probe(const int8_t* codes, int64_t bytes, int64_t rounds, int32_t* sink,
+                                  hipStream_t stream);
+
 }  // namespace i8mp

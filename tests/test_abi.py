@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert L.i8mp_abi_version() == 2
+    assert L.i8mp_abi_version() == 3
     for s in range(7):
         assert L.i8mp_status_str(s)
     assert b"133144" in L.i8mp_status_str(ERANGE)
@@ -248,3 +248,13 @@ def test_colwise_noalloc_validation():
     xb, qb, sb = ctypes.c_void_p(A16 * 1), ctypes.c_void_p(A16 * 1 + 16 * big), ctypes.c_void_p(A16 * 1 + 32 * big)
     assert f(xb, 4, big, big, qb, big, sb, 0, 0, 0, None) == ESCRATCH
     assert b"static" in L.i8mp_status_str(ESCRATCH)
+
+
+def test_mfma_probe_validation():
+    f = L.i8mp_mfma_rate_probe
+    codes, sink = fake(1), ctypes.c_void_p(A16 * 100)
+    assert f(None, 1 << 20, 4, sink, None) == EINVAL
+    assert f(codes, 1000, 4, sink, None) == EINVAL  # fewer than 24 KiB
+    assert f(codes, 1 << 20, -1, sink, None) == EINVAL
+    assert f(codes, 1 << 20, 4, None, None) == EINVAL
+    assert f(codes, 1 << 20, 4, ctypes.c_void_p(A16 * 2), None) == EINVAL  # sink inside codes
