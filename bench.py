@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context measurements (sweep, Llama layers, ablation, ...)")
+    ap.add_argument("--context", default=None,
+                    help="comma-separated context measurements to run (and no others): other_rounding, "
+                         "sr_passes, elementwise, cold_warm, mfma_ceiling, torch_bf16, torch_int8, autograd, fp8, "
+                         "single_linear, square_sweep, quantize_large, llama1b, ablation, llama3_8b")
     ap.add_argument("--only-step", action="store_true",
                     help="the timed step and its per-kernel timing only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -203,10 +207,11 @@ def main():
 
     def chain_step(i, rr=r):
         """The step as the library runs it: i8mp_linear_fwd_colmax (X's and W's
-        row passes in one launch, their column maxima reduced in one more, the
-        NT GEMM), then i8mp_linear_bwd_colmax (dY's row pass; dY's maxima
-        finalized in the launch of W's column pass; NN GEMM; dY's and X's
-        column passes in one launch; TN GEMM): 8 launches."""
+        row passes in one launch, leaving slab maxima of their columns; the NT
+        GEMM, which reduces those slabs to X's and W's column maxima in its
+        prologue), then i8mp_linear_bwd_colmax (dY's row pass; W's column
+        pass; the NN GEMM, reducing dY's slabs in its prologue; dY's and X's
+        column passes in one launch; the TN GEMM): 7 launches."""
         X, W, dY = sets[i % args.sets]
         o = i8._Opts(rr, seed, (i % 1024) << 44)
         st = L.i8mp_linear_fwd_colmax(p(X), p(W), p(Y), M, N, K, ctypes.byref(o), p(cX), p(cW), p(ws_fwd),
@@ -250,6 +255,16 @@ def main():
     frac = achieved / PEAK_INT8_TOPS
     quant_frac = {k: v["frac_hbm_peak"] for k, v in breakdown.items() if k.startswith("quant")}
 
+    # the chain's quantize launches (paired, with the column maxima reduced in
+    # the GEMM prologues) cannot be timed apart through the C ABI: charge them
+    # the step's time beyond its three GEMMs (each timed on the step's codes)
+    q_us = step_ms * 1e3 - sum(breakdown[k]["us"] for k in gemms)
+    q_bytes = 6 * quant_bytes(n, n, n)
+    chain_quant = {"us": round(q_us, 2), "gbs": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
+                   "frac_hbm_peak": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                   "note": "step time minus the three GEMMs' times, against the six passes' algorithmic bytes; "
+                           "the prologue work of the chain's GEMMs counts as quantize time"}
+
     records = [{"config": f"square_{n}_step", "shape": [M, N, K], "layout": k.split("_")[1] if k.startswith("gemm") else None,
                 "kernel": k, **v} for k, v in breakdown.items()]
     records.append({"config": f"square_{n}_step", "shape": [M, N, K], "layout": None,
@@ -257,21 +272,38 @@ def main():
                     "tops": round(value, 1)})
 
     ctx = {}
-    if not args.only_step:
-        ctx["context_other_rounding_step"] = other_rounding(chain_step, r, step_ms, args, stream, gemm_ops)
-        ctx["context_sr_quantize_passes"] = sr_passes(A, sets, n, args.kernel_iters, stream)
-        ctx["context_gemm_cold_vs_warm"] = gemm_cold_warm(A, n, args.kernel_iters, stream, records)
-        ctx["context_mfma_power_ceiling"] = mfma_ceiling(A, prim["qX"], breakdown, stream)
-    if not args.no_context and not args.only_step:
-        ctx["context_torch_bf16_matmul_tflops"] = torch_bf16(sets[0], stream, gemm_ops)
-        ctx["context_autograd_layer_step_ms"] = autograd_step(i8, sets[0], args.rounding, seed, stream)
-        ctx["context_fp8_step"] = fp8_step(i8, sets, M, N, K, stream, gemm_ops)
-        ctx["context_single_linear_256x512x512"] = single_linear_ctx(i8, stream, records)
-        ctx["context_square_sweep_vs_torch_bf16"] = context_square_sweep(i8, dev, stream, records)
-        ctx["context_quantize_llama1b_sizes"] = context_quantize_large(i8, dev, stream, records)
-        ctx["context_llama1b_7_linears_fwd_bwd"] = context_layers_both(i8, dev, stream, records)
-        ctx["context_llama1b_ablation_int8_gemms"] = context_ablation(i8, dev, stream, records)
-        ctx["context_llama3_8b_linears_and_lm_head_fwd_bwd"] = context_llama3_8b_layers(i8, dev, stream, records)
+    runs = (
+        ("step", "other_rounding", "context_other_rounding_step",
+         lambda: other_rounding(chain_step, r, step_ms, args, stream, gemm_ops)),
+        ("step", "sr_passes", "context_sr_quantize_passes", lambda: sr_passes(A, sets, n, args.kernel_iters, stream)),
+        ("step", "elementwise", "context_elementwise_reference", lambda: elementwise_reference(sets, args.kernel_iters, stream)),
+        ("step", "cold_warm", "context_gemm_cold_vs_warm", lambda: gemm_cold_warm(A, n, args.kernel_iters, stream, records)),
+        ("step", "mfma_ceiling", "context_mfma_power_ceiling", lambda: mfma_ceiling(A, prim["qX"], breakdown, stream)),
+        ("wide", "torch_bf16", "context_torch_bf16_matmul_tflops", lambda: torch_bf16(sets[0], stream, gemm_ops)),
+        ("wide", "torch_int8", "context_torch_int_mm_hipblaslt", lambda: torch_int8_mm(sets, prim, args.kernel_iters,
+                                                                                        stream, gemm_ops)),
+        ("wide", "autograd", "context_autograd_layer_step_ms",
+         lambda: autograd_step(i8, sets[0], args.rounding, seed, stream)),
+        ("wide", "fp8", "context_fp8_step", lambda: fp8_step(i8, sets, M, N, K, stream, gemm_ops)),
+        ("wide", "single_linear", "context_single_linear_256x512x512", lambda: single_linear_ctx(i8, stream, records)),
+        ("wide", "square_sweep", "context_square_sweep_vs_torch_bf16",
+         lambda: context_square_sweep(i8, dev, stream, records)),
+        ("wide", "quantize_large", "context_quantize_llama1b_sizes", lambda: context_quantize_large(i8, dev, stream, records)),
+        ("wide", "llama1b", "context_llama1b_7_linears_fwd_bwd", lambda: context_layers_both(i8, dev, stream, records)),
+        ("wide", "ablation", "context_llama1b_ablation_int8_gemms", lambda: context_ablation(i8, dev, stream, records)),
+        ("wide", "llama3_8b", "context_llama3_8b_linears_and_lm_head_fwd_bwd",
+         lambda: context_llama3_8b_layers(i8, dev, stream, records)),
+    )
+    chosen = None if args.context is None else set(args.context.split(","))
+    if chosen is not None and not chosen <= {nm for _, nm, _, _ in runs}:
+        raise SystemExit(f"--context: unknown name(s) {sorted(chosen - {nm for _, nm, _, _ in runs})}")
+    for group, nm, key, fn in runs:
+        if chosen is not None:
+            on = nm in chosen
+        else:
+            on = not args.only_step and (group == "step" or not args.no_context)
+        if on:
+            ctx[key] = fn()
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -307,7 +339,8 @@ def main():
             "gemm_frac_int8_peak": {"target": TARGET_GEMM_FRAC, **{k: breakdown[k]["frac_int8_peak"] for k in gemms},
                                     "share_of_target_dominant": round(frac / TARGET_GEMM_FRAC, 3)},
             "quant_frac_hbm_peak": {"target": TARGET_QUANT_FRAC, **quant_frac,
-                                    "share_of_target_worst": round(min(quant_frac.values()) / TARGET_QUANT_FRAC, 3)},
+                                    "share_of_target_worst": round(min(quant_frac.values()) / TARGET_QUANT_FRAC, 3),
+                                    "chain_passes_by_subtraction": chain_quant},
         },
         "breakdown": breakdown,
         "step_gemm_frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
@@ -394,7 +427,9 @@ def step_breakdown(A, sets, prim, r, seed, iters, stream):
     b["gemm_TN_wgrad"] = gemm_entry(time_us(gemm(2, N, K, M, P["qdYc"], P["sdYc"], P["qXc"], P["sXc"]), stream, iters),
                                     N, K, M)
     for nm in ("quant_row_X", "quant_row_W", "quant_row_dY"):
-        b[nm]["note"] = "row pass with column maxima + its finalize launch"
+        b[nm]["note"] = ("public i8mp_quantize_rowwise_colmax: the row pass (slab maxima) + a colmax_finalize "
+                         "launch; the chain pairs X's and W's row passes in one launch and reduces the slabs "
+                         "in the next GEMM's prologue")
     return b
 
 
@@ -466,6 +501,52 @@ def sr_passes(A, sets, n, iters, stream):
                              "unit": "T lane-ops/s", "frac": round(ach / PEAK_VALU_LANE_OPS, 4)}
             out[f"{nm}_{tag}"] = e
     return out
+
+
+def elementwise_reference(sets, iters, stream):
+    """What a plain streaming kernel reaches on the same bytes and the same
+    cold inputs: torch's bf16 copy of an n x n tensor (4 bytes moved per
+    element) and of two such tensors stacked (the paired passes' byte count),
+    its source rotating over the input sets exactly as the quantize passes'
+    do (more than the 256 MB MALL holds)."""
+    import torch
+    src1 = [t for s in sets for t in s]
+    src2 = [torch.cat([src1[i], src1[(i + 1) % len(src1)]]) for i in range(0, len(src1), 2)]
+    d1 = torch.empty_like(src1[0])
+    d2 = torch.empty_like(src2[0])
+    k = [0]
+
+    def copy(dst, srcs):
+        def f():
+            k[0] += 1
+            dst.copy_(srcs[k[0] % len(srcs)])
+        return f
+
+    out = {}
+    for nm, fn, src in (("copy_bf16_single", copy(d1, src1), src1[0]), ("copy_bf16_pair", copy(d2, src2), src2[0])):
+        us = time_us(fn, stream, iters)
+        gbs = src.numel() * 4 / (us * 1e-6) / 1e9
+        out[nm] = {"us": round(us, 2), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del src2, d1, d2
+    torch.cuda.empty_cache()
+    return out
+
+
+def torch_int8_mm(sets, prim, iters, stream, gemm_ops):
+    """hipBLASLt's int8 GEMM through torch._int_mm (int32 output, no scales)
+    on the step's codes in the forward layout, as a library reference for the
+    GEMM's fraction of the INT8 peak."""
+    import torch
+    a, b = prim["qX"], prim["qW"]
+    try:
+        out = torch._int_mm(a, b.t())
+        torch.cuda.synchronize()
+    except Exception as e:  # not every torch build routes int8 GEMMs to hipBLASLt
+        return {"unavailable": str(e).splitlines()[0][:200]}
+    us = time_us(lambda: torch._int_mm(a, b.t()), stream, iters)
+    del out
+    return {"layout": "NT", "us": round(us, 2), "tops": round(gemm_ops / us / 1e6, 1),
+            "frac_int8_peak": round(gemm_ops / us / 1e6 / PEAK_INT8_TOPS, 4), "output": "int32"}
 
 
 def gemm_cold_warm(A, n, iters, stream, records):
@@ -732,8 +813,9 @@ def layer_steps(i8, dev, stream, shapes, prefix, iters, rounding, records, confi
             per[nm]["bf16_us"] = round(t16, 1)
             tot16 += t16
         o = 3 * 2.0 * M * N * K
-        records.append({"config": config, "shape": [M, N, K], "layout": None, "kernel": "linear_fwd_colmax+linear_bwd",
-                        "rounding": rounding, "us": round(t8, 1), "tops": round(o / t8 / 1e6, 1)})
+        records.append({"config": config, "layer": nm, "shape": [M, N, K], "layout": None,
+                        "kernel": "linear_fwd_colmax+linear_bwd", "rounding": rounding, "us": round(t8, 1),
+                        "tops": round(o / t8 / 1e6, 1)})
         tot8 += t8
         ops += o
         del t, X, W, dY, Y, dX, dW, wsf, wsb
@@ -792,7 +874,8 @@ def context_ablation(i8, dev, stream, records):
 
             us = time_us(step, stream, 5, warm=2)
             tot[tag] += us
-            records.append({"config": f"llama1b_ablation_{tag}", "shape": [shape.M, shape.N, shape.K], "layout": None,
+            records.append({"config": f"llama1b_ablation_{tag}", "layer": shape.name.replace("llama1b_", ""),
+                            "shape": [shape.M, shape.N, shape.K], "layout": None,
                             "kernel": "autograd_linear_fwd_bwd", "us": round(us, 1)})
             del lin
         del t, X, W, dY, xg

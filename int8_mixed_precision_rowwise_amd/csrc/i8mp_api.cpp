@@ -480,12 +480,11 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
     // dX = dY @ W: dY row-wise over N, W column-wise over N, NN
     if (dy_colmax && colmax_w) {
       // dY's row pass leaves its slab maxima in w.col; the grad-input GEMM
-      // reduces them to dY's column maxima (needed by dY's column pass, after it)
-      e = i8mp::launch_quantize_rowwise_slabs(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
-                                              pass_offset(opts->offset, 2), w.col, false, s);
-      if (e == hipSuccess)
-        e = i8mp::launch_quantize_colwise_given(W, N, K, K, colmax_w, w.qw, kp, w.sw, r, seed,
-                                                pass_offset(opts->offset, 3), s);
+      // reduces them to dY's column maxima (needed by dY's column pass, after
+      // it).  W's column pass rides in the same launch.
+      e = i8mp::launch_quantize_rowslabs_colgiven(dY, M, N, N, w.qdy, np, w.sdy, pass_offset(opts->offset, 2), w.col,
+                                                  W, N, K, K, colmax_w, w.qw, kp, w.sw, pass_offset(opts->offset, 3),
+                                                  r, seed, s);
       side.n = 1;
       side.cols = N;
       side.part[0] = static_cast<const uint16_t*>(w.col);

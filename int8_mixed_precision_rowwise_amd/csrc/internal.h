@@ -71,6 +71,17 @@ hipError_t launch_quantize_colwise_given_pair(
     int64_t rows_b, int64_t cols_b, int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb,
     float* scale_b, uint64_t offset_b, int round, uint64_t seed, hipStream_t stream);
 
+// Tensor a's row pass leaving its slab maxima in ws_a (as
+// launch_quantize_rowwise_slabs with finalize = false; a's slab geometry is
+// rowwise_colmax_geometry(rows_a, cols_a)) and tensor b's column pass with
+// its column maxima given (as launch_quantize_colwise_given), in one launch
+// where a's rows take 4 or 8 chunks per lane, else in those two launches.
+hipError_t launch_quantize_rowslabs_colgiven(
+    const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, int8_t* qa, int64_t ldqa,
+    float* scale_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b, int64_t cols_b,
+    int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb, float* scale_b, uint64_t offset_b,
+    int round, uint64_t seed, hipStream_t stream);
+
 // FP8 (E4M3) quantization, round to nearest: codes q8 in x's layout,
 // scales per row (row-wise) or per column (column-wise, slab maxima in ws,
 // colwise_workspace_bytes).

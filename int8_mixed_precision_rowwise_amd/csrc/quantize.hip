@@ -782,6 +782,35 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax2(RowColmaxJob a,
                                                   j.offset, j.rows_per_block, j.part, part_ld, band, cm);
 }
 
+// A row pass with slab maxima (tensor a) and a column pass with its column
+// maxima given (tensor b) in one launch: the grad-input GEMM of a linear
+// layer needs dY row-wise and W column-wise, two independent passes over
+// different tensors.  Blocks [0, a.slabs) take a's bands exactly as
+// quant_rows_colmax2 does (8 waves, the same bands and slabs); the rest take
+// b's row bands kPairBands at a time, column group (blockIdx.x - a.slabs) %
+// b_groups, as quant_cols_given2 does.  At NV <= 8 the LDS (8 x NV KiB) lets
+// two blocks share a CU, so the two passes overlap instead of following one
+// another.  Results as the two separate launches.
+template <int NV, bool SR, bool ALIGNED4, bool FULL = false>
+__global__ __launch_bounds__(kColThreads) void quant_rows_cols_pair(RowColmaxJob a, int64_t a_cols,
+                                                                    int64_t part_ld, ColGivenJob b,
+                                                                    int64_t b_groups, uint64_t seed) {
+  static_assert(kColThreads == 64 * 8, "both halves run 8 waves");
+  __shared__ uint4 cm[8][NV * 64];
+  if ((int64_t)blockIdx.x < a.slabs) {
+    rows_colmax_band<NV, 8, SR, ALIGNED4, FULL>(a.x, a.rows, a_cols, a.ldx, a.q, a.ldq, a.scale, seed, a.offset,
+                                                a.rows_per_block, a.part, part_ld, blockIdx.x, cm);
+    return;
+  }
+  const int64_t i = (int64_t)blockIdx.x - a.slabs;
+  const int64_t group = i % b_groups;
+  const int64_t band0 = i / b_groups * kPairBands;
+  const int64_t band_end = min(band0 + kPairBands, b.bands);
+  for (int64_t band = band0; band < band_end; ++band)
+    cols_given_block<SR, ALIGNED4, 0>(b.x, b.rows, b.cols, b.ldx, b.colmax, b.scale, b.q, b.ldq, seed, b.offset,
+                                      band, group);
+}
+
 // Row-wise with column maxima for rows longer than 14336 elements (a row no
 // longer fits in one wave's registers).  The tensor is cut into tiles of a
 // band of rows by a segment of kLongSeg columns; a block of 8 waves walks the
@@ -1507,6 +1536,49 @@ hipError_t launch_quantize_colwise_given_pair(
       quant_cols_given2<true, false><<<grid, kColThreads, 0, stream>>>(a, b, seed);
   } else {
     quant_cols_given2<false, true><<<grid, kColThreads, 0, stream>>>(a, b, seed);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rowslabs_colgiven(
+    const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, int8_t* qa, int64_t ldqa,
+    float* scale_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b, int64_t cols_b,
+    int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb, float* scale_b, uint64_t offset_b,
+    int round, uint64_t seed, hipStream_t stream) {
+  const RowColmaxPlan pa = rcm_plan(rows_a, cols_a);
+  const int64_t per_lane = (cols_a + 511) / 512;
+  const int nv = per_lane > 2 && per_lane <= 4 ? 4 : (per_lane > 4 && per_lane <= 8 ? 8 : 0);
+  const bool a4 = cols_a % 4 == 0 && cols_b % 4 == 0;
+  if (rows_a == 0 || cols_a == 0 || cols_b == 0 || !pa.fused || nv == 0 || (round == 1 && !a4)) {
+    const hipError_t e = launch_quantize_rowwise_slabs(xa, rows_a, cols_a, ldxa, qa, ldqa, scale_a, nullptr, round,
+                                                       seed, offset_a, ws_a, false, stream);
+    if (e != hipSuccess) return e;
+    return launch_quantize_colwise_given(xb, rows_b, cols_b, ldxb, colmax_b, qb, ldqb, scale_b, round, seed,
+                                         offset_b, stream);
+  }
+  const RowColmaxJob a{xa, rows_a, ldxa, qa, ldqa, scale_a, offset_a, pa.rows_per_block, pa.slabs,
+                       static_cast<uint16_t*>(ws_a)};
+  const int64_t bands_b = max((int64_t)1, (rows_b + kColBand - 1) / kColBand);
+  const ColGivenJob b{xb, rows_b, cols_b, ldxb, colmax_b, scale_b, qb, ldqb, offset_b, bands_b,
+                      (bands_b + kPairBands - 1) / kPairBands};
+  const int64_t groups = (cols_b + (int64_t)kColTile * kColWaves - 1) / ((int64_t)kColTile * kColWaves);
+  if (a.slabs + b.blocks * groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.slabs + b.blocks * groups));
+  const bool full = cols_a == (int64_t)nv * 512;
+  if (nv == 4) {
+    if (round == 1)
+      quant_rows_cols_pair<4, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else if (full)
+      quant_rows_cols_pair<4, false, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else
+      quant_rows_cols_pair<4, false, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+  } else {
+    if (round == 1)
+      quant_rows_cols_pair<8, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else if (full)
+      quant_rows_cols_pair<8, false, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else
+      quant_rows_cols_pair<8, false, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
   }
   return hipGetLastError();
 }

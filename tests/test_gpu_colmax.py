@@ -118,6 +118,27 @@ def test_linear_chains_with_maxima_full_width_rows(rounding, rc, M, N, K):
     assert np.array_equal(tensor_bits(dW), dWo), "dW"
 
 
+# The grad-input chain runs dY's row pass and W's column pass in one launch
+# when dY's rows take 4 or 8 chunks per lane (N in 1025..4096; the chains
+# take widths in whole 16-byte chunks): ragged and whole widths of both
+# kinds, W wider than one 4096-column group with a ragged last tile, a single
+# token.  Every output against the oracle.
+@pytest.mark.parametrize("rounding,rc", ROUNDINGS)
+@pytest.mark.parametrize("M,N,K", [(300, 1504, 1000), (129, 2048, 4200), (33, 3000, 704), (200, 4088, 1104),
+                                   (1, 2504, 64), (64, 1032, 512), (40, 1032, 4104)])
+def test_linear_bwd_row_and_column_pass_in_one_launch(rounding, rc, M, N, K):
+    t = linear_inputs(LinearShape("mixed_pair", M, N, K), seed=M + N + K, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
+    seed, off = 91, 5 << 44
+    _, cx, cw = i8.linear_fwd_colmax(X, W, rounding, seed, off)
+    dX, dW = i8.linear_bwd(dY, X, W, rounding, seed, off, colmax_x=cx, colmax_w=cw)
+    torch.cuda.synchronize()
+    dXo, dWo = oracle.linear_bwd(dYb, Xb, Wb, rc, seed, off)
+    assert np.array_equal(tensor_bits(dX), dXo), "dX"
+    assert np.array_equal(tensor_bits(dW), dWo), "dW"
+
+
 def test_chains_with_maxima_and_an_empty_contraction():
     """K = 0 (forward) and N = 0 (grad-input) with column-maxima pointers given
     through the C ABI: the row scales of the empty rows are 0 and the outputs
