@@ -567,6 +567,18 @@ struct Dma {
 #pragma unroll
     for (int j = 0; j < kInst; ++j) issue_one(j, dst, slab, K, wave);
   }
+
+  // Instruction j for a slab known to lie past the contraction (only zeros
+  // land, into a buffer nobody reads): the same load at the out-of-range
+  // offset, so the slab still counts in the waits.  Needs no offset state.
+  __device__ __forceinline__ void issue_past_end(int j, int8_t* dst, int wave) const {
+    const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(dst + (wave + NW * j) * 1024)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(l), "v"(kOob), "s"(rsrc)
+                 : "memory", "m0");
+  }
 };
 
 // ---- column maxima reduced in a GEMM's prologue ----------------------------
@@ -575,17 +587,20 @@ struct Dma {
 // patterns, [slabs][part_ld], see ColmaxJob) that still have to be reduced to
 // fp32 column maxima before the backward needs them.  Instead of a launch of
 // its own, workgroup g of the following GEMM reduces group g: 32 columns of
-// one tensor over all its slabs (at most kSideSlabs).  Its slab rows come
-// into a spare LDS region by the same LDS-DMA loads as the operand slabs,
-// issued just before them, so the reduction overlaps the wait for the first
-// operand slab.  Maximum is exact and order-free: the result is colmax
-// finalize's.
-constexpr int kSideSlabs = 256;
-constexpr int kSideBytes = kSideSlabs * 64;  // 32 columns x 2 bytes per slab row
+// one tensor over all its slabs (at most side_slabs(BM): 256 for the big tile;
+// 128 for the 128 x 128 one, whose LDS must stay under half a CU's so two
+// workgroups still share a CU).  Its slab rows come into a spare LDS region
+// by the same LDS-DMA loads as the operand slabs, issued after the first
+// STAGES slabs' loads (off the first slab's critical path), and are folded
+// after the epilogue's stores, under the store drain.  Maximum is exact and order-free: the result
+// is colmax finalize's.
+constexpr int side_slabs(int bm) { return bm >= 256 ? 256 : 128; }
 
-template <int NW>
+template <int NW, int SLABS>
 struct SideJob {
-  static constexpr int kInst = kSideBytes / 1024 / NW;  // 1 KiB loads per wave
+  static constexpr int kBytes = SLABS * 64;          // 32 columns x 2 bytes per slab row
+  static constexpr int kInst = kBytes / 1024 / NW;   // 1 KiB loads per wave
+  static_assert(kInst >= 1 && kBytes % (1024 * NW) == 0, "whole 1 KiB loads per wave");
   v4u rsrc;
   bool on;          // this workgroup has a group (workgroup-uniform)
   int t;            // tensor of the group
@@ -629,7 +644,7 @@ struct SideJob {
     const int chunk = tid & 3;
     uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < kSideSlabs * 4 / NT; ++i) {
+    for (int i = 0; i < SLABS * 4 / NT; ++i) {
       const uint4 v = *reinterpret_cast<const uint4*>(side + ((tid >> 2) + i * (NT / 4)) * 64 + chunk * 16);
       m[0] = max_u16x2(m[0], v.x), m[1] = max_u16x2(m[1], v.y);
       m[2] = max_u16x2(m[2], v.z), m[3] = max_u16x2(m[3], v.w);
@@ -928,15 +943,13 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * SLAB];
 
   __shared__ __attribute__((aligned(16))) float s_lds[BM + BN];  // scales of the tile
-  __shared__ __attribute__((aligned(1024))) int8_t side_lds[SIDE ? kSideBytes : 16];
+  constexpr int SIDE_SLABS = side_slabs(BM);
+  __shared__ __attribute__((aligned(1024))) int8_t side_lds[SIDE ? SIDE_SLABS * 64 : 16];
   __shared__ uint4 side_red[SIDE ? NW : 1][4];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  SideJob<NW> sj;
-  if constexpr (SIDE) {  // the column-maxima loads go out first (see SideJob)
-    sj.init(side, blockIdx.x);
-    if (sj.on) sj.issue(side_lds, side.part_ld, wave, lane);
-  }
+  SideJob<NW, SIDE_SLABS> sj;
+  if constexpr (SIDE) sj.init(side, blockIdx.x);
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   int wg = blockIdx.x, nwg = gridDim.x;
   if constexpr (OUT_I32) {
@@ -998,12 +1011,12 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
     da.issue(lds + s * SLAB, s, K, wave);
     db.issue(lds + s * SLAB + A_BYTES, s, K, wave);
   }
+  // The column-maxima loads (see SideJob) go out behind the first STAGES
+  // slabs.  Loads complete in issue order, so each wait below, which counts
+  // slab loads only, then waits for at most kInst loads more than it needs
+  // in the first slabs and stays exact.
   if constexpr (SIDE) {
-    if (sj.on) {  // workgroup-uniform
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(STAGES * PER));  // this wave's column-maxima loads have landed
-      lds_barrier();                                        // ... and every other wave's
-      sj.reduce(side, side_lds, side_red, t, wave, lane);
-    }
+    if (sj.on) sj.issue(side_lds, side.part_ld, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((STAGES - 1) * PER));  // slab 0 has landed
   lds_barrier();
@@ -1018,8 +1031,11 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   // has landed for every wave and that every wave has finished reading slab
   // kt, whose fragments were read during the previous slab.  A sched_barrier
   // after each step keeps the matrix core fed while the LDS and memory units
-  // work.
-  auto slab = [&](Frag (&bc)[TN], Frag (&bn)[TN], int kt) __attribute__((always_inline)) {
+  // work.  `tail`: the last slab but one, whose loads (slab kt + STAGES) lie
+  // past the contraction; issuing them at the out-of-range offset directly
+  // keeps the load offsets dead after the loop (otherwise they are held, or
+  // spilled, across it).
+  auto slab = [&](Frag (&bc)[TN], Frag (&bn)[TN], int kt, bool tail) __attribute__((always_inline)) {
     const int8_t* nxt = lds + ((kt + 1) % STAGES) * SLAB;
     int8_t* dst = lds + (kt % STAGES) * SLAB;
     const int ns = kt + STAGES;
@@ -1043,8 +1059,13 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
 #pragma unroll
       for (int d = 0; d < PER; ++d)
         if (m == S::dma_at(d)) {
-          if (d < NA) da.issue_one(d, dst, ns, K, wave);
-          else db.issue_one(d - NA, dst + A_BYTES, ns, K, wave);
+          if (tail) {
+            if (d < NA) da.issue_past_end(d, dst, wave);
+            else db.issue_past_end(d - NA, dst + A_BYTES, wave);
+          } else {
+            if (d < NA) da.issue_one(d, dst, ns, K, wave);
+            else db.issue_one(d - NA, dst + A_BYTES, ns, K, wave);
+          }
         }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1053,11 +1074,11 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
   // slabs 0 .. nk-2 in pairs (the B register sets swap roles each slab)
   int kt = 0;
   for (; kt + 2 < nk; kt += 2) {
-    slab(b0, b1, kt);
-    slab(b1, b0, kt + 1);
+    slab(b0, b1, kt, false);
+    slab(b1, b0, kt + 1, false);
   }
-  if (kt + 1 < nk) {
-    slab(b0, b1, kt);
+  if (kt + 1 < nk) {  // kt = nk - 2: its loads are of slab nk + STAGES - 2 >= nk
+    slab(b0, b1, kt, true);
     ++kt;
   }
   if (nk > 0) {  // slab nk-1, whose fragments are in a and b0 (nk-1 even) or b1
@@ -1082,6 +1103,12 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
     store16_staged<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, lds, static_cast<__bf16*>(Cv), ldc, lane, wave);
   } else {
     store16_direct<BM, TM, TN, OUT_I32, VEC>(acc, m0, n0, wm0, wn0, M, N, s_lds, Cv, ldc, lane);
+  }
+  // The column maxima last: their slab rows landed long ago (every wave waited
+  // for all its loads and passed the barrier above), and the reduction runs
+  // while the output stores drain.
+  if constexpr (SIDE) {
+    if (sj.on) sj.reduce(side, side_lds, side_red, t, wave, lane);  // workgroup-uniform
   }
 }
 
@@ -1153,14 +1180,15 @@ void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t*
 }
 
 // Whether a column-maxima reduction can ride in the prologue of a pipelined
-// launch of `wgs` workgroups: one group of 32 columns per workgroup at most,
-// at most kSideSlabs slabs per tensor.
-bool side_fits(const ColmaxJob& j, int64_t wgs) {
+// launch of `wgs` workgroups of BM x BM tiles: one group of 32 columns per
+// workgroup at most, at most side_slabs(BM) slabs per tensor.
+bool side_fits(const ColmaxJob& j, int64_t wgs, int bm) {
   if (j.n <= 0 || j.n > 2) return false;
+  const int64_t max_slabs = side_slabs(bm);
   const int64_t groups = j.n * ((j.cols + 31) / 32);
   for (int t = 0; t < j.n; ++t)
-    if (j.slabs[t] > kSideSlabs) return false;
-  return groups <= wgs && j.part_ld * 2 * (int64_t)kSideSlabs < (int64_t(1) << 31);
+    if (j.slabs[t] > max_slabs) return false;
+  return groups <= wgs && j.part_ld * 2 * max_slabs < (int64_t(1) << 31);
 }
 
 // Whether the pipelined kernel can take a BM x BN tiling of this problem.
@@ -1185,7 +1213,7 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool fast = pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
-  if (side && (Ci || !(fast && side_fits(*side, tiles)))) {  // as a launch of its own
+  if (side && (Ci || !(fast && side_fits(*side, tiles, BM)))) {  // as a launch of its own
     const hipError_t e = launch_colmax_finalize(*side, stream);
     if (e != hipSuccess) return e;
     side = nullptr;
@@ -1306,7 +1334,7 @@ hipError_t run_split(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const 
   const int64_t tiles = big_tiles(M, N);
   const int64_t plane = M * p.ldp;
   const dim3 grid((unsigned)(tiles * p.splits));
-  if (side && !side_fits(*side, tiles * p.splits)) {  // as a launch of its own
+  if (side && !side_fits(*side, tiles * p.splits, 256)) {  // as a launch of its own
     const hipError_t e = launch_colmax_finalize(*side, stream);
     if (e != hipSuccess) return e;
     side = nullptr;
