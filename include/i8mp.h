@@ -25,8 +25,8 @@
  *     that fails validation launches nothing and writes nothing.
  *   - Alignment: base pointers of bf16/int8/int32 matrices are 16-byte
  *     aligned and ld * element size is a multiple of 16 bytes; scale vectors
- *     are 4-byte aligned.  The INT8 entry points accept any sizes >= 0; the
- *     FP8 GEMM entry points state their own shape rules.  Reads of an input
+ *     are 4-byte aligned.  Any sizes >= 0 are accepted (up to the stated
+ *     contraction bound of the INT8 GEMMs).  Reads of an input
  *     may touch bytes between the end of a row and the next 16-byte boundary
  *     (never outside that aligned 16-byte chunk); outputs are written only
  *     inside their rows.
@@ -314,11 +314,12 @@ i8mp_status i8mp_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t c
  * FP8 scaled matmul: acc[m,n] = sum_k A(m,k) * B(k,n) over E4M3 values in
  * fp32 (the matrix core's summation: each product is exact, the sums are
  * rounded), then C = bf16_RNE(RN32(RN32(acc) * scale_a[m]) * scale_b[n]).
- * Same layouts and scale indexing as i8mp_int8_scaled_mm.  K must be a
- * multiple of 16; the output extents along operands whose contraction runs
- * down their rows (M in TN, N in NN and TN) multiples of 4; and the bytes
- * spanned by 256 rows of a K-contiguous operand (K rows of the others) below
- * 2^31 (I8MP_EINVAL otherwise).
+ * Same layouts, scale indexing and shape rules as i8mp_int8_scaled_mm (any
+ * sizes; fp32 accumulation, so no contraction bound).  Shapes the pipelined
+ * kernel cannot take (K not a multiple of 16, an output extent read down an
+ * operand's rows not a multiple of 4, tile extents past 2^31 bytes) run on a
+ * general kernel that issues the same instruction on the same operand
+ * placement, so its sums are those of the pipelined kernel.
  */
 i8mp_status i8mp_fp8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                int64_t lda, const float* scale_a, const uint8_t* B, int64_t ldb,
@@ -332,16 +333,35 @@ i8mp_status i8mp_fp8_mm_f32(int32_t layout, int64_t M, int64_t N, int64_t K, con
 
 /*
  * The linear layer's forward and backward with FP8 codes in place of INT8
- * (same passes, layouts and outputs as i8mp_linear_fwd / i8mp_linear_bwd;
- * workspace sizes from i8mp_linear_workspace_bytes).  Each GEMM must meet
- * i8mp_fp8_scaled_mm's shape rules: K a multiple of 16 (forward); for dX, N a
- * multiple of 16 and K of 4; for dW, M a multiple of 16 and N, K of 4.
+ * (same passes, layouts, sizes and outputs as i8mp_linear_fwd /
+ * i8mp_linear_bwd; workspace sizes from i8mp_linear_workspace_bytes).  The
+ * GEMMs are i8mp_fp8_scaled_mm's; a GEMM with few output tiles and a long
+ * contraction sums its contraction in slices into fp32 partial planes in the
+ * workspace, added in a fixed order (so its output may differ from the
+ * unsliced GEMM's by that fp32 rounding, within the same error bound).
  */
 i8mp_status i8mp_linear_fwd_fp8(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
                                 int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream);
 i8mp_status i8mp_linear_bwd_fp8(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
                                 uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The FP8 forward also returning the column maxima of X and W (fp32 [K]
+ * each, either pointer may be NULL), and the FP8 backward taking them (as
+ * i8mp_linear_fwd_colmax / i8mp_linear_bwd_colmax for INT8): the backward's
+ * column-wise passes of W and X then read their tensors once, and the chains
+ * pair their quantize passes in shared launches.  Outputs are identical to
+ * i8mp_linear_fwd_fp8's and i8mp_linear_bwd_fp8's when the maxima are X's
+ * and W's.  Same workspace sizes.
+ */
+i8mp_status i8mp_linear_fwd_fp8_colmax(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                       int64_t N, int64_t K, float* colmax_x, float* colmax_w, void* ws,
+                                       size_t ws_bytes, void* stream);
+i8mp_status i8mp_linear_bwd_fp8_colmax(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                       uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                       const float* colmax_x, const float* colmax_w, void* ws,
+                                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

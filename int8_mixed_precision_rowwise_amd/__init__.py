@@ -25,6 +25,7 @@ __all__ = [
     "colwise_workspace_bytes", "quantize_rowwise_colmax", "quantize_colwise_given_colmax",
     "rowwise_colmax_workspace_bytes", "linear_fwd_colmax", "quantize_rowwise_fp8",
     "quantize_colwise_fp8", "fp8_scaled_mm", "fp8_mm_f32", "linear_fwd_fp8", "linear_bwd_fp8",
+    "linear_fwd_fp8_colmax",
     "quantize_colwise_noalloc", "STATIC_SCRATCH_BYTES", "mfma_rate_probe", "EXPORTED_SYMBOLS",
 ]
 
@@ -43,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "i8mp_quantize_rowwise_colmax", "i8mp_quantize_colwise_given_colmax", "i8mp_linear_fwd_colmax",
     "i8mp_linear_bwd_colmax", "i8mp_quantize_rowwise_fp8", "i8mp_quantize_colwise_fp8",
     "i8mp_fp8_scaled_mm", "i8mp_fp8_mm_f32", "i8mp_linear_fwd_fp8", "i8mp_linear_bwd_fp8",
+    "i8mp_linear_fwd_fp8_colmax", "i8mp_linear_bwd_fp8_colmax",
     "i8mp_quantize_colwise_noalloc", "i8mp_mfma_rate_probe",
 )
 
@@ -89,6 +91,8 @@ def _load() -> ctypes.CDLL:
         "i8mp_fp8_mm_f32": ([i32, i64, i64, i64, p, i64, p, i64, p, i64, p], i32),
         "i8mp_linear_fwd_fp8": ([p, p, p, i64, i64, i64, p, sz, p], i32),
         "i8mp_linear_bwd_fp8": ([p, p, p, p, p, i64, i64, i64, p, sz, p], i32),
+        "i8mp_linear_fwd_fp8_colmax": ([p, p, p, i64, i64, i64, p, p, p, sz, p], i32),
+        "i8mp_linear_bwd_fp8_colmax": ([p, p, p, p, p, i64, i64, i64, p, p, p, sz, p], i32),
         "i8mp_quantize_colwise_noalloc": ([p, i64, i64, i64, p, i64, p, i32, u64, u64, p], i32),
         "i8mp_mfma_rate_probe": ([p, i64, i64, p, p], i32),
     }
@@ -617,18 +621,42 @@ def linear_fwd_fp8(X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = 
     return Y
 
 
+def linear_fwd_fp8_colmax(X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None):
+    """linear_fwd_fp8 that also returns the column maxima of X and W (fp32 [K]
+    each) for linear_bwd_fp8: (Y, colmax_x, colmax_w)."""
+    M, N, K, dev = _fwd_args(X, W, out, workspace)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    cx = torch.empty(K, dtype=torch.float32, device=dev)
+    cw = torch.empty(K, dtype=torch.float32, device=dev)
+    need = linear_workspace_bytes(M, N, K, False)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.i8mp_linear_fwd_fp8_colmax(_ptr(X), _ptr(W), _ptr(Y), M, N, K, _ptr(cx), _ptr(cw),
+                                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "i8mp_linear_fwd_fp8_colmax")
+    return Y, cx, cw
+
+
 def linear_bwd_fp8(dY: torch.Tensor, X: torch.Tensor, W: torch.Tensor, want_dx: bool = True,
-                   want_dw: bool = True, workspace: torch.Tensor | None = None):
+                   want_dw: bool = True, workspace: torch.Tensor | None = None,
+                   dX: torch.Tensor | None = None, dW: torch.Tensor | None = None,
+                   colmax_x: torch.Tensor | None = None, colmax_w: torch.Tensor | None = None):
     """(dX = dY @ W, dW = dY.T @ X) with FP8 (E4M3) operands, each quantized along
-    its own contraction."""
-    M, N, K, dev = _bwd_args(dY, X, W, None, None, workspace)
-    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if want_dx else None
-    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if want_dw else None
+    its own contraction.  colmax_x / colmax_w: the column maxima from
+    linear_fwd_fp8_colmax (optional; the results are the same)."""
+    M, N, K, dev = _bwd_args(dY, X, W, dX, dW, workspace, colmax_x, colmax_w)
+    if want_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if want_dw and dW is None:
+        dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     need = linear_workspace_bytes(M, N, K, True)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        st = lib.i8mp_linear_bwd_fp8(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX), _ptr(dW), M, N, K,
-                                     _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, "i8mp_linear_bwd_fp8")
-    return dX, dW
+        st = lib.i8mp_linear_bwd_fp8_colmax(_ptr(dY), _ptr(X), _ptr(W), _ptr(dX if want_dx else None),
+                                            _ptr(dW if want_dw else None), M, N, K, _ptr(colmax_x),
+                                            _ptr(colmax_w), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "i8mp_linear_bwd_fp8_colmax")
+    return (dX if want_dx else None), (dW if want_dw else None)

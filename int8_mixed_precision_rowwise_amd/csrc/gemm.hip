@@ -1293,20 +1293,25 @@ size_t plan_bytes(const SplitPlan& p, int64_t M) {
 }
 
 // C[m, n] = bf16_RNE(RN32(RN32(float(sum_s P[s][m][n]) * sa[m]) * sb[n]));
-// one thread per 4 adjacent outputs of a row, rows over blockIdx.y.
-__global__ __launch_bounds__(256) void splitk_reduce(const int32_t* __restrict__ P, int64_t ldp,
+// one thread per 4 adjacent outputs of a row, rows over blockIdx.y.  T =
+// int32_t: exact integer partial sums (INT8); T = float: fp32 partial sums
+// (FP8), added in fp32 in plane order s = 0, 1, ... (a fixed order, so the
+// result does not depend on scheduling).
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce(const T* __restrict__ P, int64_t ldp,
                                                      int64_t plane, int splits, int64_t M,
                                                      int64_t N, const float* __restrict__ sa,
                                                      const float* __restrict__ sb,
                                                      __bf16* __restrict__ C, int64_t ldc) {
+  typedef T v4t __attribute__((ext_vector_type(4)));
   const int64_t n = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
   if (n >= N) return;
   const bool vec = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 8 == 0 && n + 4 <= N;
   for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
-    const int32_t* p = P + m * ldp + n;  // columns up to n + 3 < ldp: inside the plane
-    v4i acc = *reinterpret_cast<const v4i*>(p);
+    const T* p = P + m * ldp + n;  // columns up to n + 3 < ldp: inside the plane
+    v4t acc = *reinterpret_cast<const v4t*>(p);
 #pragma unroll 8
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4i*>(p + s * plane);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4t*>(p + s * plane);
     const float sam = sa[m];
     __bf16 h[4];
 #pragma unroll
@@ -1327,10 +1332,11 @@ __global__ __launch_bounds__(256) void splitk_reduce(const int32_t* __restrict__
   }
 }
 
-template <bool AK, bool BKM>
+template <int FMT, bool AK, bool BKM>
 hipError_t run_split(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const int8_t* A,
                      int64_t lda, const float* sa, const int8_t* B, int64_t ldb, const float* sb,
-                     uint16_t* C, int64_t ldc, int32_t* P, const ColmaxJob* side, hipStream_t stream) {
+                     uint16_t* C, int64_t ldc, void* P, const ColmaxJob* side, hipStream_t stream) {
+  // partial planes: int32 sums (INT8) or raw fp32 sums (FP8), 4 bytes either way
   const int64_t tiles = big_tiles(M, N);
   const int64_t plane = M * p.ldp;
   const dim3 grid((unsigned)(tiles * p.splits));
@@ -1340,44 +1346,146 @@ hipError_t run_split(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const 
     side = nullptr;
   }
   if (side)
-    gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true, 0, true><<<grid, 512, 0, stream>>>(
+    gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true, FMT, true><<<grid, 512, 0, stream>>>(
         M, N, K, A, lda, nullptr, B, ldb, nullptr, P, p.ldp, p.kchunk, plane, *side);
   else
-    gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true><<<grid, 512, 0, stream>>>(
+    gemm_i8_pipelined<256, 256, 4, AK, BKM, true, true, FMT><<<grid, 512, 0, stream>>>(
         M, N, K, A, lda, nullptr, B, ldb, nullptr, P, p.ldp, p.kchunk, plane, ColmaxJob{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)std::min<int64_t>(M, 65535));
-  splitk_reduce<<<rgrid, 256, 0, stream>>>(P, p.ldp, plane, p.splits, M, N, sa, sb,
-                                          reinterpret_cast<__bf16*>(C), ldc);
+  if constexpr (FMT == 1)
+    splitk_reduce<float><<<rgrid, 256, 0, stream>>>(static_cast<const float*>(P), p.ldp, plane, p.splits, M, N, sa, sb,
+                                                   reinterpret_cast<__bf16*>(C), ldc);
+  else
+    splitk_reduce<int32_t><<<rgrid, 256, 0, stream>>>(static_cast<const int32_t*>(P), p.ldp, plane, p.splits, M, N, sa,
+                                                     sb, reinterpret_cast<__bf16*>(C), ldc);
   return hipGetLastError();
+}
+
+// FP8 GEMM for any shape (the pipelined kernel needs K % 16 == 0, and
+// output extents that are multiples of 4 where an operand is read down its
+// rows).  The INT8 general kernel's structure (register-staged, byte-masked
+// loads into the same swizzled LDS tiles, two slabs in LDS) with the
+// pipelined FP8 kernel's fragments and instruction: each 64-deep slab is one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per 32 x 32 block with the operands placed
+// exactly as there, and slabs are accumulated in the same order, so on shapes
+// both kernels take the sums are bit-identical.  Contraction indices past K
+// are zero in both operands (a product of two zeros has the smallest
+// exponent sum, so it changes no group's truncation step).
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_F32, bool VEC>
+__global__ __launch_bounds__(kThreads) void gemm_f8_general(int64_t M, int64_t N, int64_t K,
+                                                            const int8_t* __restrict__ A, int64_t lda,
+                                                            const float* __restrict__ sa,
+                                                            const int8_t* __restrict__ B, int64_t ldb,
+                                                            const float* __restrict__ sb,
+                                                            void* __restrict__ Cv, int64_t ldc) {
+  constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  __shared__ __attribute__((aligned(16))) int8_t lds[2 * (A_BYTES + B_BYTES)];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = Mma<1>::zero();
+
+  Stager<BM, A_KMAJOR> sa_stage;
+  Stager<BN, B_KMAJOR> sb_stage;
+  const int nk = (int)((K + BK - 1) / BK);
+  if (nk > 0) {
+    sa_stage.load(A, lda, m0, M, 0, K, t);
+    sb_stage.load(B, ldb, n0, N, 0, K, t);
+    sa_stage.store(lds, t);
+    sb_stage.store(lds + A_BYTES, t);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    int8_t* cur = lds + (kt & 1) * (A_BYTES + B_BYTES);
+    int8_t* nxt = lds + ((kt & 1) ^ 1) * (A_BYTES + B_BYTES);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      sa_stage.load(A, lda, m0, M, (int64_t)(kt + 1) * BK, K, t);
+      sb_stage.load(B, ldb, n0, N, (int64_t)(kt + 1) * BK, K, t);
+    }
+    v8i af[TM], bf[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = frag32f8<BM, A_KMAJOR>(cur, wm0 + 32 * i, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = frag32f8<BN, B_KMAJOR>(cur + A_BYTES, wn0 + 32 * j, lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = Mma<1>::mma(bf[j], af[i], acc[i][j]);
+    if (more) {
+      sa_stage.store(nxt, t);
+      sb_stage.store(nxt + A_BYTES, t);
+    }
+    __syncthreads();
+  }
+
+  if constexpr (OUT_F32) {  // the raw fp32 sums (C holds floats)
+    store32f_raw<TM, TN>(acc, m0, n0, wm0, wn0, M, N, static_cast<float*>(Cv), ldc, lane);
+  } else {
+    // every wave has passed its last LDS read of the slabs before any scale lands
+    __syncthreads();
+    float* s_lds = reinterpret_cast<float*>(lds);
+    stage_scales<BM, BN, false>(s_lds, m0, n0, M, N, sa, sb, t);
+    store32f_direct<BM, TM, TN>(acc, m0, n0, wm0, wn0, M, N, s_lds, static_cast<__bf16*>(Cv), ldc, lane);
+  }
 }
 
 template <int BM, int BN, bool AK, bool BKM>
 hipError_t run_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sa,
                    const uint8_t* B, int64_t ldb, const float* sb, uint16_t* C, float* Cf,
-                   int64_t ldc, hipStream_t stream) {
+                   int64_t ldc, const ColmaxJob* side, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   constexpr int WGN = BM >= 256 ? 4 : 2;
   const bool vec = ldc % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
   const int8_t* a = reinterpret_cast<const int8_t*>(A);
   const int8_t* b = reinterpret_cast<const int8_t*>(B);
-  if (Cf)
+  const bool fast = pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
+  if (side && (Cf || !(fast && side_fits(*side, tiles, BM)))) {  // as a launch of its own
+    const hipError_t e = launch_colmax_finalize(*side, stream);
+    if (e != hipSuccess) return e;
+    side = nullptr;
+  }
+  if (side && vec) {
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, *side);
+  } else if (side) {
+    gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, *side);
+  } else if (!fast) {
+    if (Cf)
+      gemm_f8_general<BM, BN, AK, BKM, true, false><<<grid, kThreads, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc);
+    else
+      gemm_f8_general<BM, BN, AK, BKM, false, false><<<grid, kThreads, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc);
+  } else if (Cf) {
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, true, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, Cf, ldc, K, 0, ColmaxJob{});
-  else if (vec)
+  } else if (vec) {
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, ColmaxJob{});
-  else
+  } else {
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, ColmaxJob{});
+  }
   return hipGetLastError();
 }
 
 template <bool AK, bool BKM>
 hipError_t pick_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sa,
                     const uint8_t* B, int64_t ldb, const float* sb, uint16_t* C, float* Cf,
-                    int64_t ldc, hipStream_t stream) {
-  if (big_tiles(M, N) >= kBigTileMin) return run_fp8<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
-  return run_fp8<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, stream);
+                    int64_t ldc, const ColmaxJob* side, hipStream_t stream) {
+  if (big_tiles(M, N) >= kBigTileMin)
+    return run_fp8<256, 256, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, side, stream);
+  return run_fp8<128, 128, AK, BKM>(M, N, K, A, lda, sa, B, ldb, sb, C, Cf, ldc, side, stream);
 }
 
 }  // namespace
@@ -1389,11 +1497,11 @@ hipError_t launch_gemm_fp8(int layout, int64_t M, int64_t N, int64_t K, const ui
   if (M == 0 || N == 0) return hipSuccess;
   switch (layout) {
     case 0:
-      return pick_fp8<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, stream);
+      return pick_fp8<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, nullptr, stream);
     case 1:
-      return pick_fp8<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, stream);
+      return pick_fp8<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, nullptr, stream);
     default:
-      return pick_fp8<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, stream);
+      return pick_fp8<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C, C_f32, ldc, nullptr, stream);
   }
 }
 
@@ -1418,22 +1526,37 @@ size_t gemm_split_workspace_bytes(int layout, int64_t M, int64_t N, int64_t K, i
 hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
                              int64_t lda, const float* sa, const int8_t* B, int64_t ldb,
                              const float* sb, uint16_t* C, int64_t ldc, void* ws,
-                             const ColmaxJob* side, hipStream_t stream) {
+                             const ColmaxJob* side, int fmt, hipStream_t stream) {
   if (side && side->n <= 0) side = nullptr;
   if (M == 0 || N == 0) return side ? launch_colmax_finalize(*side, stream) : hipSuccess;
   const SplitPlan p = K > 0 ? plan_for(layout, M, N, K, lda, ldb) : SplitPlan{1, K, 0};
+  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(A);
+  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(B);
   if (p.splits < 2 || !ws) {
+    if (fmt == 1) {
+      switch (layout) {
+        case 0: return pick_fp8<true, true>(M, N, K, a8, lda, sa, b8, ldb, sb, C, nullptr, ldc, side, stream);
+        case 1: return pick_fp8<true, false>(M, N, K, a8, lda, sa, b8, ldb, sb, C, nullptr, ldc, side, stream);
+        default: return pick_fp8<false, false>(M, N, K, a8, lda, sa, b8, ldb, sb, C, nullptr, ldc, side, stream);
+      }
+    }
     switch (layout) {
       case 0: return pick<true, true>(M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, side, stream);
       case 1: return pick<true, false>(M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, side, stream);
       default: return pick<false, false>(M, N, K, A, lda, sa, B, ldb, sb, C, nullptr, ldc, side, stream);
     }
   }
-  int32_t* P = static_cast<int32_t*>(ws);
+  if (fmt == 1) {
+    switch (layout) {
+      case 0: return run_split<1, true, true>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, ws, side, stream);
+      case 1: return run_split<1, true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, ws, side, stream);
+      default: return run_split<1, false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, ws, side, stream);
+    }
+  }
   switch (layout) {
-    case 0: return run_split<true, true>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
-    case 1: return run_split<true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
-    default: return run_split<false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, P, side, stream);
+    case 0: return run_split<0, true, true>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, ws, side, stream);
+    case 1: return run_split<0, true, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, ws, side, stream);
+    default: return run_split<0, false, false>(p, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, ws, side, stream);
   }
 }
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -159,8 +160,10 @@ size_t carve_fwd(void* ws, int64_t M, int64_t N, int64_t K, FwdWs* out) {
   w.qw = static_cast<int8_t*>(c.take((size_t)(N * kp)));
   w.sx = static_cast<float*>(c.take((size_t)M * 4));
   w.sw = static_cast<float*>(c.take((size_t)N * 4));
-  w.part_x = c.take(i8mp::rowwise_colmax_workspace_bytes(M, K));
-  w.part_w = c.take(i8mp::rowwise_colmax_workspace_bytes(N, K));
+  // slab maxima of a row pass with column maxima, or (FP8 rows over 14336
+  // elements) of the column-maxima pass
+  w.part_x = c.take(std::max(i8mp::rowwise_colmax_workspace_bytes(M, K), i8mp::colwise_workspace_bytes(M, K)));
+  w.part_w = c.take(std::max(i8mp::rowwise_colmax_workspace_bytes(N, K), i8mp::colwise_workspace_bytes(N, K)));
   const size_t split = i8mp::gemm_split_workspace_bytes(I8MP_NT, M, N, K, kp, kp);
   w.split = split ? c.take(split) : nullptr;
   if (out) *out = w;
@@ -216,7 +219,7 @@ const char* i8mp_status_str(i8mp_status s) {
   return "unknown status";
 }
 
-int32_t i8mp_abi_version(void) { return 3; }
+int32_t i8mp_abi_version(void) { return 4; }
 
 i8mp_status i8mp_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                   int8_t* q, int64_t ldq, float* scale, int32_t round,
@@ -401,7 +404,7 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
     e = i8mp::launch_quantize_rowwise_colmax_pair(X, M, K, w.qx, kp, w.sx, colmax_x, pass_offset(opts->offset, 0),
                                                   w.part_x, W, N, K, w.qw, kp, w.sw, colmax_w,
                                                   pass_offset(opts->offset, 1), w.part_w, K, r, opts->seed,
-                                                  K == 0, s);
+                                                  K == 0, 0, s);
     if (K > 0) {
       side.n = 2;
       side.cols = K;
@@ -425,7 +428,7 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
   }
   if (e == hipSuccess)
     e = i8mp::launch_gemm_split(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, N, w.split,
-                                side.n ? &side : nullptr, s);
+                                side.n ? &side : nullptr, 0, s);
   return hip_status(e);
 }
 
@@ -484,7 +487,7 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
       // it).  W's column pass rides in the same launch.
       e = i8mp::launch_quantize_rowslabs_colgiven(dY, M, N, N, w.qdy, np, w.sdy, pass_offset(opts->offset, 2), w.col,
                                                   W, N, K, K, colmax_w, w.qw, kp, w.sw, pass_offset(opts->offset, 3),
-                                                  r, seed, s);
+                                                  r, seed, 0, s);
       side.n = 1;
       side.cols = N;
       side.part[0] = static_cast<const uint16_t*>(w.col);
@@ -503,14 +506,14 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
     }
     if (e == hipSuccess)
       e = i8mp::launch_gemm_split(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, K, w.split,
-                                  side.n ? &side : nullptr, s);
+                                  side.n ? &side : nullptr, 0, s);
   }
   if (want_dw && e == hipSuccess) {
     // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
     if (dy_colmax && colmax_x) {  // both column-wise passes in one launch
       e = i8mp::launch_quantize_colwise_given_pair(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, pass_offset(opts->offset, 4),
                                                    X, M, K, K, colmax_x, w.qx, kp, w.sx, pass_offset(opts->offset, 5),
-                                                   r, seed, s);
+                                                   r, seed, 0, s);
     } else {
       e = dy_colmax ? i8mp::launch_quantize_colwise_given(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, r, seed,
                                                           pass_offset(opts->offset, 4), s)
@@ -523,7 +526,7 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
                                                      pass_offset(opts->offset, 5), w.col, s);
     }
     if (e == hipSuccess)
-      e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, nullptr, s);
+      e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, nullptr, 0, s);
   }
   return hip_status(e);
 }
@@ -569,18 +572,10 @@ i8mp_status i8mp_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t c
 // FP8 GEMM shape rules (one kernel, the pipelined one): K a multiple of 16,
 // output extents along operands whose contraction runs down their rows (M
 // for TN, N for NN and TN) multiples of 4.
-bool fp8_shape_ok(int32_t layout, int64_t M, int64_t N, int64_t K) {
-  return K % 16 == 0 && (layout != I8MP_TN || M % 4 == 0) && (layout == I8MP_NT || N % 4 == 0);
-}
 
 i8mp_status i8mp_fp8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                int64_t lda, const float* scale_a, const uint8_t* B, int64_t ldb,
                                const float* scale_b, uint16_t* C, int64_t ldc, void* stream) {
-  if (!fp8_shape_ok(layout, M, N, K)) return I8MP_EINVAL;
-  // the extents a tile's buffer offsets reach must stay below 2^31
-  const int64_t lim = (int64_t(1) << 31) - 1024;
-  if ((layout == I8MP_TN ? K * lda : 256 * lda) >= lim || (layout == I8MP_NT ? 256 * ldb : K * ldb) >= lim)
-    return I8MP_EINVAL;
   i8mp_status st = validate_mm(layout, M, N, K, reinterpret_cast<const int8_t*>(A), lda,
                                reinterpret_cast<const int8_t*>(B), ldb, C, ldc, 2, scale_a, scale_b,
                                true);
@@ -595,10 +590,6 @@ i8mp_status i8mp_fp8_scaled_mm(int32_t layout, int64_t M, int64_t N, int64_t K, 
 i8mp_status i8mp_fp8_mm_f32(int32_t layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                             int64_t lda, const uint8_t* B, int64_t ldb, float* C, int64_t ldc,
                             void* stream) {
-  if (!fp8_shape_ok(layout, M, N, K)) return I8MP_EINVAL;
-  const int64_t lim = (int64_t(1) << 31) - 1024;
-  if ((layout == I8MP_TN ? K * lda : 256 * lda) >= lim || (layout == I8MP_NT ? 256 * ldb : K * ldb) >= lim)
-    return I8MP_EINVAL;
   i8mp_status st = validate_mm(layout, M, N, K, reinterpret_cast<const int8_t*>(A), lda,
                                reinterpret_cast<const int8_t*>(B), ldb, C, ldc, 4, nullptr, nullptr,
                                false);
@@ -610,22 +601,27 @@ i8mp_status i8mp_fp8_mm_f32(int32_t layout, int64_t M, int64_t N, int64_t K, con
                                           C, ldc, as_stream(stream)));
 }
 
-i8mp_status i8mp_linear_fwd_fp8(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
-                                int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+i8mp_status i8mp_linear_fwd_fp8_colmax(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                       int64_t N, int64_t K, float* colmax_x, float* colmax_w, void* ws,
+                                       size_t ws_bytes, void* stream) {
   if (!dims_ok(M, N, K)) return I8MP_EINVAL;
-  if (K % 16 != 0) return I8MP_EINVAL;
   if (!chunked_ok(X, M, K, K, 2) || !chunked_ok(W, N, K, K, 2) || !elementwise_ok(Y, M, N, N, 2))
     return I8MP_EINVAL;
+  if ((colmax_x && !vec_ok(colmax_x, K)) || (colmax_w && !vec_ok(colmax_w, K))) return I8MP_EINVAL;
   const Range ry = mat_range(Y, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
               rwt = mat_range(W, N, K, K, 2);
+  const Range rcx = colmax_x ? vec_range(colmax_x, K, 4) : Range{},
+              rcw = colmax_w ? vec_range(colmax_w, K, 4) : Range{};
   if (overlap(ry, rx) || overlap(ry, rwt)) return I8MP_EINVAL;
+  for (Range o : {ry, rx, rwt})
+    if (overlap(o, rcx) || overlap(o, rcw)) return I8MP_EINVAL;
+  if (overlap(rcx, rcw)) return I8MP_EINVAL;
   if (M == 0 || N == 0) return I8MP_OK;
   const size_t need = carve_fwd(nullptr, M, N, K, nullptr);
   if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
   const Range rw = vec_range(ws, (int64_t)need, 1);
-  for (Range o : {ry, rx, rwt})
+  for (Range o : {ry, rx, rwt, rcx, rcw})
     if (overlap(rw, o)) return I8MP_EINVAL;
-  if (256 * pad16(K) >= (int64_t(1) << 31) - 1024) return I8MP_EINVAL;
   i8mp_status st = device_check();
   if (st != I8MP_OK) return st;
   FwdWs w;
@@ -634,63 +630,130 @@ i8mp_status i8mp_linear_fwd_fp8(const uint16_t* X, const uint16_t* W, uint16_t* 
   const int64_t kp = pad16(K);
   uint8_t* qx = reinterpret_cast<uint8_t*>(w.qx);
   uint8_t* qw = reinterpret_cast<uint8_t*>(w.qw);
-  hipError_t e = i8mp::launch_quantize_rowwise_fp8(X, M, K, K, qx, kp, w.sx, s);
-  if (e == hipSuccess) e = i8mp::launch_quantize_rowwise_fp8(W, N, K, K, qw, kp, w.sw, s);
-  if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_NT, M, N, K, qx, kp, w.sx, qw, kp, w.sw, Y, nullptr, N, s);
+  const bool fused = K > 0 && i8mp::rowwise_colmax_fp8_fused(M, K);  // rows of K <= 14336 elements
+  hipError_t e = hipSuccess;
+  i8mp::ColmaxJob side{};  // X's and W's slab maxima, folded by the GEMM
+  if (colmax_x && colmax_w && fused) {  // both row-wise passes (same width K) in one launch
+    e = i8mp::launch_quantize_rowwise_colmax_pair(X, M, K, w.qx, kp, w.sx, colmax_x, 0, w.part_x, W, N, K, w.qw, kp,
+                                                  w.sw, colmax_w, 0, w.part_w, K, I8MP_RNE, 0, false, 1, s);
+    side.n = 2;
+    side.cols = K;
+    side.part[0] = static_cast<const uint16_t*>(w.part_x);
+    side.part[1] = static_cast<const uint16_t*>(w.part_w);
+    side.colmax[0] = colmax_x;
+    side.colmax[1] = colmax_w;
+    i8mp::rowwise_colmax_geometry(M, K, &side.slabs[0], &side.part_ld);
+    i8mp::rowwise_colmax_geometry(N, K, &side.slabs[1], &side.part_ld);
+  } else {
+    const uint16_t* src[2] = {X, W};
+    const int64_t rows[2] = {M, N};
+    uint8_t* q[2] = {qx, qw};
+    float* sc[2] = {w.sx, w.sw};
+    float* cm[2] = {colmax_x, colmax_w};
+    void* part[2] = {w.part_x, w.part_w};
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      if (cm[i] && fused) {
+        e = i8mp::launch_quantize_rowwise_colmax_fp8(src[i], rows[i], K, K, q[i], kp, sc[i], cm[i], part[i], true, s);
+      } else {
+        e = i8mp::launch_quantize_rowwise_fp8(src[i], rows[i], K, K, q[i], kp, sc[i], s);
+        if (e == hipSuccess && cm[i]) e = i8mp::launch_column_maxima(src[i], rows[i], K, K, cm[i], part[i], s);
+      }
+    }
+  }
+  if (e == hipSuccess)
+    e = i8mp::launch_gemm_split(I8MP_NT, M, N, K, w.qx, kp, w.sx, w.qw, kp, w.sw, Y, N, w.split,
+                                side.n ? &side : nullptr, 1, s);
   return hip_status(e);
 }
 
-i8mp_status i8mp_linear_bwd_fp8(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
-                                uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
-                                void* ws, size_t ws_bytes, void* stream) {
+i8mp_status i8mp_linear_fwd_fp8(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                                int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return i8mp_linear_fwd_fp8_colmax(X, W, Y, M, N, K, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+i8mp_status i8mp_linear_bwd_fp8_colmax(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                       uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                       const float* colmax_x, const float* colmax_w, void* ws,
+                                       size_t ws_bytes, void* stream) {
   if (!dims_ok(M, N, K)) return I8MP_EINVAL;
-  if ((dX && !fp8_shape_ok(I8MP_NN, M, K, N)) || (dW && !fp8_shape_ok(I8MP_TN, N, K, M))) return I8MP_EINVAL;
   if (!chunked_ok(dY, M, N, N, 2)) return I8MP_EINVAL;
   if (dX && (!chunked_ok(W, N, K, K, 2) || !elementwise_ok(dX, M, K, K, 2))) return I8MP_EINVAL;
   if (dW && (!chunked_ok(X, M, K, K, 2) || !elementwise_ok(dW, N, K, K, 2))) return I8MP_EINVAL;
+  if ((colmax_x && !vec_ok(colmax_x, K)) || (colmax_w && !vec_ok(colmax_w, K))) return I8MP_EINVAL;
   if (dX && dW && dX == dW && M * K > 0 && N * K > 0) return I8MP_EINVAL;
   const Range rdy = mat_range(dY, M, N, N, 2), rx = mat_range(X, M, K, K, 2),
               rwt = mat_range(W, N, K, K, 2), rdx = dX ? mat_range(dX, M, K, K, 2) : Range{},
               rdw = dW ? mat_range(dW, N, K, K, 2) : Range{};
+  const Range rcx = colmax_x ? vec_range(colmax_x, K, 4) : Range{},
+              rcw = colmax_w ? vec_range(colmax_w, K, 4) : Range{};
   for (Range o : {rdx, rdw})
-    if (overlap(o, rdy) || overlap(o, rx) || overlap(o, rwt)) return I8MP_EINVAL;
+    if (overlap(o, rdy) || overlap(o, rx) || overlap(o, rwt) || overlap(o, rcx) || overlap(o, rcw))
+      return I8MP_EINVAL;
   if (overlap(rdx, rdw)) return I8MP_EINVAL;
   const bool want_dx = dX && M > 0 && K > 0, want_dw = dW && N > 0 && K > 0;
   if (!want_dx && !want_dw) return I8MP_OK;
   const size_t need = carve_bwd(nullptr, M, N, K, nullptr);
   if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return I8MP_EWORKSPACE;
   const Range rw = vec_range(ws, (int64_t)need, 1);
-  for (Range o : {rdy, rx, rwt, rdx, rdw})
+  for (Range o : {rdy, rx, rwt, rdx, rdw, rcx, rcw})
     if (overlap(rw, o)) return I8MP_EINVAL;
-  const int64_t kp = pad16(K), np = pad16(N);
-  const int64_t lim = (int64_t(1) << 31) - 1024;
-  if ((want_dx && (256 * np >= lim || N * kp >= lim)) || (want_dw && (M * np >= lim || M * kp >= lim)))
-    return I8MP_EINVAL;
   i8mp_status st = device_check();
   if (st != I8MP_OK) return st;
   BwdWs w;
   carve_bwd(ws, M, N, K, &w);
   const hipStream_t s = as_stream(stream);
+  const int64_t kp = pad16(K), np = pad16(N);
   uint8_t* qdy = reinterpret_cast<uint8_t*>(w.qdy);
   uint8_t* qw = reinterpret_cast<uint8_t*>(w.qw);
   uint8_t* qx = reinterpret_cast<uint8_t*>(w.qx);
   hipError_t e = hipSuccess;
-  // with both gradients, dY's column maxima come from its row-wise pass, so its
-  // column-wise pass reads it once (as in the INT8 chain)
+  // with both gradients, dY's column maxima come from its row-wise pass
+  // (rows of at most 14336 elements), so its column-wise pass reads it once
   const bool dy_colmax = want_dx && want_dw && i8mp::rowwise_colmax_fp8_fused(M, N);
+  i8mp::ColmaxJob side{};  // dY's slab maxima, folded by the grad-input GEMM
   if (want_dx) {
-    e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax_fp8(dY, M, N, N, qdy, np, w.sdy, w.cdy, w.col, s)
-                  : i8mp::launch_quantize_rowwise_fp8(dY, M, N, N, qdy, np, w.sdy, s);
-    if (e == hipSuccess) e = i8mp::launch_quantize_colwise_fp8(W, N, K, K, qw, kp, w.sw, w.col, s);
-    if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_NN, M, K, N, qdy, np, w.sdy, qw, kp, w.sw, dX, nullptr, K, s);
+    // dX = dY @ W: dY row-wise over N, W column-wise over N, NN
+    if (dy_colmax && colmax_w) {  // dY's row pass and W's column pass in one launch
+      e = i8mp::launch_quantize_rowslabs_colgiven(dY, M, N, N, w.qdy, np, w.sdy, 0, w.col, W, N, K, K, colmax_w, w.qw,
+                                                  kp, w.sw, 0, I8MP_RNE, 0, 1, s);
+      side.n = 1;
+      side.cols = N;
+      side.part[0] = static_cast<const uint16_t*>(w.col);
+      side.colmax[0] = w.cdy;
+      i8mp::rowwise_colmax_geometry(M, N, &side.slabs[0], &side.part_ld);
+    } else {
+      e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax_fp8(dY, M, N, N, qdy, np, w.sdy, w.cdy, w.col, true, s)
+                    : i8mp::launch_quantize_rowwise_fp8(dY, M, N, N, qdy, np, w.sdy, s);
+      if (e == hipSuccess)
+        e = colmax_w ? i8mp::launch_quantize_colwise_given_fp8(W, N, K, K, colmax_w, qw, kp, w.sw, s)
+                     : i8mp::launch_quantize_colwise_fp8(W, N, K, K, qw, kp, w.sw, w.col, s);
+    }
+    if (e == hipSuccess)
+      e = i8mp::launch_gemm_split(I8MP_NN, M, K, N, w.qdy, np, w.sdy, w.qw, kp, w.sw, dX, K, w.split,
+                                  side.n ? &side : nullptr, 1, s);
   }
   if (want_dw && e == hipSuccess) {
-    e = dy_colmax ? i8mp::launch_quantize_colwise_given_fp8(dY, M, N, N, w.cdy, qdy, np, w.sdy, s)
-                  : i8mp::launch_quantize_colwise_fp8(dY, M, N, N, qdy, np, w.sdy, w.col, s);
-    if (e == hipSuccess) e = i8mp::launch_quantize_colwise_fp8(X, M, K, K, qx, kp, w.sx, w.col, s);
-    if (e == hipSuccess) e = i8mp::launch_gemm_fp8(I8MP_TN, N, K, M, qdy, np, w.sdy, qx, kp, w.sx, dW, nullptr, K, s);
+    // dW = dY.T @ X: dY column-wise over M, X column-wise over M, TN
+    if (dy_colmax && colmax_x) {  // both column-wise passes in one launch
+      e = i8mp::launch_quantize_colwise_given_pair(dY, M, N, N, w.cdy, w.qdy, np, w.sdy, 0, X, M, K, K, colmax_x,
+                                                   w.qx, kp, w.sx, 0, I8MP_RNE, 0, 1, s);
+    } else {
+      e = dy_colmax ? i8mp::launch_quantize_colwise_given_fp8(dY, M, N, N, w.cdy, qdy, np, w.sdy, s)
+                    : i8mp::launch_quantize_colwise_fp8(dY, M, N, N, qdy, np, w.sdy, w.col, s);
+      if (e == hipSuccess)
+        e = colmax_x ? i8mp::launch_quantize_colwise_given_fp8(X, M, K, K, colmax_x, qx, kp, w.sx, s)
+                     : i8mp::launch_quantize_colwise_fp8(X, M, K, K, qx, kp, w.sx, w.col, s);
+    }
+    if (e == hipSuccess)
+      e = i8mp::launch_gemm_split(I8MP_TN, N, K, M, w.qdy, np, w.sdy, w.qx, kp, w.sx, dW, K, w.split, nullptr, 1, s);
   }
   return hip_status(e);
+}
+
+i8mp_status i8mp_linear_bwd_fp8(const uint16_t* dY, const uint16_t* X, const uint16_t* W,
+                                uint16_t* dX, uint16_t* dW, int64_t M, int64_t N, int64_t K,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return i8mp_linear_bwd_fp8_colmax(dY, X, W, dX, dW, M, N, K, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -56,31 +56,33 @@ hipError_t launch_quantize_colwise_given(const uint16_t* x, int64_t rows, int64_
 // launch (and, with finalize, one reduction launch; without it the slab
 // maxima stay in ws_a / ws_b for a later ColmaxJob); each has its own
 // workspace of rowwise_colmax_workspace_bytes(rows, cols).  Same results as
-// two calls.
+// two calls.  fmt 0: INT8 codes; fmt 1: FP8 E4M3 codes (round = 0, rows of at
+// most 14336 elements: rowwise_colmax_fp8_fused).
 hipError_t launch_quantize_rowwise_colmax_pair(
     const uint16_t* xa, int64_t rows_a, int64_t ldxa, int8_t* qa, int64_t ldqa, float* scale_a,
     float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
     int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
-    void* ws_b, int64_t cols, int round, uint64_t seed, bool finalize, hipStream_t stream);
+    void* ws_b, int64_t cols, int round, uint64_t seed, bool finalize, int fmt, hipStream_t stream);
 
 // Two tensors quantized column-wise with their column maxima given, in one
-// launch.  Same results as two calls.
+// launch.  Same results as two calls.  fmt as above (FP8: round = 0).
 hipError_t launch_quantize_colwise_given_pair(
     const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, const float* colmax_a,
     int8_t* qa, int64_t ldqa, float* scale_a, uint64_t offset_a, const uint16_t* xb,
     int64_t rows_b, int64_t cols_b, int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb,
-    float* scale_b, uint64_t offset_b, int round, uint64_t seed, hipStream_t stream);
+    float* scale_b, uint64_t offset_b, int round, uint64_t seed, int fmt, hipStream_t stream);
 
 // Tensor a's row pass leaving its slab maxima in ws_a (as
 // launch_quantize_rowwise_slabs with finalize = false; a's slab geometry is
 // rowwise_colmax_geometry(rows_a, cols_a)) and tensor b's column pass with
 // its column maxima given (as launch_quantize_colwise_given), in one launch
 // where a's rows take 4 or 8 chunks per lane, else in those two launches.
+// fmt as above (FP8: round = 0, a's rows of at most 14336 elements).
 hipError_t launch_quantize_rowslabs_colgiven(
     const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, int8_t* qa, int64_t ldqa,
     float* scale_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b, int64_t cols_b,
     int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb, float* scale_b, uint64_t offset_b,
-    int round, uint64_t seed, hipStream_t stream);
+    int round, uint64_t seed, int fmt, hipStream_t stream);
 
 // FP8 (E4M3) quantization, round to nearest: codes q8 in x's layout,
 // scales per row (row-wise) or per column (column-wise, slab maxima in ws,
@@ -92,20 +94,25 @@ hipError_t launch_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t 
                                        hipStream_t stream);
 
 // FP8 (E4M3) row-wise quantization that also writes colmax (as
-// launch_quantize_rowwise_colmax; rows of at most 14336 elements, where
-// rowwise_colmax_fp8_fused holds), and the FP8 column-wise pass with the
-// column maxima given.
+// launch_quantize_rowwise_colmax, or with finalize = false only the slab
+// maxima in ws, as launch_quantize_rowwise_slabs; rows of at most 14336
+// elements, where rowwise_colmax_fp8_fused holds), and the FP8 column-wise
+// pass with the column maxima given.
 bool rowwise_colmax_fp8_fused(int64_t rows, int64_t cols);
+// Column maxima of x alone (fp32 [cols], as the row passes with maxima give
+// them; any width).  ws: colwise_workspace_bytes(rows, cols).
+hipError_t launch_column_maxima(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* colmax,
+                                void* ws, hipStream_t stream);
 hipError_t launch_quantize_rowwise_colmax_fp8(const uint16_t* x, int64_t rows, int64_t cols,
                                               int64_t ldx, uint8_t* q8, int64_t ldq, float* scale,
-                                              float* colmax, void* ws, hipStream_t stream);
+                                              float* colmax, void* ws, bool finalize, hipStream_t stream);
 hipError_t launch_quantize_colwise_given_fp8(const uint16_t* x, int64_t rows, int64_t cols,
                                             int64_t ldx, const float* colmax, uint8_t* q8,
                                             int64_t ldq, float* scale, hipStream_t stream);
 
-// FP8 (E4M3) scaled GEMM with fp32 accumulation, same layouts; needs
-// K % 16 == 0.  Exactly one of C (bf16, with both scales) or C_f32 (the raw
-// fp32 sums) is non-null.
+// FP8 (E4M3) scaled GEMM with fp32 accumulation, same layouts, any shape.
+// Exactly one of C (bf16, with both scales) or C_f32 (the raw fp32 sums) is
+// non-null.
 hipError_t launch_gemm_fp8(int layout, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                            int64_t lda, const float* sa, const uint8_t* B, int64_t ldb,
                            const float* sb, uint16_t* C, float* C_f32, int64_t ldc,
@@ -135,20 +142,23 @@ hipError_t launch_gemm(int layout, int64_t M, int64_t N, int64_t K, const int8_t
                        uint16_t* C_bf16, int32_t* C_i32, int64_t ldc, hipStream_t stream);
 
 // The linear chains' GEMM (bf16 output): a problem with few output tiles and
-// a long contraction splits the contraction into int32 partial planes in ws
+// a long contraction splits the contraction into partial planes in ws
 // (gemm_split_workspace_bytes; 0 when the problem is not split, and then ws
-// may be null) and reduces them exactly before the epilogue.  Same results as
-// launch_gemm.  lda/ldb as in launch_gemm.
+// may be null) and reduces them before the epilogue.  fmt 0: INT8 codes,
+// int32 planes added exactly, results as launch_gemm; fmt 1: FP8 E4M3 codes,
+// fp32 planes added in plane order (results as launch_gemm_fp8 up to those
+// additions' rounding).  lda/ldb as in launch_gemm.
 size_t gemm_split_workspace_bytes(int layout, int64_t M, int64_t N, int64_t K, int64_t lda,
                                   int64_t ldb);
 // side: column maxima to reduce as well (or null).  The GEMM's workgroups
-// do it in their prologue, while their first operand slabs load, when the
-// problem allows (pipelined kernel, at most one group of 32 columns per
-// workgroup, at most 256 slabs); otherwise it runs as its own launch first.
+// fold them after their epilogue stores, from slab rows loaded behind their
+// first operand slabs, when the problem allows (pipelined kernel, at most one
+// group of 32 columns per workgroup, at most 256 slabs, 128 for 128 x 128
+// tiles); otherwise it runs as its own launch first.
 hipError_t launch_gemm_split(int layout, int64_t M, int64_t N, int64_t K, const int8_t* A,
                              int64_t lda, const float* sa, const int8_t* B, int64_t ldb,
                              const float* sb, uint16_t* C, int64_t ldc, void* ws,
-                             const ColmaxJob* side, hipStream_t stream);
+                             const ColmaxJob* side, int fmt, hipStream_t stream);
 
 hipError_t launch_philox(uint64_t seed, uint64_t offset, int64_t n_blocks, uint32_t* out,
                          hipStream_t stream);

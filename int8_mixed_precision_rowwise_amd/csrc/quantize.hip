@@ -684,7 +684,7 @@ struct ColGivenJob {
   int64_t bands, blocks;
 };
 
-template <bool SR, bool ALIGNED4>
+template <bool SR, bool ALIGNED4, int FMT = 0>
 __global__ __launch_bounds__(kColThreads) void quant_cols_given2(ColGivenJob a, ColGivenJob b,
                                                                  uint64_t seed) {
   const bool second = (int64_t)blockIdx.x >= a.blocks;
@@ -692,8 +692,8 @@ __global__ __launch_bounds__(kColThreads) void quant_cols_given2(ColGivenJob a, 
   const int64_t band0 = (second ? (int64_t)blockIdx.x - a.blocks : (int64_t)blockIdx.x) * kPairBands;
   const int64_t band_end = min(band0 + kPairBands, j.bands);
   for (int64_t band = band0; band < band_end; ++band)
-    cols_given_block<SR, ALIGNED4, 0>(j.x, j.rows, j.cols, j.ldx, j.colmax, j.scale, j.q, j.ldq, seed,
-                                      j.offset, band, blockIdx.y);
+    cols_given_block<SR, ALIGNED4, FMT>(j.x, j.rows, j.cols, j.ldx, j.colmax, j.scale, j.q, j.ldq, seed,
+                                        j.offset, band, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,7 +770,7 @@ struct RowColmaxJob {
   uint16_t* part;
 };
 
-template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false>
+template <int NV, int WAVES, bool SR, bool ALIGNED4, bool FULL = false, int FMT = 0>
 __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax2(RowColmaxJob a, RowColmaxJob b,
                                                                  int64_t cols, int64_t part_ld,
                                                                  uint64_t seed) {
@@ -778,8 +778,8 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax2(RowColmaxJob a,
   const bool second = (int64_t)blockIdx.x >= a.slabs;
   const RowColmaxJob j = second ? b : a;
   const int64_t band = second ? (int64_t)blockIdx.x - a.slabs : (int64_t)blockIdx.x;
-  rows_colmax_band<NV, WAVES, SR, ALIGNED4, FULL>(j.x, j.rows, cols, j.ldx, j.q, j.ldq, j.scale, seed,
-                                                  j.offset, j.rows_per_block, j.part, part_ld, band, cm);
+  rows_colmax_band<NV, WAVES, SR, ALIGNED4, FULL, FMT>(j.x, j.rows, cols, j.ldx, j.q, j.ldq, j.scale, seed,
+                                                       j.offset, j.rows_per_block, j.part, part_ld, band, cm);
 }
 
 // A row pass with slab maxima (tensor a) and a column pass with its column
@@ -791,15 +791,15 @@ __global__ __launch_bounds__(64 * WAVES) void quant_rows_colmax2(RowColmaxJob a,
 // b_groups, as quant_cols_given2 does.  At NV <= 8 the LDS (8 x NV KiB) lets
 // two blocks share a CU, so the two passes overlap instead of following one
 // another.  Results as the two separate launches.
-template <int NV, bool SR, bool ALIGNED4, bool FULL = false>
+template <int NV, bool SR, bool ALIGNED4, bool FULL = false, int FMT = 0>
 __global__ __launch_bounds__(kColThreads) void quant_rows_cols_pair(RowColmaxJob a, int64_t a_cols,
                                                                     int64_t part_ld, ColGivenJob b,
                                                                     int64_t b_groups, uint64_t seed) {
   static_assert(kColThreads == 64 * 8, "both halves run 8 waves");
   __shared__ uint4 cm[8][NV * 64];
   if ((int64_t)blockIdx.x < a.slabs) {
-    rows_colmax_band<NV, 8, SR, ALIGNED4, FULL>(a.x, a.rows, a_cols, a.ldx, a.q, a.ldq, a.scale, seed, a.offset,
-                                                a.rows_per_block, a.part, part_ld, blockIdx.x, cm);
+    rows_colmax_band<NV, 8, SR, ALIGNED4, FULL, FMT>(a.x, a.rows, a_cols, a.ldx, a.q, a.ldq, a.scale, seed,
+                                                     a.offset, a.rows_per_block, a.part, part_ld, blockIdx.x, cm);
     return;
   }
   const int64_t i = (int64_t)blockIdx.x - a.slabs;
@@ -807,8 +807,8 @@ __global__ __launch_bounds__(kColThreads) void quant_rows_cols_pair(RowColmaxJob
   const int64_t band0 = i / b_groups * kPairBands;
   const int64_t band_end = min(band0 + kPairBands, b.bands);
   for (int64_t band = band0; band < band_end; ++band)
-    cols_given_block<SR, ALIGNED4, 0>(b.x, b.rows, b.cols, b.ldx, b.colmax, b.scale, b.q, b.ldq, seed, b.offset,
-                                      band, group);
+    cols_given_block<SR, ALIGNED4, FMT>(b.x, b.rows, b.cols, b.ldx, b.colmax, b.scale, b.q, b.ldq, seed, b.offset,
+                                        band, group);
 }
 
 // Row-wise with column maxima for rows longer than 14336 elements (a row no
@@ -1089,11 +1089,16 @@ struct RcmWaves {
 
 template <int NV>
 void launch_rcm2_nv(const RowColmaxJob& a, const RowColmaxJob& b, int64_t cols, int64_t part_ld,
-                    int round, uint64_t seed, hipStream_t stream) {
+                    int round, uint64_t seed, int fmt, hipStream_t stream) {
   constexpr int WAVES_WIDE = RcmWaves<NV>::wide;
   const dim3 grid((unsigned)(a.slabs + b.slabs));
   const bool a4 = (cols % 4) == 0;
-  if (round == 1) {
+  if (fmt == 1) {  // FP8: round to nearest only
+    if (cols == NV * 512)
+      quant_rows_colmax2<NV, WAVES_WIDE, false, true, true, 1><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+    else
+      quant_rows_colmax2<NV, WAVES_WIDE, false, true, false, 1><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+  } else if (round == 1) {
     if (a4)
       quant_rows_colmax2<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
     else
@@ -1221,7 +1226,7 @@ bool rowwise_colmax_fp8_fused(int64_t rows, int64_t cols) { return rcm_plan(rows
 
 hipError_t launch_quantize_rowwise_colmax_fp8(const uint16_t* x, int64_t rows, int64_t cols,
                                               int64_t ldx, uint8_t* q8, int64_t ldq, float* scale,
-                                              float* colmax, void* ws, hipStream_t stream) {
+                                              float* colmax, void* ws, bool finalize, hipStream_t stream) {
   if (cols == 0) return hipSuccess;
   const RowColmaxPlan p = rcm_plan(rows, cols);
   if (!p.fused) return hipErrorInvalidValue;  // rows over 14336 elements: not offered
@@ -1246,8 +1251,9 @@ hipError_t launch_quantize_rowwise_colmax_fp8(const uint16_t* x, int64_t rows, i
     else
       launch_rcm_f8_nv<28>(p, x, rows, cols, ldx, q, ldq, scale, part, stream);
   }
-  colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(
-      part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
+  if (finalize)
+    colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(
+        part, p.part_ld, rows > 0 ? p.slabs : 0, cols, colmax);
   return hipGetLastError();
 }
 
@@ -1277,6 +1283,22 @@ hipError_t launch_quantize_colwise_fp8(const uint16_t* x, int64_t rows, int64_t 
   quant_cols<false, true, 1><<<grid, kColThreads, 0, stream>>>(
       x, rows, cols, ldx, p.rows_per_block, part, p.part_ld, p.slabs, scale,
       reinterpret_cast<int8_t*>(q8), ldq, 0, 0);
+  return hipGetLastError();
+}
+
+// Column maxima alone (fp32 [cols]): the first pass of the two-pass column
+// quantize and the slab reduction.  ws: colwise_workspace_bytes(rows, cols).
+hipError_t launch_column_maxima(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* colmax,
+                                void* ws, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  const ColPlan p = col_plan(rows, cols);
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  if (p.slabs > 0) {
+    col_absmax_partial<<<dim3((unsigned)p.col_tiles, (unsigned)p.slabs), kColThreads, 0, stream>>>(
+        x, rows, cols, ldx, p.rows_per_slab, part, p.part_ld);
+  }
+  colmax_finalize<<<dim3((unsigned)((cols + 31) / 32)), kFinThreads, 0, stream>>>(part, p.part_ld, p.slabs, cols,
+                                                                                  colmax);
   return hipGetLastError();
 }
 
@@ -1449,7 +1471,7 @@ hipError_t launch_quantize_rowwise_colmax_pair(
     const uint16_t* xa, int64_t rows_a, int64_t ldxa, int8_t* qa, int64_t ldqa, float* scale_a,
     float* colmax_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b,
     int64_t ldxb, int8_t* qb, int64_t ldqb, float* scale_b, float* colmax_b, uint64_t offset_b,
-    void* ws_b, int64_t cols, int round, uint64_t seed, bool finalize, hipStream_t stream) {
+    void* ws_b, int64_t cols, int round, uint64_t seed, bool finalize, int fmt, hipStream_t stream) {
   if (cols == 0) {  // no maxima; the row scales are still written (0)
     const hipError_t e = launch_quantize_rowwise(xa, rows_a, 0, ldxa, qa, ldqa, scale_a, round, seed, offset_a, stream);
     if (e != hipSuccess) return e;
@@ -1457,6 +1479,13 @@ hipError_t launch_quantize_rowwise_colmax_pair(
   }
   const RowColmaxPlan pa = rcm_plan(rows_a, cols), pb = rcm_plan(rows_b, cols);
   if (!pa.fused || rows_a == 0 || rows_b == 0) {
+    if (fmt == 1) {  // rows of at most 14336 elements (the FP8 row pass with maxima)
+      const hipError_t e = launch_quantize_rowwise_colmax_fp8(xa, rows_a, cols, ldxa, reinterpret_cast<uint8_t*>(qa),
+                                                              ldqa, scale_a, colmax_a, ws_a, finalize, stream);
+      if (e != hipSuccess) return e;
+      return launch_quantize_rowwise_colmax_fp8(xb, rows_b, cols, ldxb, reinterpret_cast<uint8_t*>(qb), ldqb,
+                                                scale_b, colmax_b, ws_b, finalize, stream);
+    }
     const hipError_t e = launch_quantize_rowwise_slabs(xa, rows_a, cols, ldxa, qa, ldqa, scale_a, colmax_a,
                                                        round, seed, offset_a, ws_a, finalize, stream);
     if (e != hipSuccess) return e;
@@ -1469,21 +1498,21 @@ hipError_t launch_quantize_rowwise_colmax_pair(
                        static_cast<uint16_t*>(ws_b)};
   const int64_t per_lane = (cols + 511) / 512;
   if (per_lane <= 1)
-    launch_rcm2_nv<1>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<1>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else if (per_lane <= 2)
-    launch_rcm2_nv<2>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<2>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else if (per_lane <= 4)
-    launch_rcm2_nv<4>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<4>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else if (per_lane <= 8)
-    launch_rcm2_nv<8>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<8>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else if (per_lane == 11)
-    launch_rcm2_nv<11>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<11>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else if (per_lane <= 12)
-    launch_rcm2_nv<12>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<12>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else if (per_lane <= 16)
-    launch_rcm2_nv<16>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<16>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   else
-    launch_rcm2_nv<28>(a, b, cols, pa.part_ld, round, seed, stream);
+    launch_rcm2_nv<28>(a, b, cols, pa.part_ld, round, seed, fmt, stream);
   if (finalize)
     colmax_finalize2<<<dim3((unsigned)((cols + 31) / 32), 2), kFinThreads, 0, stream>>>(
         a.part, a.slabs, colmax_a, b.part, b.slabs, colmax_b, pa.part_ld, cols);
@@ -1511,8 +1540,15 @@ hipError_t launch_quantize_colwise_given_pair(
     const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, const float* colmax_a,
     int8_t* qa, int64_t ldqa, float* scale_a, uint64_t offset_a, const uint16_t* xb,
     int64_t rows_b, int64_t cols_b, int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb,
-    float* scale_b, uint64_t offset_b, int round, uint64_t seed, hipStream_t stream) {
+    float* scale_b, uint64_t offset_b, int round, uint64_t seed, int fmt, hipStream_t stream) {
   if (cols_a == 0 || cols_b == 0) {
+    if (fmt == 1) {
+      const hipError_t e = launch_quantize_colwise_given_fp8(xa, rows_a, cols_a, ldxa, colmax_a,
+                                                             reinterpret_cast<uint8_t*>(qa), ldqa, scale_a, stream);
+      if (e != hipSuccess) return e;
+      return launch_quantize_colwise_given_fp8(xb, rows_b, cols_b, ldxb, colmax_b, reinterpret_cast<uint8_t*>(qb),
+                                               ldqb, scale_b, stream);
+    }
     const hipError_t e = launch_quantize_colwise_given(xa, rows_a, cols_a, ldxa, colmax_a, qa, ldqa, scale_a,
                                                        round, seed, offset_a, stream);
     if (e != hipSuccess) return e;
@@ -1529,7 +1565,9 @@ hipError_t launch_quantize_colwise_given_pair(
   const int64_t groups = max((cols_a + span - 1) / span, (cols_b + span - 1) / span);
   if (a.blocks + b.blocks > 0x7FFFFFFF || groups > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.blocks + b.blocks), (unsigned)groups);
-  if (round == 1) {
+  if (fmt == 1) {
+    quant_cols_given2<false, true, 1><<<grid, kColThreads, 0, stream>>>(a, b, seed);
+  } else if (round == 1) {
     if (cols_a % 4 == 0 && cols_b % 4 == 0)
       quant_cols_given2<true, true><<<grid, kColThreads, 0, stream>>>(a, b, seed);
     else
@@ -1544,12 +1582,22 @@ hipError_t launch_quantize_rowslabs_colgiven(
     const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ldxa, int8_t* qa, int64_t ldqa,
     float* scale_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b, int64_t cols_b,
     int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb, float* scale_b, uint64_t offset_b,
-    int round, uint64_t seed, hipStream_t stream) {
+    int round, uint64_t seed, int fmt, hipStream_t stream) {
   const RowColmaxPlan pa = rcm_plan(rows_a, cols_a);
   const int64_t per_lane = (cols_a + 511) / 512;
   const int nv = per_lane > 2 && per_lane <= 4 ? 4 : (per_lane > 4 && per_lane <= 8 ? 8 : 0);
   const bool a4 = cols_a % 4 == 0 && cols_b % 4 == 0;
   if (rows_a == 0 || cols_a == 0 || cols_b == 0 || !pa.fused || nv == 0 || (round == 1 && !a4)) {
+    if (fmt == 1) {  // rows of at most 14336 elements (the FP8 row pass with maxima)
+      const hipError_t e = cols_a == 0 ? launch_quantize_rowwise_fp8(xa, rows_a, 0, ldxa, reinterpret_cast<uint8_t*>(qa),
+                                                                     ldqa, scale_a, stream)
+                                       : launch_quantize_rowwise_colmax_fp8(xa, rows_a, cols_a, ldxa,
+                                                                            reinterpret_cast<uint8_t*>(qa), ldqa,
+                                                                            scale_a, nullptr, ws_a, false, stream);
+      if (e != hipSuccess) return e;
+      return launch_quantize_colwise_given_fp8(xb, rows_b, cols_b, ldxb, colmax_b, reinterpret_cast<uint8_t*>(qb),
+                                               ldqb, scale_b, stream);
+    }
     const hipError_t e = launch_quantize_rowwise_slabs(xa, rows_a, cols_a, ldxa, qa, ldqa, scale_a, nullptr, round,
                                                        seed, offset_a, ws_a, false, stream);
     if (e != hipSuccess) return e;
@@ -1565,7 +1613,16 @@ hipError_t launch_quantize_rowslabs_colgiven(
   if (a.slabs + b.blocks * groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.slabs + b.blocks * groups));
   const bool full = cols_a == (int64_t)nv * 512;
-  if (nv == 4) {
+  if (fmt == 1) {  // FP8: round to nearest only
+    if (nv == 4 && full)
+      quant_rows_cols_pair<4, false, true, true, 1><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else if (nv == 4)
+      quant_rows_cols_pair<4, false, true, false, 1><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else if (full)
+      quant_rows_cols_pair<8, false, true, true, 1><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else
+      quant_rows_cols_pair<8, false, true, false, 1><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+  } else if (nv == 4) {
     if (round == 1)
       quant_rows_cols_pair<4, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
     else if (full)

@@ -42,7 +42,7 @@ from typing import Callable, Optional
 
 import torch
 
-from . import linear_bwd, linear_bwd_fp8, linear_fwd, linear_fwd_colmax, linear_fwd_fp8
+from . import linear_bwd, linear_bwd_fp8, linear_fwd, linear_fwd_colmax, linear_fwd_fp8, linear_fwd_fp8_colmax
 
 __all__ = ["Int8MixedPrecisionConfig", "Int8MixedPrecisionLinearFunction",
            "Int8MixedPrecisionLinear", "swap_linear_modules", "STEP_STRIDE", "STEPS_PER_KEY",
@@ -163,7 +163,9 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
         x2 = _as_rows(x, x.shape[-1])
         w = weight if weight.is_contiguous() else weight.contiguous()
         cx = cw = None
-        if config.output and config.fp8:
+        if config.output and config.fp8 and (config.grad_input or config.grad_weight):
+            y, cx, cw = linear_fwd_fp8_colmax(x2, w)
+        elif config.output and config.fp8:
             y = linear_fwd_fp8(x2, w)
         elif config.output and (config.grad_input or config.grad_weight):
             y, cx, cw = linear_fwd_colmax(x2, w, config.rounding, seed, offset)
@@ -184,7 +186,7 @@ class Int8MixedPrecisionLinearFunction(torch.autograd.Function):
         int_dx, int_dw = need_dx and cfg.grad_input, need_dw and cfg.grad_weight
         dx = dw = None
         if (int_dx or int_dw) and cfg.fp8:
-            dx, dw = linear_bwd_fp8(dy2, x2, w, want_dx=int_dx, want_dw=int_dw)
+            dx, dw = linear_bwd_fp8(dy2, x2, w, want_dx=int_dx, want_dw=int_dw, colmax_x=cx, colmax_w=cw)
         elif int_dx or int_dw:
             dx, dw = linear_bwd(dy2, x2, w, cfg.rounding, ctx.seed, ctx.offset,
                                 want_dx=int_dx, want_dw=int_dw, colmax_x=cx, colmax_w=cw)

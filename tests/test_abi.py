@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert L.i8mp_abi_version() == 3
+    assert L.i8mp_abi_version() == 4
     for s in range(7):
         assert L.i8mp_status_str(s)
     assert b"133144" in L.i8mp_status_str(ERANGE)

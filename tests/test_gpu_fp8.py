@@ -210,11 +210,13 @@ def gpu_mm(layout, A, sa, B, sb):
     return tensor_bits(i8.fp8_scaled_mm(layout, pad(A), dev(sa), pad(B), dev(sb)))
 
 
-# every layout takes output extents that are multiples of 4; NT (both operands
-# K-contiguous) any extents
+# Any shape: the pipelined kernel's (K a multiple of 16, extents read down
+# an operand's rows multiples of 4) and the general kernel's (the rest: K of
+# 8, 24, 40, 1000; odd M and N in every layout).
 FP8_SHAPES = [("NT", 1, 1, 16), ("NT", 17, 33, 64), ("NT", 255, 130, 512)] + [
     (lay, M, N, K) for lay in ("NT", "NN", "TN")
-    for M, N, K in ((4, 4, 16), (12, 4, 32), (20, 36, 64), (256, 132, 512), (300, 260, 1008), (1024, 1024, 1024))]
+    for M, N, K in ((4, 4, 16), (12, 4, 32), (20, 36, 64), (256, 132, 512), (300, 260, 1008), (1024, 1024, 1024),
+                    (1, 1, 8), (3, 5, 24), (17, 33, 40), (255, 130, 1000), (129, 257, 520))]
 
 
 @pytest.mark.parametrize("layout,M,N,K", FP8_SHAPES)
@@ -226,15 +228,37 @@ def test_fp8_scaled_mm(layout, M, N, K):
                  f"{layout} {M}x{N}x{K}", group_term(layout, A, B))
 
 
-def test_fp8_shape_rules():
-    z = lambda r, c: torch.zeros((r, c), dtype=torch.uint8, device="cuda")  # noqa: E731
-    s = lambda n: torch.ones(n, device="cuda")  # noqa: E731
-    # K = 24 (not a multiple of 16); N = 3 read down B's rows; M = 3 read down A's rows
-    for layout, A, B, M, N in (("NT", z(4, 24), z(4, 24), 4, 4), ("NN", z(4, 16), z(16, 3), 4, 3),
-                               ("TN", z(16, 3), z(16, 4), 3, 4)):
-        with pytest.raises(i8.I8mpError) as e:
-            i8.fp8_scaled_mm(layout, A, s(M), B, s(N))
-        assert e.value.status == 1
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_fp8_general_kernel_equals_pipelined(layout):
+    """Shapes the pipelined kernel cannot take run on the general kernel, which
+    issues the same instruction on the same operand placement: its sums are
+    the pipelined kernel's, bit for bit.  NT: K = 40 (general) against the same
+    operands with 8 zero contraction columns appended (K = 48, pipelined; zero
+    codes add nothing).  NN / TN: an output extent read down an operand's rows
+    of 255 (general) against the same operands at 256 (pipelined), rows /
+    columns in common compared."""
+    dev = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()  # noqa: E731
+    if layout == "NT":
+        A, sa, B, sb = fp8_operands("NT", 300, 260, 40, seed=11)
+        A48 = np.pad(A, ((0, 0), (0, 8)))
+        B48 = np.pad(B, ((0, 0), (0, 8)))
+        got = gpu_mm("NT", A, sa, B, sb)
+        want = gpu_mm("NT", A48, sa, B48, sb)
+        assert np.array_equal(got, want)
+        f_got = i8.fp8_mm_f32("NT", padded_copy(dev(A), 64), padded_copy(dev(B), 64))
+        f_want = i8.fp8_mm_f32("NT", dev(A48), dev(B48))
+        torch.cuda.synchronize()
+        assert torch.equal(f_got.view(torch.int32), f_want.view(torch.int32)), "fp32 sums"
+        return
+    A, sa, B, sb = fp8_operands(layout, 256, 256, 520, seed=12)
+    if layout == "NN":  # N read down B's rows: 255 columns of B
+        got = gpu_mm("NN", A, sa, B[:, :255], sb[:255])
+        want = gpu_mm("NN", A, sa, B, sb)
+        assert np.array_equal(got, want[:, :255])
+    else:  # TN: M read down A's rows, N down B's: 255 columns of A
+        got = gpu_mm("TN", A[:, :255], sa[:255], B, sb)
+        want = gpu_mm("TN", A, sa, B, sb)
+        assert np.array_equal(got, want[:255])
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
@@ -285,6 +309,73 @@ def test_linear_chains_fp8(M, N, K):
     torch.cuda.synchronize()
     assert torch.equal(gx.view(torch.int16), want_dx.view(torch.int16)), "dX differs from the primitives"
     assert torch.equal(gw.view(torch.int16), want_dw.view(torch.int16)), "dW differs from the primitives"
+
+
+def oracle_fp8_chain_check(Y, dX, dW, Xb, Wb, dYb, tag):
+    """Y, dX, dW of an FP8 chain against the oracle's quantization and exact
+    sums, within the derived bound."""
+    M, K = Xb.shape
+    N = Wb.shape[0]
+    qx, sx = oracle.quantize_rowwise_fp8(Xb)
+    qw, sw = oracle.quantize_rowwise_fp8(Wb)
+    y, _, ad = oracle.fp8_scaled_mm(oracle.NT, qx, sx, qw, sw, want_acc=True)
+    within_bound(Y, y, ad, np.abs(sx[:, None] * sw[None, :]).astype(np.float64), K, f"{tag} Y",
+                 group_term("NT", qx, qw))
+    qdy, sdy = oracle.quantize_rowwise_fp8(dYb)
+    qwc, swc = oracle.quantize_colwise_fp8(Wb)
+    y, _, ad = oracle.fp8_scaled_mm(oracle.NN, qdy, sdy, qwc, swc, want_acc=True)
+    within_bound(dX, y, ad, np.abs(sdy[:, None] * swc[None, :]).astype(np.float64), N, f"{tag} dX",
+                 group_term("NN", qdy, qwc))
+    qdyc, sdyc = oracle.quantize_colwise_fp8(dYb)
+    qxc, sxc = oracle.quantize_colwise_fp8(Xb)
+    y, _, ad = oracle.fp8_scaled_mm(oracle.TN, qdyc, sdyc, qxc, sxc, want_acc=True)
+    within_bound(dW, y, ad, np.abs(sdyc[:, None] * sxc[None, :]).astype(np.float64), M, f"{tag} dW",
+                 group_term("TN", qdyc, qxc))
+
+
+# The chains that hand X's and W's column maxima from the forward to the
+# backward: the paired launches (X and W rows; dY rows with W columns, dY
+# rows of 4 or 8 chunks per lane, whole and ragged; dY and X columns), the
+# maxima folded in the GEMMs, rows over 14336 elements (the forward's maxima
+# then from a pass of their own), contractions that are not multiples of 16
+# (general GEMM kernel).  Outputs equal the plain chains' byte for byte, the
+# maxima equal the oracle's, and the outputs are within the bound of the
+# oracle's exact sums.
+@pytest.mark.parametrize("M,N,K", [(300, 264, 1024), (136, 2048, 1024), (64, 3000, 512), (96, 4096, 520),
+                                   (40, 24, 15000), (33, 40, 40), (1, 1032, 4104)])
+def test_linear_chains_fp8_with_column_maxima(M, N, K):
+    t = linear_inputs(LinearShape("fp8_colmax", M, N, K), seed=M + N + K, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
+    Y, cx, cw = i8.linear_fwd_fp8_colmax(X, W)
+    dX, dW = i8.linear_bwd_fp8(dY, X, W, colmax_x=cx, colmax_w=cw)
+    Y0 = i8.linear_fwd_fp8(X, W)
+    dX0, dW0 = i8.linear_bwd_fp8(dY, X, W)
+    torch.cuda.synchronize()
+    same_f32(cx, oracle.col_absmax(Xb), "colmax X")
+    same_f32(cw, oracle.col_absmax(Wb), "colmax W")
+    for got, want, what in ((Y, Y0, "Y"), (dX, dX0, "dX"), (dW, dW0, "dW")):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{what} differs from the plain chain's"
+    oracle_fp8_chain_check(tensor_bits(Y), tensor_bits(dX), tensor_bits(dW), Xb, Wb, dYb, f"colmax chain {M}x{N}x{K}")
+
+
+# Few output tiles and a long contraction: the chain GEMM sums its
+# contraction in slices into fp32 planes (forward at 256 x 256 x 8192,
+# grad-input at 256 x 8192 x 256, grad-weight at 8192 x 256 x 256), plain and
+# with column maxima (the same bytes), within the bound of the exact sums.
+@pytest.mark.parametrize("M,N,K", [(256, 256, 8192), (256, 8192, 256), (8192, 256, 256)])
+def test_linear_chains_fp8_contraction_split(M, N, K):
+    t = linear_inputs(LinearShape("fp8_split", M, N, K), seed=7, device="cuda")
+    X, W, dY = t["X"], t["W"], t["dY"]
+    Xb, Wb, dYb = tensor_bits(X), tensor_bits(W), tensor_bits(dY)
+    Y, cx, cw = i8.linear_fwd_fp8_colmax(X, W)
+    dX, dW = i8.linear_bwd_fp8(dY, X, W, colmax_x=cx, colmax_w=cw)
+    Y0 = i8.linear_fwd_fp8(X, W)
+    dX0, dW0 = i8.linear_bwd_fp8(dY, X, W)
+    torch.cuda.synchronize()
+    for got, want, what in ((Y, Y0, "Y"), (dX, dX0, "dX"), (dW, dW0, "dW")):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{what}: column-maxima chain differs"
+    oracle_fp8_chain_check(tensor_bits(Y), tensor_bits(dX), tensor_bits(dW), Xb, Wb, dYb, f"split chain {M}x{N}x{K}")
 
 
 def test_fp8_group_truncation_rule():
