@@ -14,6 +14,12 @@ struct u32x4 {
   uint32_t w[4];
 };
 
+// a ^ b ^ c in one instruction: gfx950's three-input bitwise operation with
+// the truth table of XOR (0x96), where two dependent XORs would take two.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Ten rounds; the key is bumped by the two Weyl constants between rounds.
 // Each round forms the full 64-bit products of counter words 0 and 2 with
 // the two round multipliers and mixes their halves into the next counter.
@@ -23,8 +29,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   for (int i = 0; i < 10; ++i) {
     const uint64_t p = (uint64_t)0xD2511F53u * c0;
     const uint64_t t = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(t >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(t >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p >> 32), c3, k1);
     c1 = (uint32_t)t;
     c3 = (uint32_t)p;
     c0 = n0;
