@@ -55,9 +55,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 GEMM_COUNTERS = os.path.join(PROFILES, "gemm_counters_square_4096.txt")
 VALU_COUNTERS = os.path.join(PROFILES, "quantize_valu_counters_square_4096.txt")
 TRIALS = 5
+CONTEXTS = ("other_rounding", "sr_passes", "elementwise", "cold_warm", "mfma_ceiling", "torch_bf16", "torch_int8",
+            "autograd", "fp8", "single_linear", "square_sweep", "quantize_large", "llama1b", "ablation", "llama3_8b")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -72,15 +74,18 @@ def parse():
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context measurements (sweep, Llama layers, ablation, ...)")
     ap.add_argument("--context", default=None,
-                    help="comma-separated context measurements to run (and no others): other_rounding, "
-                         "sr_passes, elementwise, cold_warm, mfma_ceiling, torch_bf16, torch_int8, autograd, fp8, "
-                         "single_linear, square_sweep, quantize_large, llama1b, ablation, llama3_8b")
+                    help="comma-separated context measurements to run (and no others): " + ", ".join(CONTEXTS))
     ap.add_argument("--only-step", action="store_true",
                     help="the timed step and its per-kernel timing only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy one 256 MiB buffer with torch (a plain "
                          "copy kernel of known size for scaling HBM byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args(argv)
+    if args.context is not None:
+        unknown = sorted(set(args.context.split(",")) - set(CONTEXTS))
+        if unknown:
+            ap.error(f"--context: unknown name(s) {unknown}")
+    return args
 
 
 # --------------------------------------------------------------------------- counter summaries
@@ -295,8 +300,7 @@ def main():
          lambda: context_llama3_8b_layers(i8, dev, stream, records)),
     )
     chosen = None if args.context is None else set(args.context.split(","))
-    if chosen is not None and not chosen <= {nm for _, nm, _, _ in runs}:
-        raise SystemExit(f"--context: unknown name(s) {sorted(chosen - {nm for _, nm, _, _ in runs})}")
+    assert {nm for _, nm, _, _ in runs} == set(CONTEXTS)
     for group, nm, key, fn in runs:
         if chosen is not None:
             on = nm in chosen
