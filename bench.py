@@ -896,9 +896,16 @@ def context_ablation(i8, dev, stream, records):
 
 def context_llama3_8b_layers(i8, dev, stream, records):
     """The seven Llama-3-8B decoder linears and the LM head [4096 -> 128256]
-    at 8192 tokens."""
+    at 8192 tokens, with round to nearest even, and the same steps with
+    stochastic rounding (rows of 14336 and 128256 elements take the two-read
+    kernels there)."""
     from workloads import llama3_8b_layers
-    res, _ = layer_steps(i8, dev, stream, llama3_8b_layers(), "llama3_8b_", 5, "rne", records, "llama3_8b_layers_rne")
+    res, t16 = layer_steps(i8, dev, stream, llama3_8b_layers(), "llama3_8b_", 5, "rne", records,
+                           "llama3_8b_layers_rne")
+    sr, _ = layer_steps(i8, dev, stream, llama3_8b_layers(), "llama3_8b_", 5, "sr", records, "llama3_8b_layers_sr")
+    res["sr"] = {"int8_us": sr["int8_us"], "int8_tops": sr["int8_tops"], "time_vs_rne": round(sr["int8_us"] / res["int8_us"], 3),
+                 "speedup_vs_bf16": round(t16 / sr["int8_us"], 3),
+                 "per_linear_us": {k: v["int8_us"] for k, v in sr["per_linear"].items()}}
     return res
 
 

@@ -412,8 +412,8 @@ i8mp_status i8mp_linear_fwd_colmax(const uint16_t* X, const uint16_t* W, uint16_
       side.part[1] = static_cast<const uint16_t*>(w.part_w);
       side.colmax[0] = colmax_x;
       side.colmax[1] = colmax_w;
-      i8mp::rowwise_colmax_geometry(M, K, &side.slabs[0], &side.part_ld);
-      i8mp::rowwise_colmax_geometry(N, K, &side.slabs[1], &side.part_ld);
+      i8mp::rowwise_colmax_geometry(M, K, r, &side.slabs[0], &side.part_ld);
+      i8mp::rowwise_colmax_geometry(N, K, r, &side.slabs[1], &side.part_ld);
     }
   } else {
     e = colmax_x ? i8mp::launch_quantize_rowwise_colmax(X, M, K, K, w.qx, kp, w.sx, colmax_x, r, opts->seed,
@@ -492,7 +492,7 @@ i8mp_status i8mp_linear_bwd_colmax(const uint16_t* dY, const uint16_t* X, const 
       side.cols = N;
       side.part[0] = static_cast<const uint16_t*>(w.col);
       side.colmax[0] = w.cdy;
-      i8mp::rowwise_colmax_geometry(M, N, &side.slabs[0], &side.part_ld);
+      i8mp::rowwise_colmax_geometry(M, N, r, &side.slabs[0], &side.part_ld);
     } else {
       e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax(dY, M, N, N, w.qdy, np, w.sdy, w.cdy, r, seed,
                                                            pass_offset(opts->offset, 2), w.col, s)
@@ -642,8 +642,8 @@ i8mp_status i8mp_linear_fwd_fp8_colmax(const uint16_t* X, const uint16_t* W, uin
     side.part[1] = static_cast<const uint16_t*>(w.part_w);
     side.colmax[0] = colmax_x;
     side.colmax[1] = colmax_w;
-    i8mp::rowwise_colmax_geometry(M, K, &side.slabs[0], &side.part_ld);
-    i8mp::rowwise_colmax_geometry(N, K, &side.slabs[1], &side.part_ld);
+    i8mp::rowwise_colmax_geometry(M, K, 0, &side.slabs[0], &side.part_ld);
+    i8mp::rowwise_colmax_geometry(N, K, 0, &side.slabs[1], &side.part_ld);
   } else {
     const uint16_t* src[2] = {X, W};
     const int64_t rows[2] = {M, N};
@@ -720,7 +720,7 @@ i8mp_status i8mp_linear_bwd_fp8_colmax(const uint16_t* dY, const uint16_t* X, co
       side.cols = N;
       side.part[0] = static_cast<const uint16_t*>(w.col);
       side.colmax[0] = w.cdy;
-      i8mp::rowwise_colmax_geometry(M, N, &side.slabs[0], &side.part_ld);
+      i8mp::rowwise_colmax_geometry(M, N, 0, &side.slabs[0], &side.part_ld);
     } else {
       e = dy_colmax ? i8mp::launch_quantize_rowwise_colmax_fp8(dY, M, N, N, qdy, np, w.sdy, w.cdy, w.col, true, s)
                     : i8mp::launch_quantize_rowwise_fp8(dY, M, N, N, qdy, np, w.sdy, s);

@@ -129,8 +129,11 @@ struct ColmaxJob {
   int64_t part_ld, cols;
   int n;  // tensors (0: nothing to reduce)
 };
-// The slab-maxima geometry of a row pass with column maxima over rows x cols.
-void rowwise_colmax_geometry(int64_t rows, int64_t cols, int64_t* slabs, int64_t* part_ld);
+// The slab-maxima geometry of a row pass with column maxima over rows x cols
+// under rounding `round` (stochastic rounding takes the banded path for rows
+// of more than 16 chunks per lane, 12 when the width is not a multiple of 4,
+// with its own slab count).
+void rowwise_colmax_geometry(int64_t rows, int64_t cols, int round, int64_t* slabs, int64_t* part_ld);
 // The reduction as its own launch (colmax_finalize, or colmax_finalize2 for
 // two tensors).
 hipError_t launch_colmax_finalize(const ColmaxJob& job, hipStream_t stream);

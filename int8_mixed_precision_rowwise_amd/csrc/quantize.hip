@@ -208,12 +208,19 @@ __device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, u
       u[4 + j] = word_to_uniform(w1.w[j]);
     }
   } else {
+    // Elements e0 .. e0+7 take words s .. s+7 (s = e0 mod 4) of the three
+    // consecutive blocks from block offset + e0 / 4 on.  s is the same in
+    // every lane of a wave where the callers call this (e0 = row * cols + a
+    // multiple of 8); each element selects among its four candidate words,
+    // all at constant indices.
+    const uint64_t b = offset + (e0 >> 2);
+    const u32x4 w0 = philox_block(seed, b), w1 = philox_block(seed, b + 1), w2 = philox_block(seed, b + 2);
+    const uint32_t w[12] = {w0.w[0], w0.w[1], w0.w[2], w0.w[3], w1.w[0], w1.w[1],
+                            w1.w[2], w1.w[3], w2.w[0], w2.w[1], w2.w[2], w2.w[3]};
+    const uint32_t s = (uint32_t)(e0 & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint64_t e = e0 + j;
-      const u32x4 w = philox_block(seed, offset + (e >> 2));
-      const uint32_t k = (uint32_t)(e & 3);
-      const uint32_t word = k == 0 ? w.w[0] : k == 1 ? w.w[1] : k == 2 ? w.w[2] : w.w[3];
+      const uint32_t word = s == 0 ? w[j] : s == 1 ? w[j + 1] : s == 2 ? w[j + 2] : w[j + 3];
       u[j] = word_to_uniform(word);
     }
   }
@@ -1014,6 +1021,18 @@ ColPlan col_plan(int64_t rows, int64_t cols) {
   return p;
 }
 
+// Widest row (16-byte chunks per lane) held in registers under stochastic
+// rounding: beyond it the row and the Philox draws beside it no longer fit
+// (the 28-chunk kernels spilled the row to scratch and ran 4x slower than
+// round to nearest), so those rows take the two-read kernels instead.  Rows
+// whose length is not a multiple of 4 draw a third Philox block per chunk:
+// for them the limit is 12.
+constexpr int kSrFusedChunks = 16;
+constexpr int kSrFusedChunksUnaligned = 12;
+__host__ __device__ constexpr int64_t widest_in_registers(int round, int64_t cols) {
+  return round == 1 ? (cols % 4 == 0 ? kSrFusedChunks : kSrFusedChunksUnaligned) : 28;
+}
+
 template <int NV>
 void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
                     int64_t ldq, float* scale, int round, uint64_t seed, uint64_t offset,
@@ -1023,10 +1042,12 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
   constexpr bool PF = false;
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
-    if (a4)
-      quant_rows_wave<NV, true, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
-    else
-      quant_rows_wave<NV, true, false, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    if constexpr (NV <= kSrFusedChunks) {
+      if (a4)
+        quant_rows_wave<NV, true, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+      else if constexpr (NV <= kSrFusedChunksUnaligned)
+        quant_rows_wave<NV, true, false, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    }
   } else if (cols == NV * 512) {
     quant_rows_wave<NV, false, true, PF, 0, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   } else {
@@ -1040,7 +1061,9 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
 // regions grow with the row), about 256 blocks, each a band of whole rows
 // (a multiple of 16 rows, so the bands do not depend on the wave count).
 // Rows longer than 14336 elements go through rows_long_stats and
-// rows_long_quant (bands of rows by segments of 4096 columns).
+// rows_long_quant (bands of rows by segments of 4096 columns), and so do rows
+// of more than kSrFusedChunks chunks per lane under stochastic rounding.
+
 struct RowColmaxPlan {
   bool fused;
   int waves;
@@ -1049,10 +1072,10 @@ struct RowColmaxPlan {
   size_t part_bytes;   // slab maxima; the segment maxima ([rows][nseg] bf16 bits) follow
 };
 
-RowColmaxPlan rcm_plan(int64_t rows, int64_t cols) {
+RowColmaxPlan rcm_plan(int64_t rows, int64_t cols, int round = 0) {
   RowColmaxPlan p;
   const int64_t per_lane = (cols + 511) / 512;
-  p.fused = per_lane <= 28;
+  p.fused = per_lane <= widest_in_registers(round, cols);
   p.part_ld = (cols + 7) / 8 * 8;
   if (p.fused) {
     // about one block per CU (a block's registers and LDS fill most of one)
@@ -1099,10 +1122,12 @@ void launch_rcm2_nv(const RowColmaxJob& a, const RowColmaxJob& b, int64_t cols, 
     else
       quant_rows_colmax2<NV, WAVES_WIDE, false, true, false, 1><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
   } else if (round == 1) {
-    if (a4)
-      quant_rows_colmax2<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
-    else
-      quant_rows_colmax2<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+    if constexpr (NV <= kSrFusedChunks) {
+      if (a4)
+        quant_rows_colmax2<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+      else if constexpr (NV <= kSrFusedChunksUnaligned)
+        quant_rows_colmax2<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+    }
   } else if (cols == NV * 512) {
     // two tensors' bands: with the 16-wave shape's LDS (WAVES x NV KiB) only one
     // block fits per CU, so a pair would run as two rounds; 8 waves (two rows
@@ -1121,14 +1146,32 @@ void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int6
   const dim3 grid((unsigned)p.slabs);
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
-    if (a4)
-      quant_rows_colmax<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
-    else
-      quant_rows_colmax<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+    if constexpr (NV <= kSrFusedChunks) {
+      if (a4)
+        quant_rows_colmax<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+      else if constexpr (NV <= kSrFusedChunksUnaligned)
+        quant_rows_colmax<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+    }
   } else if (cols == NV * 512) {
     quant_rows_colmax<NV, WAVES, false, true, true><<<grid, 64 * WAVES, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
   } else {
     quant_rows_colmax<NV, WAVES_WIDE, false, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+  }
+}
+
+// Rows past widest_in_registers chunks per lane: one block per row, the row
+// read twice (maximum, then codes).
+void launch_rows_block(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
+                       int64_t ldq, float* scale, int round, uint64_t seed, uint64_t offset,
+                       hipStream_t stream) {
+  const dim3 grid((unsigned)rows);
+  if (round == 1) {
+    if (cols % 4 == 0)
+      quant_rows_block<true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+    else
+      quant_rows_block<true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+  } else {
+    quant_rows_block<false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
   }
 }
 
@@ -1139,7 +1182,9 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols
                                    uint64_t offset, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int64_t per_lane = (cols + 511) / 512;  // 16-byte chunks per lane
-  if (per_lane <= 1)
+  if (per_lane > widest_in_registers(round, cols))
+    launch_rows_block(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
+  else if (per_lane <= 1)
     launch_rows_nv<1>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
   else if (per_lane <= 2)
     launch_rows_nv<2>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
@@ -1153,20 +1198,8 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols
     launch_rows_nv<12>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
   else if (per_lane <= 16)
     launch_rows_nv<16>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
-  else if (per_lane <= 28)
+  else
     launch_rows_nv<28>(x, rows, cols, ldx, q, ldq, scale, round, seed, offset, stream);
-  else {
-    const dim3 grid((unsigned)rows);
-    const bool a4 = (cols % 4) == 0;
-    if (round == 1) {
-      if (a4)
-        quant_rows_block<true, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
-      else
-        quant_rows_block<true, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
-    } else {
-      quant_rows_block<false, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
-    }
-  }
   return hipGetLastError();
 }
 
@@ -1384,9 +1417,14 @@ hipError_t launch_quantize_colwise_static(const uint16_t* x, int64_t rows, int64
 }
 
 size_t rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols) {
-  const RowColmaxPlan p = rcm_plan(rows, cols);
-  if (p.fused) return p.part_bytes;
-  return (p.part_bytes + 255) / 256 * 256 + (size_t)(max(rows, (int64_t)1) * p.nseg * 2);
+  size_t need = 0;
+  for (int round = 0; round < 2; ++round) {  // either rounding's plan fits
+    const RowColmaxPlan p = rcm_plan(rows, cols, round);
+    const size_t n = p.fused ? p.part_bytes
+                             : (p.part_bytes + 255) / 256 * 256 + (size_t)(max(rows, (int64_t)1) * p.nseg * 2);
+    need = max(need, n);
+  }
+  return need;
 }
 
 hipError_t launch_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
@@ -1403,7 +1441,7 @@ hipError_t launch_quantize_rowwise_slabs(const uint16_t* x, int64_t rows, int64_
                                          bool finalize, hipStream_t stream) {
   // no columns: no maxima, but every row's scale is still written (0)
   if (cols == 0) return launch_quantize_rowwise(x, rows, 0, ldx, q, ldq, scale, round, seed, offset, stream);
-  const RowColmaxPlan p = rcm_plan(rows, cols);
+  const RowColmaxPlan p = rcm_plan(rows, cols, round);
   uint16_t* part = static_cast<uint16_t*>(ws);
   if (rows > 0) {
     if (p.fused) {
@@ -1477,7 +1515,7 @@ hipError_t launch_quantize_rowwise_colmax_pair(
     if (e != hipSuccess) return e;
     return launch_quantize_rowwise(xb, rows_b, 0, ldxb, qb, ldqb, scale_b, round, seed, offset_b, stream);
   }
-  const RowColmaxPlan pa = rcm_plan(rows_a, cols), pb = rcm_plan(rows_b, cols);
+  const RowColmaxPlan pa = rcm_plan(rows_a, cols, round), pb = rcm_plan(rows_b, cols, round);
   if (!pa.fused || rows_a == 0 || rows_b == 0) {
     if (fmt == 1) {  // rows of at most 14336 elements (the FP8 row pass with maxima)
       const hipError_t e = launch_quantize_rowwise_colmax_fp8(xa, rows_a, cols, ldxa, reinterpret_cast<uint8_t*>(qa),
@@ -1519,8 +1557,8 @@ hipError_t launch_quantize_rowwise_colmax_pair(
   return hipGetLastError();
 }
 
-void rowwise_colmax_geometry(int64_t rows, int64_t cols, int64_t* slabs, int64_t* part_ld) {
-  const RowColmaxPlan p = rcm_plan(rows, cols);
+void rowwise_colmax_geometry(int64_t rows, int64_t cols, int round, int64_t* slabs, int64_t* part_ld) {
+  const RowColmaxPlan p = rcm_plan(rows, cols, round);
   *slabs = rows > 0 ? p.slabs : 0;
   *part_ld = p.part_ld;
 }
@@ -1583,7 +1621,7 @@ hipError_t launch_quantize_rowslabs_colgiven(
     float* scale_a, uint64_t offset_a, void* ws_a, const uint16_t* xb, int64_t rows_b, int64_t cols_b,
     int64_t ldxb, const float* colmax_b, int8_t* qb, int64_t ldqb, float* scale_b, uint64_t offset_b,
     int round, uint64_t seed, int fmt, hipStream_t stream) {
-  const RowColmaxPlan pa = rcm_plan(rows_a, cols_a);
+  const RowColmaxPlan pa = rcm_plan(rows_a, cols_a, round);
   const int64_t per_lane = (cols_a + 511) / 512;
   const int nv = per_lane > 2 && per_lane <= 4 ? 4 : (per_lane > 4 && per_lane <= 8 ? 8 : 0);
   const bool a4 = cols_a % 4 == 0 && cols_b % 4 == 0;

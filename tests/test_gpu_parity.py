@@ -53,7 +53,8 @@ def test_philox_words(seed, offset):
 # --------------------------------------------------------------------------- quantization
 
 ROW_SHAPES = [(1, 1), (3, 17), (5, 255), (7, 513), (64, 2048), (9, 5000), (6, 5632), (4, 8192),
-              (5, 14336), (3, 16385), (2, 30001), (2, 128256)]
+              (5, 14336), (3, 16385), (2, 30001), (2, 128256), (33, 7001), (70, 8191),
+              (20, 9000), (11, 12290)]
 
 
 @pytest.mark.parametrize("rounding,rc", ROUNDINGS)
