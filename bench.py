@@ -55,7 +55,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 GEMM_COUNTERS = os.path.join(PROFILES, "gemm_counters_square_4096.txt")
 VALU_COUNTERS = os.path.join(PROFILES, "quantize_valu_counters_square_4096.txt")
 TRIALS = 5
-CONTEXTS = ("other_rounding", "sr_passes", "elementwise", "cold_warm", "mfma_ceiling", "torch_bf16", "torch_int8",
+CONTEXTS = ("other_rounding", "sr_passes", "elementwise", "cold_warm", "mfma_ceiling", "hip_graph", "torch_bf16",
+            "torch_int8",
             "autograd", "fp8", "single_linear", "square_sweep", "quantize_large", "llama1b", "ablation", "llama3_8b")
 
 
@@ -210,19 +211,21 @@ def main():
     ws_fwd = torch.empty(L.i8mp_linear_workspace_bytes(M, N, K, 0), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(L.i8mp_linear_workspace_bytes(M, N, K, 1), dtype=torch.uint8, device=dev)
 
-    def chain_step(i, rr=r):
+    def chain_step(i, rr=r, on=None):
         """The step as the library runs it: i8mp_linear_fwd_colmax (X's and W's
         row passes in one launch, leaving slab maxima of their columns; the NT
         GEMM, which reduces those slabs to X's and W's column maxima in its
-        prologue), then i8mp_linear_bwd_colmax (dY's row pass; W's column
-        pass; the NN GEMM, reducing dY's slabs in its prologue; dY's and X's
-        column passes in one launch; the TN GEMM): 7 launches."""
+        prologue), then i8mp_linear_bwd_colmax (dY's row pass and W's column
+        pass in one launch; the NN GEMM, reducing dY's slabs in its prologue;
+        dY's and X's column passes in one launch; the TN GEMM): 6 launches, on
+        the bench's stream or on the stream `on` (a ctypes pointer)."""
         X, W, dY = sets[i % args.sets]
         o = i8._Opts(rr, seed, (i % 1024) << 44)
+        s_ = sp if on is None else on
         st = L.i8mp_linear_fwd_colmax(p(X), p(W), p(Y), M, N, K, ctypes.byref(o), p(cX), p(cW), p(ws_fwd),
-                                      ws_fwd.numel(), sp)
+                                      ws_fwd.numel(), s_)
         st = st or L.i8mp_linear_bwd_colmax(p(dY), p(X), p(W), p(dX), p(dW), M, N, K, ctypes.byref(o),
-                                            p(cX), p(cW), p(ws_bwd), ws_bwd.numel(), sp)
+                                            p(cX), p(cW), p(ws_bwd), ws_bwd.numel(), s_)
         A.ok(st, "linear chain step")
 
     # the chains' outputs equal the public primitives' (one quantize pass and
@@ -284,6 +287,8 @@ def main():
         ("step", "elementwise", "context_elementwise_reference", lambda: elementwise_reference(sets, args.kernel_iters, stream)),
         ("step", "cold_warm", "context_gemm_cold_vs_warm", lambda: gemm_cold_warm(A, n, args.kernel_iters, stream, records)),
         ("step", "mfma_ceiling", "context_mfma_power_ceiling", lambda: mfma_ceiling(A, prim["qX"], breakdown, stream)),
+        ("step", "hip_graph", "context_step_as_hip_graph",
+         lambda: graph_step(chain_step, (Y, dX, dW), args, stream, step_ms)),
         ("wide", "torch_bf16", "context_torch_bf16_matmul_tflops", lambda: torch_bf16(sets[0], stream, gemm_ops)),
         ("wide", "torch_int8", "context_torch_int_mm_hipblaslt", lambda: torch_int8_mm(sets, prim, args.kernel_iters,
                                                                                         stream, gemm_ops)),
@@ -438,6 +443,32 @@ def step_breakdown(A, sets, prim, r, seed, iters, stream):
 
 
 # --------------------------------------------------------------------------- context measurements
+
+
+def graph_step(chain_step, outs, args, stream, step_ms):
+    """The step captured as a HIP graph (torch.cuda.CUDAGraph; the library
+    allocates, clears and synchronizes nothing, so the capture holds the six
+    kernel launches of each step), one step per input set, then replayed
+    back to back: ms per step against the eager launches'.  The last replay's
+    outputs are checked against the eager step's on the same inputs."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(args.sets):
+            chain_step(i, on=cs)
+    reps = max(1, args.steps // args.sets)
+    us = time_us(g.replay, stream, reps, warm=2)
+    got = [t.clone() for t in outs]
+    chain_step(args.sets - 1)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(got, outs)):
+        raise RuntimeError("the graph replay's outputs differ from the eager step's")
+    del g
+    ms = us / 1e3 / args.sets
+    return {"ms_per_step": round(ms, 4), "time_vs_eager": round(ms / step_ms, 3),
+            "steps_per_replay": args.sets, "replays": reps}
 
 
 def other_rounding(chain_step, r, step_ms, args, stream, gemm_ops):

@@ -256,6 +256,16 @@ def test_llama3_8b_layer_rne(layer):
     run_layer(shape, "rne")
 
 
+@pytest.mark.parametrize("layer", ["llama3_8b_gate_proj", "llama3_8b_down_proj"])
+def test_llama3_8b_layer_sr_with_column_maxima(layer):
+    """Stochastic rounding on 14336-wide rows (dY of gate_proj; X and W of
+    down_proj): the plain row passes take the block-per-row kernel and the
+    chains' row passes with column maxima the banded two-read kernels, since
+    the row with its uniforms no longer fits one wave's registers."""
+    shape = next(s for s in llama3_8b_layers() if s.name == layer)
+    run_layer(shape, "sr", seed=11, offset=5, colmax=True)
+
+
 def test_llama3_8b_lm_head_with_column_maxima():
     """The LM head [4096 -> 128256] at 8192 tokens through the column-maxima
     chains: dY's 128256-wide rows take the banded two-pass row kernel, and its
