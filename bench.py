@@ -17,8 +17,9 @@ trials of exactly --steps steps each are timed with HIP events on that stream
 trial's.
 
 Each kernel of the step is also timed on its own: --kernel-iters back-to-back
-launches between two events on the launch stream (quantize passes on rotating
-inputs), so the per-launch figure carries no event overhead.  `roofline`
+launches between two events on the launch stream (quantize passes rotating
+over 1 GiB of inputs, four times the MALL), so the per-launch figure carries no
+event overhead.  `roofline`
 describes the GEMM with the largest time; `breakdown` every pass.
 
 Printed: one JSON line.  `value` is the step's INT8 GEMM throughput,
@@ -256,7 +257,8 @@ def main():
     value = 3 * gemm_ops / (step_ms * 1e-3) / 1e12
 
     # each kernel of the step on its own, back to back
-    breakdown = step_breakdown(A, sets, prim, r, seed, args.kernel_iters, stream)
+    pool = cold_pool(sets, n, dev)
+    breakdown = step_breakdown(A, sets, pool, prim, r, seed, args.kernel_iters, stream)
     gemms = [k for k in breakdown if k.startswith("gemm")]
     dom = max(gemms, key=lambda k: breakdown[k]["us"])
     achieved = gemm_ops / (breakdown[dom]["us"] * 1e-6) / 1e12
@@ -283,8 +285,8 @@ def main():
     runs = (
         ("step", "other_rounding", "context_other_rounding_step",
          lambda: other_rounding(chain_step, r, step_ms, args, stream, gemm_ops)),
-        ("step", "sr_passes", "context_sr_quantize_passes", lambda: sr_passes(A, sets, n, args.kernel_iters, stream)),
-        ("step", "elementwise", "context_elementwise_reference", lambda: elementwise_reference(sets, args.kernel_iters, stream)),
+        ("step", "sr_passes", "context_sr_quantize_passes", lambda: sr_passes(A, pool, n, args.kernel_iters, stream)),
+        ("step", "elementwise", "context_elementwise_reference", lambda: elementwise_reference(pool, args.kernel_iters, stream)),
         ("step", "cold_warm", "context_gemm_cold_vs_warm", lambda: gemm_cold_warm(A, n, args.kernel_iters, stream, records)),
         ("step", "mfma_ceiling", "context_mfma_power_ceiling", lambda: mfma_ceiling(A, prim["qX"], breakdown, stream)),
         ("step", "hip_graph", "context_step_as_hip_graph",
@@ -386,9 +388,21 @@ def primitive_step(A, inputs, r, seed, off):
     return out
 
 
-def step_breakdown(A, sets, prim, r, seed, iters, stream):
+def cold_pool(sets, n, dev, nbytes=1 << 30):
+    """n x n bf16 tensors totalling at least `nbytes` (4x the 256 MB MALL):
+    the step's inputs, then standard normal draws.  Quantize passes and the
+    copy reference rotate over them, so every timed call reads cold HBM."""
+    import torch
+    pool = [t for s in sets for t in s]
+    g = torch.Generator(device=dev).manual_seed(4321)
+    while len(pool) * n * n * 2 < nbytes:
+        pool.append(torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16))
+    return pool
+
+
+def step_breakdown(A, sets, pool, prim, r, seed, iters, stream):
     """Each primitive pass of the step timed as `iters` back-to-back launches:
-    quantize passes rotate over the input sets (each reads HBM), GEMMs run on
+    quantize passes rotate over the cold pool (each reads HBM), GEMMs run on
     the step's codes (warm, as right after their quantize passes)."""
     import torch
     L, p, sp = A.L, A.p, A.sp
@@ -403,9 +417,9 @@ def step_breakdown(A, sets, prim, r, seed, iters, stream):
     ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
     k = [0]
 
-    def pick(j):
+    def pick(j):  # every step tensor is n x n: any pool tensor stands in for tensor j
         k[0] += 1
-        return sets[k[0] % len(sets)][j]
+        return pool[k[0] % len(pool)]
 
     def row(j, R, C):
         return lambda: A.ok(L.i8mp_quantize_rowwise_colmax(p(pick(j)), R, C, C, p(q), C, p(srow), p(cm), r, seed, 0,
@@ -493,7 +507,7 @@ def other_rounding(chain_step, r, step_ms, args, stream, gemm_ops):
             "tops": round(3 * gemm_ops / (ms * 1e-3) / 1e12, 1), "time_vs_this_step": round(ms / step_ms, 3)}
 
 
-def sr_passes(A, sets, n, iters, stream):
+def sr_passes(A, pool, n, iters, stream):
     """The step's quantize passes at n x n under both roundings, in
     algorithmic GB/s against the HBM peak and, for stochastic rounding, in
     VALU lane operations against the VALU issue peak.  VALU operations per
@@ -501,17 +515,17 @@ def sr_passes(A, sets, n, iters, stream):
     per dispatch of the same kernels on the current sources); null otherwise."""
     import torch
     L, p, sp = A.L, A.p, A.sp
-    q = torch.empty((n, n), dtype=torch.int8, device=sets[0][0].device)
+    q = torch.empty((n, n), dtype=torch.int8, device=pool[0].device)
     s = torch.empty(n, device=q.device)
     cm = torch.empty(n, device=q.device)
-    wsb = L.i8mp_quantize_rowwise_colmax_workspace_bytes(n, n)
+    wsb = max(L.i8mp_quantize_rowwise_colmax_workspace_bytes(n, n), 1)
     ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-    maxima = [A.i8.quantize_rowwise_colmax(t[0])[2] for t in sets]  # each X's column maxima
+    maxima = [A.i8.quantize_rowwise_colmax(t)[2] for t in pool]  # each tensor's column maxima
     k = [0]
 
     def nxt():
         k[0] += 1
-        return sets[k[0] % len(sets)][0], maxima[k[0] % len(sets)]
+        return pool[k[0] % len(pool)], maxima[k[0] % len(pool)]
 
     def row_pass(rr):
         x, _ = nxt()
@@ -538,14 +552,13 @@ def sr_passes(A, sets, n, iters, stream):
     return out
 
 
-def elementwise_reference(sets, iters, stream):
+def elementwise_reference(pool, iters, stream):
     """What a plain streaming kernel reaches on the same bytes and the same
     cold inputs: torch's bf16 copy of an n x n tensor (4 bytes moved per
     element) and of two such tensors stacked (the paired passes' byte count),
-    its source rotating over the input sets exactly as the quantize passes'
-    do (more than the 256 MB MALL holds)."""
+    its source rotating over the cold pool as the quantize passes' do."""
     import torch
-    src1 = [t for s in sets for t in s]
+    src1 = pool
     src2 = [torch.cat([src1[i], src1[(i + 1) % len(src1)]]) for i in range(0, len(src1), 2)]
     d1 = torch.empty_like(src1[0])
     d2 = torch.empty_like(src2[0])

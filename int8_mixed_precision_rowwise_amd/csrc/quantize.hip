@@ -1062,7 +1062,7 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
 // (a multiple of 16 rows, so the bands do not depend on the wave count).
 // Rows longer than 14336 elements go through rows_long_stats and
 // rows_long_quant (bands of rows by segments of 4096 columns), and so do rows
-// of more than kSrFusedChunks chunks per lane under stochastic rounding.
+// wider than widest_in_registers under stochastic rounding.
 
 struct RowColmaxPlan {
   bool fused;
