@@ -307,6 +307,10 @@ __device__ __forceinline__ void quantize_row_mode(const uint4 (&v)[NV], const Gr
       else
         store_partial(qr + c0, codes, (int)(cols - c0));
     }
+    // Under stochastic rounding, one chunk's Philox blocks at a time: left
+    // free, the scheduler starts the next chunks' blocks early and the live
+    // words of several chunks push the register count past 128.
+    if constexpr (SR && MODE > 0) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -728,16 +732,20 @@ __device__ __forceinline__ void rows_colmax_band(
   uint4 v[NV];
   int64_t r = r_begin + wave;
   if (r < r_end) load_row<NV, FULL>(v, x + r * ldx, cols, lane);
-  for (; r < r_end; r += WAVES) {
+  // One row: its column maxima into the wave's LDS region, then its codes.
+  auto row = [&](const uint4 (&cur)[NV], int64_t rr) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {  // load_row zeroed the columns past the end
       us2 m[4];
       const uint4 o = cm[wave][i * 64 + lane];
       m[0] = as_us2(o.x), m[1] = as_us2(o.y), m[2] = as_us2(o.z), m[3] = as_us2(o.w);
-      max_chunk(m, v[i]);
+      max_chunk(m, cur[i]);
       cm[wave][i * 64 + lane] = pack_max(m);
     }
-    quantize_row<NV, SR, ALIGNED4, FMT, FULL, true>(v, r, cols, q, ldq, scale, seed, offset, lane);
+    quantize_row<NV, SR, ALIGNED4, FMT, FULL, true>(cur, rr, cols, q, ldq, scale, seed, offset, lane);
+  };
+  for (; r < r_end; r += WAVES) {
+    row(v, r);
     const int64_t rn = r + WAVES;
     if (rn < r_end) load_row<NV, FULL>(v, x + rn * ldx, cols, lane);
   }
@@ -1043,7 +1051,9 @@ void launch_rows_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, 
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if constexpr (NV <= kSrFusedChunks) {
-      if (a4)
+      if (cols == NV * 512)
+        quant_rows_wave<NV, true, true, PF, 0, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
+      else if (a4)
         quant_rows_wave<NV, true, true, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
       else if constexpr (NV <= kSrFusedChunksUnaligned)
         quant_rows_wave<NV, true, false, PF><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset);
@@ -1123,7 +1133,9 @@ void launch_rcm2_nv(const RowColmaxJob& a, const RowColmaxJob& b, int64_t cols, 
       quant_rows_colmax2<NV, WAVES_WIDE, false, true, false, 1><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
   } else if (round == 1) {
     if constexpr (NV <= kSrFusedChunks) {
-      if (a4)
+      if (cols == NV * 512)
+        quant_rows_colmax2<NV, WAVES_WIDE, true, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
+      else if (a4)
         quant_rows_colmax2<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
       else if constexpr (NV <= kSrFusedChunksUnaligned)
         quant_rows_colmax2<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(a, b, cols, part_ld, seed);
@@ -1147,7 +1159,9 @@ void launch_rcm_nv(const RowColmaxPlan& p, const uint16_t* x, int64_t rows, int6
   const bool a4 = (cols % 4) == 0;
   if (round == 1) {
     if constexpr (NV <= kSrFusedChunks) {
-      if (a4)
+      if (cols == NV * 512)
+        quant_rows_colmax<NV, WAVES_WIDE, true, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
+      else if (a4)
         quant_rows_colmax<NV, WAVES_WIDE, true, true><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
       else if constexpr (NV <= kSrFusedChunksUnaligned)
         quant_rows_colmax<NV, WAVES_WIDE, true, false><<<grid, 64 * WAVES_WIDE, 0, stream>>>(x, rows, cols, ldx, q, ldq, scale, seed, offset, p.rows_per_block, part, p.part_ld);
@@ -1661,14 +1675,18 @@ hipError_t launch_quantize_rowslabs_colgiven(
     else
       quant_rows_cols_pair<8, false, true, false, 1><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
   } else if (nv == 4) {
-    if (round == 1)
+    if (round == 1 && full)
+      quant_rows_cols_pair<4, true, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else if (round == 1)
       quant_rows_cols_pair<4, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
     else if (full)
       quant_rows_cols_pair<4, false, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
     else
       quant_rows_cols_pair<4, false, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
   } else {
-    if (round == 1)
+    if (round == 1 && full)
+      quant_rows_cols_pair<8, true, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
+    else if (round == 1)
       quant_rows_cols_pair<8, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
     else if (full)
       quant_rows_cols_pair<8, false, true, true><<<grid, kColThreads, 0, stream>>>(a, cols_a, pa.part_ld, b, groups, seed);
