@@ -732,20 +732,16 @@ __device__ __forceinline__ void rows_colmax_band(
   uint4 v[NV];
   int64_t r = r_begin + wave;
   if (r < r_end) load_row<NV, FULL>(v, x + r * ldx, cols, lane);
-  // One row: its column maxima into the wave's LDS region, then its codes.
-  auto row = [&](const uint4 (&cur)[NV], int64_t rr) __attribute__((always_inline)) {
+  for (; r < r_end; r += WAVES) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {  // load_row zeroed the columns past the end
       us2 m[4];
       const uint4 o = cm[wave][i * 64 + lane];
       m[0] = as_us2(o.x), m[1] = as_us2(o.y), m[2] = as_us2(o.z), m[3] = as_us2(o.w);
-      max_chunk(m, cur[i]);
+      max_chunk(m, v[i]);
       cm[wave][i * 64 + lane] = pack_max(m);
     }
-    quantize_row<NV, SR, ALIGNED4, FMT, FULL, true>(cur, rr, cols, q, ldq, scale, seed, offset, lane);
-  };
-  for (; r < r_end; r += WAVES) {
-    row(v, r);
+    quantize_row<NV, SR, ALIGNED4, FMT, FULL, true>(v, r, cols, q, ldq, scale, seed, offset, lane);
     const int64_t rn = r + WAVES;
     if (rn < r_end) load_row<NV, FULL>(v, x + rn * ldx, cols, lane);
   }
