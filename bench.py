@@ -388,14 +388,15 @@ def primitive_step(A, inputs, r, seed, off):
     return out
 
 
-def cold_pool(sets, n, dev, nbytes=1 << 30):
-    """n x n bf16 tensors totalling at least `nbytes` (4x the 256 MB MALL):
-    the step's inputs, then standard normal draws.  Quantize passes and the
-    copy reference rotate over them, so every timed call reads cold HBM."""
+def cold_pool(sets, n, dev, nbytes=1 << 30, most=128):
+    """n x n bf16 tensors totalling at least `nbytes` (4x the 256 MB MALL),
+    at most `most` of them: the step's inputs, then standard normal draws.
+    Quantize passes and the copy reference rotate over them, so every timed
+    call reads cold HBM (at the default size: 32 tensors of 32 MiB)."""
     import torch
     pool = [t for s in sets for t in s]
     g = torch.Generator(device=dev).manual_seed(4321)
-    while len(pool) * n * n * 2 < nbytes:
+    while len(pool) * n * n * 2 < nbytes and len(pool) < most:
         pool.append(torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16))
     return pool
 
