@@ -161,8 +161,9 @@ i8mp_status i8mp_quantize_colwise_noalloc(const uint16_t* x, int64_t rows, int64
  *       cols) bytes, 256-byte aligned; its contents on entry do not matter.
  */
 /* Bytes of scratch i8mp_quantize_rowwise_colmax needs for rows x cols (slab
- * column maxima, and for rows over 14336 elements, or over 8192 under
- * stochastic rounding, the row-segment maxima), enough for either rounding;
+ * column maxima, and for rows over 14336 elements, or under stochastic
+ * rounding over 8192 (6144 when cols is not a multiple of 4), the
+ * row-segment maxima), enough for either rounding;
  * 0 for cols = 0 or invalid sizes. */
 size_t i8mp_quantize_rowwise_colmax_workspace_bytes(int64_t rows, int64_t cols);
 i8mp_status i8mp_quantize_rowwise_colmax(const uint16_t* x, int64_t rows, int64_t cols,
