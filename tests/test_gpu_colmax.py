@@ -30,7 +30,7 @@ ROUNDINGS = [("rne", oracle.RNE), ("sr", oracle.SR)]
 SHAPES = [(1, 1), (3, 17), (9, 255), (40, 513), (257, 2048), (100, 4096), (5000, 512),
           (33, 5000), (17, 6144), (21, 6152), (3000, 6200), (12, 8192), (9, 14336),
           (600, 14336), (3, 16385), (2, 30001), (300, 16392), (1030, 20001),
-          (33, 7001), (70, 8191), (20, 9000), (64, 12290)]
+          (33, 7001), (70, 8191), (20, 9000), (64, 12290), (40, 5632)]
 
 
 def same_f32(t: torch.Tensor, want: np.ndarray, what: str):
