@@ -691,7 +691,9 @@ def autograd_step(i8, inputs, rounding, seed, stream):
         lin.weight.grad = None
         lin(xg).backward(dY0)
 
-    res = {tag: round(time_us(lambda: layer_step(lin), stream, 20, warm=5) / 1e3, 4)
+    # 50 steps: the host enqueues a step of the autograd op in ~185 us against
+    # ~250 us of GPU work, so short runs time the host's head start as well
+    res = {tag: round(time_us(lambda: layer_step(lin), stream, 50, warm=10) / 1e3, 4)
            for tag, lin in (("int8", lin8), ("bf16", lin16))}
     res["speedup_vs_bf16"] = round(res["bf16"] / res["int8"], 3)
     return res
