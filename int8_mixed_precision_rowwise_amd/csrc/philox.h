@@ -52,10 +52,10 @@ __device__ __forceinline__ u32x4 philox_block(uint64_t seed, uint64_t block) {
                        (uint32_t)(seed >> 32));
 }
 
-// The stochastic-rounding uniform of a word: top 24 bits scaled by 2^-24
-// (exact in binary32, in [0, 1 - 2^-24]).
-__device__ __forceinline__ float word_to_uniform(uint32_t w) {
-  return (float)(w >> 8) * 5.9604644775390625e-08f;
-}
+// The stochastic-rounding uniform of a word in units of 2^-24: its top 24
+// bits as a float (exact in binary32).  The uniform itself is that times
+// 2^-24, in [0, 1 - 2^-24]; the quantizer applies the factor inside the FMA
+// that adds it to the quotient.
+__device__ __forceinline__ float word_uniform_units(uint32_t w) { return (float)(w >> 8); }
 
 }  // namespace i8mp

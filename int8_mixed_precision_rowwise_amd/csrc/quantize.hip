@@ -141,11 +141,15 @@ __device__ __forceinline__ float quotient(float x, float s, float rcp) {
 // value in [-127, 127] rounds it to an integer n (ties to even: the added
 // constant is even), and the sum's bit pattern is that of 1.5 * 2^23 plus n,
 // so its low byte is n in two's complement.
+//
+// Stochastic rounding: u is the uniform in units of 2^-24 (word_uniform_units);
+// u * 2^-24 is exact, so the FMA rounds v + u * 2^-24 once, exactly as the
+// addition of the uniform would.
 template <bool SR, int MODE>
 __device__ __forceinline__ uint32_t code_of(float x, float s, float rcp, float u) {
   const float v = quotient<MODE>(x, s, rcp);
   if constexpr (SR) {
-    return (uint32_t)(int)__builtin_amdgcn_fmed3f(floorf(v + u), -127.0f, 127.0f);
+    return (uint32_t)(int)__builtin_amdgcn_fmed3f(floorf(__builtin_fmaf(u, 0x1p-24f, v)), -127.0f, 127.0f);
   } else {
     return __float_as_uint(__builtin_amdgcn_fmed3f(v, -127.0f, 127.0f) + 0x1.8p23f);
   }
@@ -193,8 +197,9 @@ __device__ __forceinline__ float elem(const uint4& v, int j) {
   return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
 }
 
-// Uniforms of the 8 elements starting at logical index e0.  ALIGNED4: e0 is
-// a multiple of 4, so the chunk needs exactly two Philox blocks.
+// Uniforms (in units of 2^-24) of the 8 elements starting at logical index
+// e0.  ALIGNED4: e0 is a multiple of 4, so the chunk needs exactly two Philox
+// blocks.
 template <bool ALIGNED4>
 __device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, uint64_t e0,
                                                float u[8]) {
@@ -204,8 +209,8 @@ __device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, u
     const u32x4 w1 = philox_block(seed, b + 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u[j] = word_to_uniform(w0.w[j]);
-      u[4 + j] = word_to_uniform(w1.w[j]);
+      u[j] = word_uniform_units(w0.w[j]);
+      u[4 + j] = word_uniform_units(w1.w[j]);
     }
   } else {
     // Elements e0 .. e0+7 take words s .. s+7 (s = e0 mod 4) of the three
@@ -221,7 +226,7 @@ __device__ __forceinline__ void chunk_uniforms(uint64_t seed, uint64_t offset, u
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t word = s == 0 ? w[j] : s == 1 ? w[j + 1] : s == 2 ? w[j + 2] : w[j + 3];
-      u[j] = word_to_uniform(word);
+      u[j] = word_uniform_units(word);
     }
   }
 }
