@@ -299,3 +299,59 @@ def test_quotient_exhaustive(rounding):
             raise AssertionError(f"x bits {xb[bad[0], bad[1]]:#06x} amax bits {a[bad[0]]:#06x}: "
                                  f"gpu {qn[bad[0], bad[1]]} oracle {qo[bad[0], bad[1]]}")
         del xg, q
+
+
+def test_quantize_and_gemm_past_2_31_elements():
+    """Tensors of more than 2^31 elements, where any 32-bit element or byte
+    index would wrap: the row pass (both roundings) and the row pass with
+    column maxima plus the column pass given them (RNE) over 524289 rows of
+    4096 bf16 values (4.3 GB; the last row starts at element 2^31), and an NT
+    GEMM with 65536 x 32776 outputs (2.1e9) at contraction 64.  Sampled rows,
+    whole 8-column slices and sampled outputs against the oracle."""
+    rows, cols = 524289, 4096
+    print(f"case: {rows} x {cols} quantize, 65536 x 32776 x 64 NT", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.randn((rows, cols), generator=g, device="cuda", dtype=torch.bfloat16)
+    sample_rows = [0, 1, 262144, 524286, 524287, 524288]
+    seed, off = 29, 3 << 40
+    for rounding in ("rne", "sr"):
+        q, s = i8.quantize_rowwise(x, rounding, seed, off)
+        torch.cuda.synchronize()
+        for r in sample_rows:
+            xb = tensor_bits(x[r:r + 1])
+            qo, so = oracle.quantize_rowwise(xb, RC[rounding], seed, off + r * cols // 4)
+            assert np.array_equal(q[r:r + 1].cpu().numpy(), qo), f"{rounding} row {r} codes"
+            assert np.array_equal(s[r:r + 1].cpu().numpy().view(np.uint32), so.view(np.uint32)), f"row {r} scale"
+        del q, s
+    q, s, cm = i8.quantize_rowwise_colmax(x)
+    q2, s2 = i8.quantize_colwise_given_colmax(x, cm)
+    torch.cuda.synchronize()
+    for c0 in (0, 2048, cols - 8):
+        xb = tensor_bits(x[:, c0:c0 + 8])
+        assert np.array_equal(cm[c0:c0 + 8].cpu().numpy().view(np.uint32),
+                              oracle.col_absmax(xb).view(np.uint32)), f"column maxima at {c0}"
+        qo, so = oracle.quantize_colwise(xb, oracle.RNE, 0, 0)
+        assert np.array_equal(q2[:, c0:c0 + 8].cpu().numpy(), qo), f"column codes at {c0}"
+        assert np.array_equal(s2[c0:c0 + 8].cpu().numpy().view(np.uint32), so.view(np.uint32)), f"scales at {c0}"
+    for r in sample_rows:
+        qo, so = oracle.quantize_rowwise(tensor_bits(x[r:r + 1]), oracle.RNE, 0, 0)
+        assert np.array_equal(q[r:r + 1].cpu().numpy(), qo), f"row {r} codes (with maxima)"
+    del x, q, s, cm, q2, s2
+    torch.cuda.empty_cache()
+
+    M, N, K = 65536, 32776, 64
+    rng = np.random.default_rng(7)
+    qa = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    qb = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    sa = rng.uniform(1e-3, 2e-3, size=M).astype(np.float32)
+    sb = rng.uniform(1e-3, 2e-3, size=N).astype(np.float32)
+    Y = i8.int8_scaled_mm("NT", torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(),
+                          torch.from_numpy(qb).cuda(), torch.from_numpy(sb).cuda())
+    torch.cuda.synchronize()
+    ms = np.concatenate([rng.integers(0, M, 2048), np.arange(M - 16, M).repeat(4)])
+    ns = np.concatenate([rng.integers(0, N, 2048), np.tile(np.array([0, 1, N - 2, N - 1]), 16)])
+    _, y = oracle.scaled_mm_at(oracle.LAYOUTS["NT"], qa, sa, qb, sb, ms, ns)
+    got = tensor_bits(Y[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()])
+    assert np.array_equal(got, y), f"{int(np.count_nonzero(got != y))} sampled outputs differ"
+    del Y
+    torch.cuda.empty_cache()
