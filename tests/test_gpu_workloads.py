@@ -355,3 +355,33 @@ def test_quantize_and_gemm_past_2_31_elements():
     assert np.array_equal(got, y), f"{int(np.count_nonzero(got != y))} sampled outputs differ"
     del Y
     torch.cuda.empty_cache()
+
+
+def test_chains_past_2_31_elements():
+    """The forward chain with column maxima and the grad-input chain with
+    X of 524289 x 4096 (2^31 + 4096 elements; its codes fill more than 2 GB
+    of the workspace) and dX of the same size: sampled rows of Y and dX against
+    the oracle's quantized operands and scaled matmul."""
+    M, N, K = 524289, 256, 4096
+    print(f"case: chains {M} x {N} x {K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(37)
+    X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    W = (0.02 * torch.randn((N, K), generator=g, device="cuda")).to(torch.bfloat16)
+    dY = (1e-3 * torch.randn((M, N), generator=g, device="cuda")).to(torch.bfloat16)
+    seed, off = 5, 1 << 44
+    Y, cx, cw = i8.linear_fwd_colmax(X, W, "rne", seed, off)
+    dX, _ = i8.linear_bwd(dY, X, W, "rne", seed, off, want_dw=False, colmax_x=cx, colmax_w=cw)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 262144, 524286, 524287, 524288])
+    Wb = tensor_bits(W)
+    qw, sw = oracle.quantize_rowwise(Wb, oracle.RNE)
+    qwc, swc = oracle.quantize_colwise(Wb, oracle.RNE)
+    for r in rows:
+        qx, sx = oracle.quantize_rowwise(tensor_bits(X[r:r + 1]), oracle.RNE)
+        _, y = oracle.scaled_mm_at(oracle.LAYOUTS["NT"], qx, sx, qw, sw, np.zeros(N, np.int64), np.arange(N))
+        assert np.array_equal(tensor_bits(Y[r]), y), f"Y row {r}"
+        qd, sd = oracle.quantize_rowwise(tensor_bits(dY[r:r + 1]), oracle.RNE)
+        _, dx = oracle.scaled_mm_at(oracle.LAYOUTS["NN"], qd, sd, qwc, swc, np.zeros(K, np.int64), np.arange(K))
+        assert np.array_equal(tensor_bits(dX[r]), dx), f"dX row {r}"
+    del X, W, dY, Y, dX, cx, cw
+    torch.cuda.empty_cache()
