@@ -491,13 +491,21 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int R, bool KMAJOR, int NW>
+// REBASE (operands read down their rows only): each slab's loads use a
+// descriptor based at the slab's first row, so the offsets stay within one
+// slab (BK rows) however far the operand extends, beyond 2^31 bytes included.
+// Without it the whole operand must lie within 32-bit offsets of one
+// descriptor; the launchers take this form only for operands that do not.
+template <int R, bool KMAJOR, int NW, bool REBASE = false>
 struct Dma {
   static constexpr int kInst = R * BK / 1024 / NW;  // instructions per wave per slab (NW waves)
   v4u rsrc;              // buffer descriptor (scalar registers)
   uint32_t off0[kInst];  // offset of this lane's chunk in slab 0
   int kpos[kInst];       // contraction index of the chunk within a slab (BK: outside the operand)
   uint32_t kstride;      // offset advance per contraction index
+  const int8_t* base;    // REBASE: row 0 of the tile's columns
+  int64_t bytes;         // REBASE: bytes from base to the operand's end
+  int64_t ld_;           // REBASE: leading dimension (bytes)
 
   // p: operand base, ld: leading dim (bytes), mn0: first output row/col of
   // the tile, MN: output extent along this operand, K: contraction length.
@@ -531,7 +539,14 @@ struct Dma {
     } else {
       constexpr int CPR = R / 16;
       const int64_t cols_in = min((int64_t)R, MN - mn0);
-      rsrc = make_rsrc(p + mn0, (K - 1) * ld + cols_in);
+      if constexpr (REBASE) {
+        base = p + mn0;
+        bytes = (K - 1) * ld + cols_in;
+        ld_ = ld;
+        rsrc = make_rsrc(base, min(bytes, (int64_t)kOob));  // for issue_past_end
+      } else {
+        rsrc = make_rsrc(p + mn0, (K - 1) * ld + cols_in);
+      }
       kstride = (uint32_t)ld;
 #pragma unroll
       for (int j = 0; j < kInst; ++j) {
@@ -550,7 +565,15 @@ struct Dma {
   __device__ __forceinline__ void issue_one(int j, int8_t* dst, int slab, int64_t K, int wave) const {
     const int k0 = BK * slab;
     const int limit = (int)min(K - k0, (int64_t)BK);  // contraction indices left in this slab
-    const uint32_t o = kpos[j] < limit ? off0[j] + (uint32_t)k0 * kstride : kOob;
+    uint32_t o;
+    v4u r = rsrc;
+    if constexpr (REBASE && !KMAJOR) {
+      const int64_t sh = (int64_t)k0 * ld_;
+      o = kpos[j] < limit ? off0[j] : kOob;
+      r = make_rsrc(base + sh, max((int64_t)0, min(bytes - sh, (int64_t)kOob)));
+    } else {
+      o = kpos[j] < limit ? off0[j] + (uint32_t)k0 * kstride : kOob;
+    }
     const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
         (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(dst + (wave + NW * j) * 1024)));
     // Issued as inline assembly: the compiler then does not treat the LDS
@@ -559,7 +582,7 @@ struct Dma {
     // the workgroup barrier.
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(l), "v"(o), "s"(rsrc)
+                 : "s"(l), "v"(o), "s"(r)
                  : "memory", "m0");
   }
 
@@ -920,7 +943,7 @@ struct Mma<1> {
 };
 
 template <int BM, int BN, int WGN, bool A_KMAJOR, bool B_KMAJOR, bool OUT_I32, bool VEC, int FMT = 0,
-          bool SIDE = false>
+          bool SIDE = false, bool REBASE = false>
 __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_t N, int64_t K,
                                                               const int8_t* __restrict__ A, int64_t lda,
                                                               const float* __restrict__ sa,
@@ -989,8 +1012,8 @@ __global__ __launch_bounds__(128 * WGN) void gemm_i8_pipelined(int64_t M, int64_
     }
   }
 
-  Dma<BM, A_KMAJOR, NW> da;
-  Dma<BN, B_KMAJOR, NW> db;
+  Dma<BM, A_KMAJOR, NW, REBASE> da;
+  Dma<BN, B_KMAJOR, NW, REBASE> db;
   da.init(A, lda, m0, M, K, wave, lane);
   db.init(B, ldb, n0, N, K, wave, lane);
 
@@ -1163,19 +1186,23 @@ __global__ __launch_bounds__(512) void mfma_rate_probe(const int8_t* __restrict_
 }
 
 template <int BM, int BN, bool AK, bool BKM, bool OUT_I32, bool VEC>
-void launch(bool fast, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
-            const float* sa, const int8_t* B, int64_t ldb, const float* sb, void* C, int64_t ldc,
-            const ColmaxJob* side, hipStream_t stream) {
+void launch(bool fast, bool rebase, dim3 grid, int64_t M, int64_t N, int64_t K, const int8_t* A,
+            int64_t lda, const float* sa, const int8_t* B, int64_t ldb, const float* sb, void* C,
+            int64_t ldc, const ColmaxJob* side, hipStream_t stream) {
   // 256 x 256 tiles: 8 waves (2 per SIMD, 128 x 64 each) so one wave's MFMAs
   // run while the other waits on its slab-load issue; 128 x 128: 4 waves.
   // side (pipelined kernel only) is a column-maxima reduction the caller has
-  // checked fits (side_fits).
+  // checked fits (side_fits).  rebase: the pipelined kernel with per-slab
+  // descriptors (rebase_ok; 256 x 256 tiles, packed bf16 output only).
   constexpr int WGN = BM >= 256 ? 4 : 2;
   if (fast && side)
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC, 0, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0, *side);
   else if (fast)
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, OUT_I32, VEC><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0, ColmaxJob{});
-  else
+  else if (rebase && BM == 256 && !OUT_I32 && VEC && !(AK && BKM)) {
+    if constexpr (BM == 256 && !OUT_I32 && VEC && !(AK && BKM))
+      gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 0, false, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, K, 0, ColmaxJob{});
+  } else
     gemm_i8_general<BM, BN, AK, BKM, OUT_I32, VEC><<<grid, kThreads, 0, stream>>>(M, N, K, A, lda, sa, B, ldb, sb, C, ldc);
 }
 
@@ -1206,6 +1233,22 @@ bool pipelined_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
   return K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024 && mn_ok;
 }
 
+// Whether the pipelined kernel with per-slab descriptors (REBASE) takes a
+// problem the plain form cannot because an operand read down its rows spans
+// 2^31 bytes or more (e.g. a grad-weight GEMM over a wide output at many
+// tokens): 256 x 256 tiles, the same shape rules, and each slab (BK rows of
+// such an operand) within 32-bit offsets.
+template <int BM, int BN, bool AK, bool BKM>
+bool rebase_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+  if (BM != 256 || (AK && BKM)) return false;
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t a_ext = AK ? (int64_t)BM * lda : (int64_t)BK * lda;
+  const int64_t b_ext = BKM ? (int64_t)BN * ldb : (int64_t)BK * ldb;
+  const bool mn_ok = (AK || M % 4 == 0) && (BKM || N % 4 == 0);
+  return K > 0 && K % 16 == 0 && a_ext < lim - 1024 && b_ext < lim - 1024 && mn_ok &&
+         !pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
+}
+
 template <int BM, int BN, bool AK, bool BKM>
 hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const float* sa,
                const int8_t* B, int64_t ldb, const float* sb, uint16_t* Cb, int32_t* Ci,
@@ -1213,6 +1256,7 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool fast = pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
+  const bool rebase = rebase_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
   if (side && (Ci || !(fast && side_fits(*side, tiles, BM)))) {  // as a launch of its own
     const hipError_t e = launch_colmax_finalize(*side, stream);
     if (e != hipSuccess) return e;
@@ -1222,11 +1266,11 @@ hipError_t run(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, co
   const uintptr_t c = Ci ? reinterpret_cast<uintptr_t>(Ci) : reinterpret_cast<uintptr_t>(Cb);
   const bool vec = Ci ? (ldc % 4 == 0 && c % 16 == 0) : (ldc % 8 == 0 && c % 16 == 0);
   if (Ci) {  // the int32 hook: no column maxima ride along
-    if (vec) launch<BM, BN, AK, BKM, true, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, nullptr, stream);
-    else launch<BM, BN, AK, BKM, true, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, nullptr, stream);
+    if (vec) launch<BM, BN, AK, BKM, true, true>(fast, rebase, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, nullptr, stream);
+    else launch<BM, BN, AK, BKM, true, false>(fast, rebase, grid, M, N, K, A, lda, sa, B, ldb, sb, Ci, ldc, nullptr, stream);
   } else {
-    if (vec) launch<BM, BN, AK, BKM, false, true>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, side, stream);
-    else launch<BM, BN, AK, BKM, false, false>(fast, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, side, stream);
+    if (vec) launch<BM, BN, AK, BKM, false, true>(fast, rebase, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, side, stream);
+    else launch<BM, BN, AK, BKM, false, false>(fast, rebase, grid, M, N, K, A, lda, sa, B, ldb, sb, Cb, ldc, side, stream);
   }
   return hipGetLastError();
 }
@@ -1455,12 +1499,16 @@ hipError_t run_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t ld
   const int8_t* a = reinterpret_cast<const int8_t*>(A);
   const int8_t* b = reinterpret_cast<const int8_t*>(B);
   const bool fast = pipelined_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
+  const bool rebase = !Cf && vec && rebase_ok<BM, BN, AK, BKM>(M, N, K, lda, ldb);
   if (side && (Cf || !(fast && side_fits(*side, tiles, BM)))) {  // as a launch of its own
     const hipError_t e = launch_colmax_finalize(*side, stream);
     if (e != hipSuccess) return e;
     side = nullptr;
   }
-  if (side && vec) {
+  if (rebase) {  // an operand read down its rows spans 2^31 bytes or more
+    if constexpr (BM == 256 && !(AK && BKM))
+      gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1, false, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, ColmaxJob{});
+  } else if (side && vec) {
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, true, 1, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, *side);
   } else if (side) {
     gemm_i8_pipelined<BM, BN, WGN, AK, BKM, false, false, 1, true><<<grid, 128 * WGN, 0, stream>>>(M, N, K, a, lda, sa, b, ldb, sb, C, ldc, K, 0, *side);

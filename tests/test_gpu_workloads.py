@@ -385,3 +385,54 @@ def test_chains_past_2_31_elements():
         assert np.array_equal(tensor_bits(dX[r]), dx), f"dX row {r}"
     del X, W, dY, Y, dX, cx, cw
     torch.cuda.empty_cache()
+
+
+def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of finite float32 values, round to nearest even."""
+    b = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("layout", ["TN", "NN"])
+def test_gemm_operand_past_2_31_bytes(layout):
+    """An operand read down its rows that spans 2^31 bytes (TN: A stored
+    32768 x 65536; NN: B stored 32768 x 65536), which the pipelined kernel
+    addresses with one descriptor per slab.  INT8 outputs sampled against the
+    oracle; FP8 outputs against the fp32 sums of the FP8 hook (the general
+    kernel, whose sums the pipelined kernel reproduces bit for bit) with the
+    epilogue applied on the host in the same order."""
+    M, N, K = (65536, 256, 32768) if layout == "TN" else (256, 65536, 32768)
+    a_shape = (K, M) if layout == "TN" else (M, K)
+    b_shape = (K, N)
+    print(f"case: {layout} {M} x {N} x {K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(41)
+    rng = np.random.default_rng(41)
+    ms = np.concatenate([rng.integers(0, M, 512), [0, M - 1, M - 1, 0]])
+    ns = np.concatenate([rng.integers(0, N, 512), [0, N - 1, 0, N - 1]])
+    ms_t, ns_t = torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()
+    sa = torch.rand(M, generator=g, device="cuda") * 1e-3 + 1e-3
+    sb = torch.rand(N, generator=g, device="cuda") * 1e-3 + 1e-3
+    A = torch.randint(-127, 128, a_shape, generator=g, device="cuda", dtype=torch.int8)
+    B = torch.randint(-127, 128, b_shape, generator=g, device="cuda", dtype=torch.int8)
+    Y = i8.int8_scaled_mm(layout, A, sa, B, sb)
+    torch.cuda.synchronize()
+    _, y = oracle.scaled_mm_at(oracle.LAYOUTS[layout], A.cpu().numpy(), sa.cpu().numpy(), B.cpu().numpy(),
+                               sb.cpu().numpy(), ms, ns)
+    got = tensor_bits(Y[ms_t, ns_t])
+    assert np.array_equal(got, y), f"INT8 {layout}: {int(np.count_nonzero(got != y))} sampled outputs differ"
+    del A, B, Y
+    torch.cuda.empty_cache()
+    # E4M3 codes, the two NaN patterns moved to the largest finite magnitude
+    A8 = torch.randint(0, 256, a_shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    B8 = torch.randint(0, 256, b_shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    for t in (A8, B8):  # elementwise: boolean-mask indexing does not take 2^31 elements
+        t.sub_(((t & 0x7F) == 0x7F).to(torch.uint8))
+    Y8 = i8.fp8_scaled_mm(layout, A8, sa, B8, sb)
+    F = i8.fp8_mm_f32(layout, A8, B8)
+    torch.cuda.synchronize()
+    f = F[ms_t, ns_t].cpu().numpy()
+    want = _bf16_rne_bits((f * sa.cpu().numpy()[ms]).astype(np.float32) * sb.cpu().numpy()[ns])
+    got8 = tensor_bits(Y8[ms_t, ns_t])
+    assert np.array_equal(got8, want), f"FP8 {layout}: {int(np.count_nonzero(got8 != want))} sampled outputs differ"
+    del A8, B8, Y8, F
+    torch.cuda.empty_cache()
