@@ -436,3 +436,29 @@ def test_gemm_operand_past_2_31_bytes(layout):
     assert np.array_equal(got8, want), f"FP8 {layout}: {int(np.count_nonzero(got8 != want))} sampled outputs differ"
     del A8, B8, Y8, F
     torch.cuda.empty_cache()
+
+
+def test_lm_head_grad_weight_at_32768_tokens():
+    """The Llama-3 LM head's grad-weight chain at 32768 tokens: dY of
+    32768 x 128256 (8.4 GB) quantized column-wise, and dW = dY.T @ X on the
+    pipelined kernel with per-slab descriptors (dY's 4.2 GB of codes are read
+    down their rows).  Sampled 8 x 8 blocks of dW against the oracle, from
+    8-column slices of dY and X (column-wise quantization treats columns
+    independently under RNE)."""
+    M, N, K = 32768, 128256, 4096
+    print(f"case: lm head grad-weight {M} x {N} x {K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(43)
+    X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    W = (0.02 * torch.randn((N, K), generator=g, device="cuda")).to(torch.bfloat16)
+    dY = (1e-3 * torch.randn((M, N), generator=g, device="cuda")).to(torch.bfloat16)
+    _, dW = i8.linear_bwd(dY, X, W, "rne", 0, 0, want_dx=False)
+    torch.cuda.synchronize()
+    for n0, k0 in ((0, 0), (64000, 2048), (N - 8, K - 8)):
+        qd, sd = oracle.quantize_colwise(tensor_bits(dY[:, n0:n0 + 8]), oracle.RNE)
+        qx, sx = oracle.quantize_colwise(tensor_bits(X[:, k0:k0 + 8]), oracle.RNE)
+        ms, ns = np.repeat(np.arange(8), 8), np.tile(np.arange(8), 8)
+        _, y = oracle.scaled_mm_at(oracle.LAYOUTS["TN"], qd, sd, qx, sx, ms, ns)
+        got = tensor_bits(dW[n0:n0 + 8, k0:k0 + 8]).reshape(-1)
+        assert np.array_equal(got, y), f"dW block at ({n0}, {k0})"
+    del X, W, dY, dW
+    torch.cuda.empty_cache()
