@@ -450,3 +450,47 @@ def test_fp8_chains_4096_equal_primitives():
                             (dW, i8.fp8_scaled_mm("TN", *pdc, *pxc), "dW")):
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{what} differs from the primitives"
+
+
+def test_fp8_chains_on_two_streams_give_the_same_bytes():
+    """The FP8 chains of two layers (the first splits its forward contraction
+    into fp32 planes, added in a fixed order; the second takes the paired
+    full-width row passes) run once in order on the current stream, then
+    concurrently on two other streams of the default priority in the other
+    order, with the workspaces refilled with junk: byte-identical outputs."""
+    from workloads import LinearShape, linear_inputs
+    shapes = [LinearShape("det8_a", 256, 512, 8192), LinearShape("det8_b", 1024, 768, 4096)]
+    jobs = []
+    for k, s in enumerate(shapes):
+        t = linear_inputs(s, seed=200 + k, device="cuda")
+        ws_f = torch.empty(i8.linear_workspace_bytes(s.M, s.N, s.K, False), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(i8.linear_workspace_bytes(s.M, s.N, s.K, True), dtype=torch.uint8, device="cuda")
+        outs = [torch.empty((s.M, s.N), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((s.M, s.K), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((s.N, s.K), dtype=torch.bfloat16, device="cuda")]
+        jobs.append((t["X"], t["W"], t["dY"], ws_f, ws_b, outs))
+
+    def step(job):
+        X, W, dY, ws_f, ws_b, (Y, dX, dW) = job
+        _, cx, cw = i8.linear_fwd_fp8_colmax(X, W, out=Y, workspace=ws_f)
+        i8.linear_bwd_fp8(dY, X, W, workspace=ws_b, dX=dX, dW=dW, colmax_x=cx, colmax_w=cw)
+
+    step(jobs[0])
+    step(jobs[1])
+    torch.cuda.synchronize()
+    ref = [[o.clone() for o in job[5]] for job in jobs]
+    for job in jobs:
+        for o in job[5]:
+            o.fill_(0)
+        job[3].fill_(0xA5)
+        job[4].fill_(0x5A)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        step(jobs[1])
+    with torch.cuda.stream(s1):
+        step(jobs[0])
+    torch.cuda.synchronize()
+    for k, job in enumerate(jobs):
+        for got, want, what in zip(job[5], ref[k], ("Y", "dX", "dW")):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"layer {k} {what}"
