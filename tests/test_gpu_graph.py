@@ -1,4 +1,4 @@
-"""The linear chains captured in a HIP graph.
+"""The linear chains (INT8 and FP8) captured in a HIP graph.
 
 The library allocates, clears and synchronizes nothing inside its calls, so a
 capture (torch.cuda.CUDAGraph on its capture stream) holds exactly the
@@ -74,4 +74,48 @@ def test_linear_chains_replayed_from_a_hip_graph(rounding, M, N, K):
             assert same_bytes(a, b), f"replay {rep}: {name} differs from the eager chains"
         assert torch.equal(got["cx"].view(torch.int32), cxe.view(torch.int32)), f"replay {rep}: colmax X"
         assert torch.equal(got["cw"].view(torch.int32), cwe.view(torch.int32)), f"replay {rep}: colmax W"
+    del g
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 1000), (256, 512, 8192)])
+def test_fp8_chains_replayed_from_a_hip_graph(M, N, K):
+    """The FP8 chains (the second shape splits its forward contraction into
+    fp32 planes) captured and replayed with new inputs: every replay equals
+    the eager chains byte for byte."""
+    shape = LinearShape("graph8", M, N, K)
+    dev = torch.device("cuda")
+    t = linear_inputs(shape, seed=0, device=dev)
+    X, W, dY = t["X"].clone(), t["W"].clone(), t["dY"].clone()
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    wsf = torch.empty(max(1, i8.linear_workspace_bytes(M, N, K, False)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(1, i8.linear_workspace_bytes(M, N, K, True)), dtype=torch.uint8, device=dev)
+
+    def step():
+        _, cx, cw = i8.linear_fwd_fp8_colmax(X, W, out=Y, workspace=wsf)
+        i8.linear_bwd_fp8(dY, X, W, workspace=wsb, dX=dX, dW=dW, colmax_x=cx, colmax_w=cw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        u = linear_inputs(shape, seed=rep + 1, device=dev)
+        X.copy_(u["X"])
+        W.copy_(u["W"])
+        dY.copy_(u["dY"])
+        g.replay()
+        torch.cuda.synchronize()
+        got = (Y.clone(), dX.clone(), dW.clone())
+        Ye, cxe, cwe = i8.linear_fwd_fp8_colmax(X, W)
+        dXe, dWe = i8.linear_bwd_fp8(dY, X, W, colmax_x=cxe, colmax_w=cwe)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("Y", "dX", "dW"), got, (Ye, dXe, dWe)):
+            assert same_bytes(a, b), f"replay {rep}: {name} differs from the eager chains"
     del g
