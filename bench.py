@@ -720,8 +720,28 @@ def fp8_step(i8, sets, M, N, K, stream, gemm_ops):
         i8.linear_bwd_fp8(dY, X, W, workspace=wsb, dX=dX, dW=dW, colmax_x=cx, colmax_w=cw)
 
     ms = time_us(step, stream, 20, warm=5) / 1e3
-    return {"ms_per_step": round(ms, 4), "tops": round(3 * gemm_ops / (ms * 1e-3) / 1e12, 1),
-            "note": "linear_fwd_fp8_colmax + linear_bwd_fp8 with the maxima, same inputs"}
+    out = {"ms_per_step": round(ms, 4), "tops": round(3 * gemm_ops / (ms * 1e-3) / 1e12, 1),
+           "note": "linear_fwd_fp8_colmax + linear_bwd_fp8 with the maxima, same inputs"}
+    # the forward GEMM alone against hipBLASLt's FP8 GEMM on the same E4M3 codes
+    # with the same row-wise scales (torch._scaled_mm, scale_a [M, 1], scale_b [1, N])
+    X, W, _ = sets[0]
+    qx, sx = i8.quantize_rowwise_fp8(X)
+    qw, sw = i8.quantize_rowwise_fp8(W)
+    ours = time_us(lambda: i8.fp8_scaled_mm("NT", qx, sx, qw, sw, out=Y), stream, 20)
+    gemm = {"ours_us": round(ours, 2), "ours_tops": round(gemm_ops / (ours * 1e-6) / 1e12, 1)}
+    try:
+        a, b = qx.view(torch.float8_e4m3fn), qw.view(torch.float8_e4m3fn)
+        f = lambda: torch._scaled_mm(a, b.t(), scale_a=sx.view(-1, 1), scale_b=sw.view(1, -1),  # noqa: E731
+                                     out_dtype=torch.bfloat16)
+        f()
+        torch.cuda.synchronize()
+        theirs = time_us(f, stream, 20)
+        gemm.update(hipblaslt_rowwise_us=round(theirs, 2),
+                    hipblaslt_rowwise_tops=round(gemm_ops / (theirs * 1e-6) / 1e12, 1))
+    except (RuntimeError, TypeError) as e:  # not offered by this torch build
+        gemm["hipblaslt_rowwise"] = f"unavailable: {str(e)[:80]}"
+    out["gemm_NT_vs_hipblaslt"] = gemm
+    return out
 
 
 def single_linear_ctx(i8, stream, records):
